@@ -1,0 +1,135 @@
+"""Oracle for the CAAT partial-sync sublayer forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The GPU library and its
+Python binding never import it, and the two share no code.
+
+The arithmetic lives in ``caat_oracle.c`` (plain C, fp64, OpenMP over rank and
+token rows); this module only converts arrays and calls it.  Source of the method:
+"Tensor-Parallelism with Partially Synchronized Activations", App. A.2 Eq. 22 and 24,
+§3.2 (logical devices), §4 Eq. 9 and "Private channel scaling".
+
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
+against closed forms, library routines on special cases, the page's P = 2 block
+form (Eq. 8 / Eq. 19), a hand-derived worked example and brute force on tiny shapes.
+The bf16 roundings of the GPU path (intermediate activations, partials, outputs)
+are not modelled: the page fixes none of them, and the tolerance absorbs them.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+GELU, GELU_TANH, SWIGLU, NONE = 0, 1, 2, 3
+LAYERNORM, RMSNORM = 0, 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        fp = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_shared_channels.argtypes = [ctypes.c_int, ctypes.c_double]
+        lib.oracle_shared_channels.restype = ctypes.c_int
+        lib.oracle_activation.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        lib.oracle_activation.restype = ctypes.c_double
+        lib.oracle_sublayer.argtypes = (
+            [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double]
+            + [fp] * 6 + [dp] * 3)
+        lib.oracle_sublayer.restype = ctypes.c_int
+        lib.oracle_partial_sync_norm.argtypes = (
+            [ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_double]
+            + [fp] * 4 + [dp] * 2)
+        lib.oracle_partial_sync_norm.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: widen exactly to float32 on the CPU
+        a = a.detach().to("cpu").float().numpy()
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _fptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_float)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _dptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def shared_channels(h: int, p: float) -> int:
+    """n_s = floor(h p) (App. A.2, Eq. 22), near-integers counted as integers."""
+    return _load().oracle_shared_channels(int(h), float(p))
+
+
+def activation(act: int, g: float, u: float = 0.0) -> float:
+    """The nonlinearity sigma of Eq. 20-22 on one value (SwiGLU: silu(g) * u)."""
+    return _load().oracle_activation(int(act), float(g), float(u))
+
+
+def sublayer(x, W1, W2, gamma, *, act, norm, n_s, ffn=0, beta=None, resid=None,
+             s_priv=1.0, eps=1e-5, want_partials=False):
+    """Forward of one CAAT sublayer for every rank, in fp64.
+
+    x [P][T][kin]; W1 [P][F1][h] (ignored for act=NONE); W2 [P][h][k2];
+    gamma, beta [h]; resid [P][T][h] or None (= x).  Returns (out, out_resid) or
+    (out, out_resid, partials), float64 arrays of shape [P][T][h].
+    """
+    x = _f32(x)
+    W2 = _f32(W2)
+    P, T, kin = x.shape
+    h = W2.shape[1]
+    if act == NONE:
+        W1 = None
+        ffn = 0
+    else:
+        W1 = _f32(W1)
+        fs = W2.shape[2]
+        ffn = fs * P
+    gamma = _f32(gamma)
+    beta = _f32(beta)
+    resid = _f32(resid)
+    out = np.empty((P, T, h), np.float64)
+    out_resid = np.empty((P, T, h), np.float64)
+    zt = np.empty((P, T, h), np.float64) if want_partials else None
+    rc = _load().oracle_sublayer(P, T, h, ffn, act, norm, n_s, float(s_priv), float(eps),
+                                 _fptr(x), _fptr(resid), _fptr(W1), _fptr(W2),
+                                 _fptr(gamma), _fptr(beta),
+                                 _dptr(zt), _dptr(out), _dptr(out_resid))
+    if rc != 0:
+        raise ValueError("oracle_sublayer rejected its arguments")
+    if want_partials:
+        return out, out_resid, zt
+    return out, out_resid
+
+
+def partial_sync_norm(partials, resid, gamma, *, norm, n_s, beta=None, s_priv=1.0, eps=1e-5):
+    """Partial channel-reduce + residual + norm on given partials [P][T][h], fp64."""
+    partials = _f32(partials)
+    resid = _f32(resid)
+    gamma = _f32(gamma)
+    beta = _f32(beta)
+    P, T, h = partials.shape
+    out = np.empty((P, T, h), np.float64)
+    out_resid = np.empty((P, T, h), np.float64)
+    rc = _load().oracle_partial_sync_norm(P, T, h, norm, n_s, float(s_priv), float(eps),
+                                          _fptr(partials), _fptr(resid), _fptr(gamma),
+                                          _fptr(beta), _dptr(out), _dptr(out_resid))
+    if rc != 0:
+        raise ValueError("oracle_partial_sync_norm rejected its arguments")
+    return out, out_resid
