@@ -1,0 +1,153 @@
+/*
+ * caat.h - C ABI of libcaat: the forward pass of one CAAT tensor-parallel sublayer
+ * (partially synchronized activations) on an AMD Instinct MI355X (gfx950), with all
+ * P tensor-parallel ranks emulated on the one device.
+ *
+ * Method: "Tensor-Parallelism with Partially Synchronized Activations"
+ * (Lamprecht, Karnieli, Hanani, Giladi, Soudry).
+ *   - MLP sublayer: App. A.2, Eq. 22 (P = 2: §3.1, Eq. 6-8).  Rank m computes
+ *       Zt_m = act(X_m A_m) B_m       (column-parallel A, row-parallel B)
+ *   - Attention output projection: App. A.2, Eq. 24 (P = 2: App. A.1, Eq. 19).
+ *       Zt_m = H_m O_m                (O row-parallel; rank m holds all h columns)
+ *   - Partial channel-reduce (Eq. 22 / 24): for channel l < n_s = floor(h p),
+ *       Z_m[l] = sum over ranks of Zt[l]; otherwise Z_m[l] = s_priv * Zt_m[l].
+ *     The shared channels are the first n_s (§3).  s_priv is the private channel
+ *     scaling of §4 (Eq. 14-15); it is 1 unless set.
+ *   - Then, per rank, the residual add and the normalization (§4, Eq. 9):
+ *       r_m = R_m + Z_m,  out_m = Norm(r_m)
+ *     LayerNorm: (r - mean) / sqrt(var + eps) * gamma + beta (biased variance).
+ *     RMSNorm:   r / sqrt(mean(r^2) + eps) * gamma.
+ *   - All ranks run on one device, one after another in the page's terms
+ *     ("logical devices", §3.2), so the channel-reduce is a local sum.
+ *
+ * Conventions for every call below.
+ *   Pointers: device pointers (HBM) unless stated; 16-byte aligned; dense,
+ *     row-major, in the handle's dtype (CAAT_BF16: bfloat16, CAAT_F32: float).
+ *     The caller owns every buffer; the library never allocates device memory.
+ *   Shapes (h hidden size, P ranks, T tokens, f_s = ffn / P):
+ *     x / in     [P][T][h]       (act = CAAT_NONE: the head outputs H, [P][T][h/P])
+ *     W1         [P][F1][h]      F1 = f_s, or 2 f_s for SwiGLU: rows [0, f_s) are the
+ *                                gate and rows [f_s, 2 f_s) the up projection of the
+ *                                same column range of the full matrices.  Row k of
+ *                                shard m is column k of A_m.  Unused for CAAT_NONE.
+ *     W2         [P][h][k2]      k2 = f_s (MLP) or h/P (out-projection).  Row l of
+ *                                shard m is column l of B_m (or of O_m).
+ *     Y          [P][T][f_s]     activation after the first GEMM (workspace)
+ *     partials   [P][T][h]       Zt before any reduction (workspace)
+ *     resid, out, out_resid  [P][T][h]
+ *     gamma, beta [h]            shared by all ranks; beta is used by LayerNorm only
+ *   Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *     only enqueues kernels on it and returns without a host synchronisation.
+ *   Errors: every call returns a caat_status.  Arguments are checked before any
+ *     launch; a call that returns an error has enqueued nothing.  A failed launch
+ *     returns CAAT_EDEVICE.  Faults during execution surface at the caller's next
+ *     synchronisation of the stream.  No C++ exception crosses this interface.
+ *   Concurrency: calls on one handle that overlap on different streams must use
+ *     different workspaces (one handle per stream).
+ */
+#ifndef CAAT_H
+#define CAAT_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct caat_ctx *caat_handle;
+
+typedef enum {
+    CAAT_OK = 0,
+    CAAT_EINVAL = -1,       /* bad argument: null pointer, bad shape, misalignment */
+    CAAT_ENOMEM = -2,       /* host allocation of the handle failed */
+    CAAT_EWORKSPACE = -3,   /* no workspace set, or smaller than caat_workspace_bytes */
+    CAAT_EDEVICE = -4,      /* a HIP call or kernel launch failed */
+    CAAT_EUNSUPPORTED = -5  /* not a gfx950 device, or a size beyond the kernels' limits */
+} caat_status;
+
+typedef enum { CAAT_LAYERNORM = 0, CAAT_RMSNORM = 1 } caat_norm;
+
+/* sigma of Eq. 20-22.  CAAT_GELU: a * Phi(a) (erf form).  CAAT_GELU_TANH: the tanh
+ * approximation of GeLU.  CAAT_SWIGLU: silu(x A_gate) * (x A_up).  CAAT_NONE: the
+ * attention output projection (no first GEMM, no activation). */
+typedef enum { CAAT_GELU = 0, CAAT_GELU_TANH = 1, CAAT_SWIGLU = 2, CAAT_NONE = 3 } caat_act;
+
+typedef enum { CAAT_F32 = 0, CAAT_BF16 = 1 } caat_dtype;
+
+/* Creates a handle for one sublayer shape.  Host only: touches no device.
+ *   h: hidden size, 8 <= h <= 16384, h % 8 == 0.
+ *   ffn: FFN size of the full MLP, ffn % P == 0, (ffn / P) % 8 == 0; ignored for
+ *        CAAT_NONE, which instead needs (h / P) % 8 == 0.
+ *   P: emulated ranks, 1..16.  p: sync fraction in [0, 1] (NaN rejected).
+ *   n_s = floor(h p) shared channels (an h p within 1e-9 h of an integer counts as
+ *   that integer), see caat_shared_channels.
+ * Returns CAAT_EINVAL on a bad argument, CAAT_ENOMEM if the handle cannot be made. */
+int caat_create(caat_handle *out, int h, int ffn, int P, double p, int norm, int act,
+                int dtype);
+
+/* Frees the handle (not the caller's buffers).  NULL is accepted. */
+int caat_destroy(caat_handle handle);
+
+/* Normalization epsilon (default 1e-5), eps >= 0. */
+int caat_set_eps(caat_handle handle, float eps);
+
+/* Private channel scale s_priv (default 1; the page's setting is sqrt(P), §4). */
+int caat_set_private_scale(caat_handle handle, float s);
+
+/* n_s, the number of shared channels [0, n_s); or CAAT_EINVAL for a NULL handle. */
+int caat_shared_channels(caat_handle handle);
+
+/* Bytes of device workspace a forward over T tokens needs: Y and the partials.
+ * Returns 0 for a NULL handle or T < 1. */
+size_t caat_workspace_bytes(caat_handle handle, int T);
+
+/* Attaches caller-owned device memory as the workspace (16-byte aligned). */
+int caat_set_workspace(caat_handle handle, void *dev_ptr, size_t bytes);
+
+/* Whole sublayer, residual = the input x (MLP only; Eq. 9 with R = X):
+ * x [P][T][h] -> out [P][T][h].  Needs a workspace of caat_workspace_bytes(T). */
+int caat_forward(caat_handle handle, int T, const void *x, const void *W1, const void *W2,
+                 const void *gamma, void *out, void *stream);
+
+typedef struct {
+    int T;
+    const void *in;      /* x [P][T][h], or H [P][T][h/P] for CAAT_NONE */
+    const void *resid;   /* R [P][T][h]; NULL means resid = in (MLP only) */
+    const void *W1;      /* NULL for CAAT_NONE */
+    const void *W2;
+    const void *gamma;
+    const void *beta;    /* NULL means zero (LayerNorm) */
+    void *out;           /* Norm(r) [P][T][h] */
+    void *out_resid;     /* r = R + Z [P][T][h], the next residual; NULL: not stored */
+    void *stream;
+} caat_args;
+
+/* Whole sublayer with an explicit residual, beta and residual output.  The attention
+ * out-projection (CAAT_NONE) must come through here, since its input is not [P][T][h]. */
+int caat_forward_ex(caat_handle handle, const caat_args *args);
+
+/* Step a1 alone (MLP only): Y = act(x W1^T) per rank, x [P][T][h] -> Y [P][T][f_s].
+ * First sum of Eq. 22 and the nonlinearity. */
+int caat_column_gemm_act(caat_handle handle, int T, const void *x, const void *W1, void *Y,
+                         void *stream);
+
+/* Step a2 alone: partials Zt [P][T][h] = in W2^T per rank, in = Y [P][T][f_s] (MLP,
+ * second sum of Eq. 22) or H [P][T][h/P] (out-projection, Eq. 24). */
+int caat_row_gemm(caat_handle handle, int T, const void *in, const void *W2, void *partials,
+                  void *stream);
+
+/* Steps a3-a5 alone: partial channel-reduce of the given partials [P][T][h] (Eq. 22 /
+ * 24), private scaling, residual add and normalization (Eq. 9).  resid [P][T][h] is
+ * required; beta and out_resid may be NULL. */
+int caat_partial_sync_norm(caat_handle handle, int T, const void *partials, const void *resid,
+                           const void *gamma, const void *beta, void *out, void *out_resid,
+                           void *stream);
+
+/* Static text for a caat_status. */
+const char *caat_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAAT_H */

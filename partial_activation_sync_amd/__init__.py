@@ -1,0 +1,237 @@
+"""MI355X-native forward of one CAAT tensor-parallel sublayer (partially synchronized
+activations), all P ranks emulated on one GPU.
+
+This module is the thin Python binding of ``libcaat.so`` (C ABI in ``include/caat.h``):
+the functions carry the C names and only marshal arguments (tensor -> device
+pointer, torch's current stream -> hipStream_t).  Every step of the sublayer runs
+in the library's HIP kernels; there is no Python or CPU fallback, and every call
+raises if the library is missing or returns an error.
+
+Method: "Tensor-Parallelism with Partially Synchronized Activations", App. A.2,
+Eq. 22 / Eq. 24 (partial channel-reduce), §4 Eq. 9 (residual + norm), §3.2
+(logical devices).
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcaat.so")
+
+GELU, GELU_TANH, SWIGLU, NONE = 0, 1, 2, 3
+LAYERNORM, RMSNORM = 0, 1
+F32, BF16 = 0, 1
+OK, EINVAL, ENOMEM, EWORKSPACE, EDEVICE, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+ACT = {"gelu": GELU, "gelu_tanh": GELU_TANH, "swiglu": SWIGLU, "none": NONE}
+NORM = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM}
+DTYPE = {"f32": F32, "bf16": BF16}
+
+_lib = None
+
+
+class CaatError(RuntimeError):
+    def __init__(self, what, code):
+        super().__init__(f"{what}: {caat_error_string(code)} ({code})")
+        self.code = code
+
+
+class caat_args(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("in_", ctypes.c_void_p), ("resid", ctypes.c_void_p),
+                ("W1", ctypes.c_void_p), ("W2", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("out_resid", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+
+
+def lib():
+    """The loaded libcaat.so.  torch is imported first so that the library binds to the
+    HIP runtime torch already uses (one runtime, shared streams)."""
+    global _lib
+    if _lib is None:
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.caat_create.argtypes = [ctypes.POINTER(vp), i, i, i, ctypes.c_double, i, i, i]
+        L.caat_destroy.argtypes = [vp]
+        L.caat_set_eps.argtypes = [vp, ctypes.c_float]
+        L.caat_set_private_scale.argtypes = [vp, ctypes.c_float]
+        L.caat_shared_channels.argtypes = [vp]
+        L.caat_workspace_bytes.argtypes = [vp, i]
+        L.caat_workspace_bytes.restype = sz
+        L.caat_set_workspace.argtypes = [vp, vp, sz]
+        L.caat_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp]
+        L.caat_forward_ex.argtypes = [vp, ctypes.POINTER(caat_args)]
+        L.caat_column_gemm_act.argtypes = [vp, i, vp, vp, vp, vp]
+        L.caat_row_gemm.argtypes = [vp, i, vp, vp, vp, vp]
+        L.caat_partial_sync_norm.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp]
+        L.caat_error_string.argtypes = [i]
+        L.caat_error_string.restype = ctypes.c_char_p
+        for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
+                     "caat_shared_channels", "caat_set_workspace", "caat_forward",
+                     "caat_forward_ex", "caat_column_gemm_act", "caat_row_gemm",
+                     "caat_partial_sync_norm"):
+            getattr(L, name).restype = i
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL; ints pass through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("libcaat takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libcaat takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise CaatError(what, rc)
+    return rc
+
+
+def caat_error_string(code: int) -> str:
+    return lib().caat_error_string(int(code)).decode()
+
+
+def caat_create(h, ffn, P, p, norm, act, dtype):
+    handle = ctypes.c_void_p()
+    _check(lib().caat_create(ctypes.byref(handle), int(h), int(ffn), int(P), float(p),
+                             int(norm), int(act), int(dtype)), "caat_create")
+    return handle
+
+
+def caat_destroy(handle):
+    return _check(lib().caat_destroy(handle), "caat_destroy")
+
+
+def caat_set_eps(handle, eps):
+    return _check(lib().caat_set_eps(handle, float(eps)), "caat_set_eps")
+
+
+def caat_set_private_scale(handle, s):
+    return _check(lib().caat_set_private_scale(handle, float(s)), "caat_set_private_scale")
+
+
+def caat_shared_channels(handle) -> int:
+    n = lib().caat_shared_channels(handle)
+    if n < 0:
+        raise CaatError("caat_shared_channels", n)
+    return n
+
+
+def caat_workspace_bytes(handle, T) -> int:
+    return int(lib().caat_workspace_bytes(handle, int(T)))
+
+
+def caat_set_workspace(handle, ws, nbytes=None):
+    if ws is not None and nbytes is None:
+        nbytes = ws.numel() * ws.element_size()
+    return _check(lib().caat_set_workspace(handle, _ptr(ws), int(nbytes or 0)), "caat_set_workspace")
+
+
+def caat_forward(handle, T, x, W1, W2, gamma, out, stream=None):
+    return _check(lib().caat_forward(handle, int(T), _ptr(x), _ptr(W1), _ptr(W2), _ptr(gamma),
+                                     _ptr(out), _stream(stream)), "caat_forward")
+
+
+def caat_forward_ex(handle, T, inp, W1, W2, gamma, out, resid=None, beta=None, out_resid=None,
+                    stream=None):
+    a = caat_args(int(T), _ptr(inp), _ptr(resid), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(beta),
+                  _ptr(out), _ptr(out_resid), _stream(stream))
+    return _check(lib().caat_forward_ex(handle, ctypes.byref(a)), "caat_forward_ex")
+
+
+def caat_column_gemm_act(handle, T, x, W1, Y, stream=None):
+    return _check(lib().caat_column_gemm_act(handle, int(T), _ptr(x), _ptr(W1), _ptr(Y),
+                                             _stream(stream)), "caat_column_gemm_act")
+
+
+def caat_row_gemm(handle, T, inp, W2, partials, stream=None):
+    return _check(lib().caat_row_gemm(handle, int(T), _ptr(inp), _ptr(W2), _ptr(partials),
+                                      _stream(stream)), "caat_row_gemm")
+
+
+def caat_partial_sync_norm(handle, T, partials, resid, gamma, beta, out, out_resid, stream=None):
+    return _check(lib().caat_partial_sync_norm(handle, int(T), _ptr(partials), _ptr(resid),
+                                               _ptr(gamma), _ptr(beta), _ptr(out),
+                                               _ptr(out_resid), _stream(stream)),
+                  "caat_partial_sync_norm")
+
+
+class Sublayer:
+    """One sublayer handle plus a torch-allocated workspace; checks tensor shapes and
+    dtypes, then calls the C entry points (no arithmetic here)."""
+
+    def __init__(self, h, ffn, P, p, norm="layernorm", act="gelu", dtype="bf16", eps=1e-5,
+                 s_priv=1.0):
+        import torch
+        self.h, self.P, self.p = int(h), int(P), float(p)
+        self.act = ACT[act] if isinstance(act, str) else int(act)
+        self.norm = NORM[norm] if isinstance(norm, str) else int(norm)
+        self.dtype_code = DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
+        self.torch_dtype = torch.bfloat16 if self.dtype_code == BF16 else torch.float32
+        self.ffn = 0 if self.act == NONE else int(ffn)
+        self.handle = caat_create(self.h, self.ffn, self.P, self.p, self.norm, self.act,
+                                  self.dtype_code)
+        caat_set_eps(self.handle, eps)
+        caat_set_private_scale(self.handle, s_priv)
+        self.n_s = caat_shared_channels(self.handle)
+        self.f_s = self.ffn // self.P if self.act != NONE else 0
+        self.kin = self.h // self.P if self.act == NONE else self.h
+        self._ws = None
+        self._ws_T = 0
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.caat_destroy(h)
+            self.handle = None
+
+    def workspace(self, T, device="cuda"):
+        import torch
+        if self._ws is None or self._ws_T < T:
+            nbytes = caat_workspace_bytes(self.handle, T)
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            self._ws_T = T
+            caat_set_workspace(self.handle, self._ws)
+        return self._ws
+
+    def _expect(self, t, shape, name):
+        if t is None:
+            return
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != self.torch_dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {self.torch_dtype}")
+
+    def forward(self, inp, W1, W2, gamma, out, resid=None, beta=None, out_resid=None, stream=None):
+        P, h = self.P, self.h
+        T = inp.shape[1]
+        self._expect(inp, (P, T, self.kin), "in")
+        if self.act != NONE:
+            F1 = 2 * self.f_s if self.act == SWIGLU else self.f_s
+            self._expect(W1, (P, F1, h), "W1")
+        self._expect(W2, (P, h, self.f_s if self.act != NONE else self.kin), "W2")
+        self._expect(gamma, (h,), "gamma")
+        self._expect(beta, (h,), "beta")
+        self._expect(resid, (P, T, h), "resid")
+        self._expect(out, (P, T, h), "out")
+        self._expect(out_resid, (P, T, h), "out_resid")
+        self.workspace(T, inp.device)
+        return caat_forward_ex(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
+                               out, resid=resid, beta=beta, out_resid=out_resid, stream=stream)

@@ -1,0 +1,270 @@
+// libcaat: the C ABI (include/caat.h).  Argument checks, the shared-channel count,
+// workspace sizing, the device check and the launch sequence K1 -> K2 -> K3 on the
+// caller's stream.  No host synchronisation and no device allocation happen here.
+//
+// "Tensor-Parallelism with Partially Synchronized Activations": the sublayer is
+// App. A.2, Eq. 22 (MLP) / Eq. 24 (attention out-projection), followed by §4, Eq. 9
+// (residual + normalization), with every rank on one device (§3.2, logical devices).
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "caat_internal.h"
+
+#define CAAT_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+int g_arch_ok[MAX_DEVICES];  // 0 unknown, 1 gfx950, -1 other
+
+// Whether the current device is gfx950; cached per device ordinal.
+int device_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CAAT_EDEVICE;
+    if (dev < 0 || dev >= MAX_DEVICES) return CAAT_EUNSUPPORTED;
+    if (g_arch_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CAAT_EDEVICE;
+        g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return g_arch_ok[dev] == 1 ? CAAT_OK : CAAT_EUNSUPPORTED;
+}
+
+bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+bool aligned16_or_null(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t esize(const caat_ctx *c) { return c->dtype == CAAT_BF16 ? 2 : 4; }
+
+size_t y_bytes(const caat_ctx *c, int T) {
+    return c->act == CAAT_NONE ? 0 : align256((size_t)c->P * T * c->fs * esize(c));
+}
+size_t partial_bytes(const caat_ctx *c, int T) {
+    return align256((size_t)c->P * T * c->h * esize(c));
+}
+
+// Shared channels (§3: the first h p channels; Eq. 22: l < floor(h p)).  An h p that
+// lands a rounding error below an integer counts as that integer.
+int shared_count(int h, double p) {
+    const double hp = (double)h * p;
+    const double k = nearbyint(hp);
+    if (fabs(hp - k) <= 1e-9 * (double)h) return (int)k;
+    return (int)floor(hp);
+}
+
+caat::GemmArgs col_args(const caat_ctx *c, int T, const void *x, const void *W1, void *Y) {
+    caat::GemmArgs g{};
+    g.P = c->P; g.N = c->fs; g.T = T; g.K = c->h;
+    g.W = W1; g.w_stride = (size_t)c->F1 * c->h;
+    g.X = x;  g.x_stride = (size_t)T * c->h;
+    g.out = Y; g.o_stride = (size_t)T * c->fs;
+    g.up_off = c->fs;
+    switch (c->act) {
+    case CAAT_GELU: g.epi = caat::EPI_GELU; break;
+    case CAAT_GELU_TANH: g.epi = caat::EPI_GELU_TANH; break;
+    default: g.epi = caat::EPI_SWIGLU; break;
+    }
+    return g;
+}
+
+caat::GemmArgs row_args(const caat_ctx *c, int T, const void *in, const void *W2, void *Z) {
+    caat::GemmArgs g{};
+    g.P = c->P; g.N = c->h; g.T = T; g.K = c->k2;
+    g.W = W2; g.w_stride = (size_t)c->h * c->k2;
+    g.X = in; g.x_stride = (size_t)T * c->k2;
+    g.out = Z; g.o_stride = (size_t)T * c->h;
+    g.up_off = 0;
+    g.epi = caat::EPI_STORE;
+    return g;
+}
+
+int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
+    if (c->dtype == CAAT_BF16) {
+        if (!caat::gemm_bf16_supported(g)) return CAAT_EUNSUPPORTED;
+        return caat::gemm_bf16(g, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
+    }
+    return caat::gemm_f32(g, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
+}
+
+int run_psync(const caat_ctx *c, int T, const void *partials, const void *resid,
+              const void *gamma, const void *beta, void *out, void *out_resid, hipStream_t s) {
+    caat::PsyncArgs a{};
+    a.P = c->P; a.T = T; a.h = c->h; a.n_s = c->n_s; a.norm = c->norm;
+    a.s_priv = c->s_priv; a.eps = c->eps;
+    a.partials = partials; a.resid = resid; a.gamma = gamma;
+    a.beta = (c->norm == CAAT_LAYERNORM) ? beta : nullptr;
+    a.out = out; a.out_resid = out_resid;
+    return caat::psync_norm(a, c->dtype, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
+}
+
+// T limit: every per-rank operand stays addressable with 32-bit byte offsets.
+bool t_ok(const caat_ctx *c, int T) {
+    if (T < 1) return false;
+    const uint64_t widest = (uint64_t)(c->h > c->fs ? c->h : c->fs);
+    return (uint64_t)T * widest * esize(c) < 0x80000000ull;
+}
+
+}  // namespace
+
+CAAT_API int caat_create(caat_handle *out, int h, int ffn, int P, double p, int norm, int act,
+                         int dtype) {
+    if (out == nullptr) return CAAT_EINVAL;
+    *out = nullptr;
+    if (h < 8 || h > 16384 || h % 8 != 0) return CAAT_EINVAL;
+    if (P < 1 || P > 16) return CAAT_EINVAL;
+    if (!(p >= 0.0 && p <= 1.0)) return CAAT_EINVAL;  // also rejects NaN
+    if (norm != CAAT_LAYERNORM && norm != CAAT_RMSNORM) return CAAT_EINVAL;
+    if (act < CAAT_GELU || act > CAAT_NONE) return CAAT_EINVAL;
+    if (dtype != CAAT_F32 && dtype != CAAT_BF16) return CAAT_EINVAL;
+    int fs = 0, kin, k2;
+    if (act == CAAT_NONE) {
+        if (h % P != 0 || (h / P) % 8 != 0) return CAAT_EINVAL;
+        kin = h / P;
+        k2 = kin;
+        ffn = 0;
+    } else {
+        if (ffn < P || ffn % P != 0 || (ffn / P) % 8 != 0) return CAAT_EINVAL;
+        fs = ffn / P;
+        kin = h;
+        k2 = fs;
+    }
+    caat_ctx *c = new (std::nothrow) caat_ctx;
+    if (c == nullptr) return CAAT_ENOMEM;
+    memset(c, 0, sizeof(*c));
+    c->h = h; c->ffn = ffn; c->P = P; c->fs = fs;
+    c->F1 = (act == CAAT_SWIGLU) ? 2 * fs : fs;
+    c->kin = kin; c->k2 = k2;
+    c->n_s = shared_count(h, p);
+    c->norm = norm; c->act = act; c->dtype = dtype;
+    c->p = p; c->eps = 1e-5f; c->s_priv = 1.0f;
+    *out = c;
+    return CAAT_OK;
+}
+
+CAAT_API int caat_destroy(caat_handle handle) {
+    delete handle;
+    return CAAT_OK;
+}
+
+CAAT_API int caat_set_eps(caat_handle handle, float eps) {
+    if (handle == nullptr || !(eps >= 0.0f) || isinf(eps)) return CAAT_EINVAL;
+    handle->eps = eps;
+    return CAAT_OK;
+}
+
+CAAT_API int caat_set_private_scale(caat_handle handle, float s) {
+    if (handle == nullptr || !isfinite(s)) return CAAT_EINVAL;
+    handle->s_priv = s;
+    return CAAT_OK;
+}
+
+CAAT_API int caat_shared_channels(caat_handle handle) {
+    return handle == nullptr ? CAAT_EINVAL : handle->n_s;
+}
+
+CAAT_API size_t caat_workspace_bytes(caat_handle handle, int T) {
+    if (handle == nullptr || T < 1) return 0;
+    return y_bytes(handle, T) + partial_bytes(handle, T);
+}
+
+CAAT_API int caat_set_workspace(caat_handle handle, void *dev_ptr, size_t bytes) {
+    if (handle == nullptr) return CAAT_EINVAL;
+    if (dev_ptr != nullptr && !aligned16(dev_ptr)) return CAAT_EINVAL;
+    handle->ws = dev_ptr;
+    handle->ws_bytes = dev_ptr ? bytes : 0;
+    return CAAT_OK;
+}
+
+CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
+    if (c == nullptr || a == nullptr) return CAAT_EINVAL;
+    const int T = a->T;
+    if (T < 1) return CAAT_EINVAL;
+    if (!aligned16(a->in) || !aligned16(a->W2) || !aligned16(a->gamma) || !aligned16(a->out))
+        return CAAT_EINVAL;
+    if (c->act != CAAT_NONE && !aligned16(a->W1)) return CAAT_EINVAL;
+    if (!aligned16_or_null(a->resid) || !aligned16_or_null(a->beta) ||
+        !aligned16_or_null(a->out_resid))
+        return CAAT_EINVAL;
+    const void *resid = a->resid;
+    if (resid == nullptr) {
+        if (c->act == CAAT_NONE) return CAAT_EINVAL;  // H is [P][T][h/P]: not a residual
+        resid = a->in;
+    }
+    if (!t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    const size_t need = caat_workspace_bytes(c, T);
+    if (c->ws == nullptr || c->ws_bytes < need) return CAAT_EWORKSPACE;
+    int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(a->stream);
+    char *ws = reinterpret_cast<char *>(c->ws);
+    void *Y = ws;
+    void *Z = ws + y_bytes(c, T);
+    const void *gemm_in = a->in;
+    if (c->act != CAAT_NONE) {
+        rc = run_gemm(c, col_args(c, T, a->in, a->W1, Y), s);
+        if (rc != CAAT_OK) return rc;
+        gemm_in = Y;
+    }
+    rc = run_gemm(c, row_args(c, T, gemm_in, a->W2, Z), s);
+    if (rc != CAAT_OK) return rc;
+    return run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s);
+}
+
+CAAT_API int caat_forward(caat_handle c, int T, const void *x, const void *W1, const void *W2,
+                          const void *gamma, void *out, void *stream) {
+    if (c == nullptr) return CAAT_EINVAL;
+    if (c->act == CAAT_NONE) return CAAT_EINVAL;
+    caat_args a{};
+    a.T = T; a.in = x; a.resid = x; a.W1 = W1; a.W2 = W2; a.gamma = gamma;
+    a.beta = nullptr; a.out = out; a.out_resid = nullptr; a.stream = stream;
+    return caat_forward_ex(c, &a);
+}
+
+CAAT_API int caat_column_gemm_act(caat_handle c, int T, const void *x, const void *W1, void *Y,
+                                  void *stream) {
+    if (c == nullptr || c->act == CAAT_NONE) return CAAT_EINVAL;
+    if (T < 1 || !aligned16(x) || !aligned16(W1) || !aligned16(Y)) return CAAT_EINVAL;
+    if (!t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    return run_gemm(c, col_args(c, T, x, W1, Y), reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API int caat_row_gemm(caat_handle c, int T, const void *in, const void *W2, void *partials,
+                           void *stream) {
+    if (c == nullptr) return CAAT_EINVAL;
+    if (T < 1 || !aligned16(in) || !aligned16(W2) || !aligned16(partials)) return CAAT_EINVAL;
+    if (!t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    return run_gemm(c, row_args(c, T, in, W2, partials), reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API int caat_partial_sync_norm(caat_handle c, int T, const void *partials, const void *resid,
+                                    const void *gamma, const void *beta, void *out,
+                                    void *out_resid, void *stream) {
+    if (c == nullptr || T < 1) return CAAT_EINVAL;
+    if (!aligned16(partials) || !aligned16(resid) || !aligned16(gamma) || !aligned16(out))
+        return CAAT_EINVAL;
+    if (!aligned16_or_null(beta) || !aligned16_or_null(out_resid)) return CAAT_EINVAL;
+    if (!t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    return run_psync(c, T, partials, resid, gamma, beta, out, out_resid,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API const char *caat_error_string(int code) {
+    switch (code) {
+    case CAAT_OK: return "success";
+    case CAAT_EINVAL: return "invalid argument";
+    case CAAT_ENOMEM: return "host allocation failed";
+    case CAAT_EWORKSPACE: return "workspace missing or too small";
+    case CAAT_EDEVICE: return "HIP call or kernel launch failed";
+    case CAAT_EUNSUPPORTED: return "unsupported device or size";
+    default: return "unknown status";
+    }
+}

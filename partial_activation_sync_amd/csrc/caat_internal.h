@@ -1,0 +1,60 @@
+// Internal declarations shared by the libcaat sources (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "caat.h"
+
+struct caat_ctx {
+    int h;        // hidden size
+    int ffn;      // full FFN size (0 for the out-projection)
+    int P;        // emulated tensor-parallel ranks
+    int fs;       // ffn / P: Y columns per rank
+    int F1;       // W1 rows per rank: fs, or 2 fs for SwiGLU
+    int kin;      // input width: h (MLP) or h / P (out-projection)
+    int k2;       // contraction length of the row-parallel GEMM: fs or h / P
+    int n_s;      // shared channels [0, n_s)
+    int norm;     // caat_norm
+    int act;      // caat_act
+    int dtype;    // caat_dtype
+    double p;     // sync fraction as given
+    float eps;    // normalization epsilon
+    float s_priv; // private channel scale
+    void *ws;     // caller's workspace
+    size_t ws_bytes;
+};
+
+namespace caat {
+
+// Epilogues of the GEMM kernels.
+enum Epilogue { EPI_STORE = 0, EPI_GELU = 1, EPI_GELU_TANH = 2, EPI_SWIGLU = 3 };
+
+// One shard-batched "NT" GEMM: for every rank m, token t < T and output column n < N,
+//   acc = sum_{k < K} W[m][row(n)][k] * X[m][t][k]
+// and out[m][t][n] = epilogue(acc).  For EPI_SWIGLU, N counts Y columns and column n
+// uses W rows n (gate) and up_off + n (up): out = silu(gate) * up.
+struct GemmArgs {
+    int P, N, T, K;
+    const void *W;  size_t w_stride;   // elements between ranks; rows of K elements
+    const void *X;  size_t x_stride;   // elements between ranks; rows of K elements
+    void *out;      size_t o_stride;   // elements between ranks; rows of N elements
+    int up_off;                        // SwiGLU: W row offset of the up projection
+    int epi;
+};
+
+hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s);
+hipError_t gemm_f32(const GemmArgs &a, hipStream_t s);
+bool gemm_bf16_supported(const GemmArgs &a);
+
+struct PsyncArgs {
+    int P, T, h, n_s, norm;
+    float s_priv, eps;
+    const void *partials, *resid, *gamma, *beta;
+    void *out, *out_resid;
+};
+
+hipError_t psync_norm(const PsyncArgs &a, int dtype, hipStream_t s);
+
+}  // namespace caat

@@ -1,0 +1,259 @@
+// K3: partial channel-reduce + private scaling + residual add + LayerNorm/RMSNorm.
+//
+// "Tensor-Parallelism with Partially Synchronized Activations": the reduce is the
+// sum over ranks of channels l < n_s only (App. A.2, Eq. 22 / Eq. 24); private
+// channels keep the rank's own value, times s_priv (§4, private channel scaling);
+// then each rank adds its own residual and normalizes (§4, Eq. 9).  All ranks are
+// on this device ("logical devices", §3.2), so the reduce is a local sum.
+//
+// HBM-bound.  One workgroup per token t.  Thread i owns 8-channel chunks
+// c = i + j * blockDim (j < NCH), the same chunks for every rank, so:
+//   phase A: S[c] = sum over m (ascending, fp32) of partials[m][t][c], shared chunks only;
+//   phase B: ranks in groups of G: r = resid + (l < n_s ? S : s_priv * partial),
+//            row statistics by wave reductions + one LDS exchange, normalize, store.
+// Every partial element is read exactly once (shared part in A, private part in B),
+// the channel mask is a per-element integer compare in registers, and the reduction
+// order is fixed (no atomics), so results are run-to-run deterministic.
+#include "caat_internal.h"
+
+namespace caat {
+namespace {
+
+constexpr int G = 4;            // ranks normalized per LDS exchange
+constexpr int MAX_WAVES = 4;    // blockDim <= 256
+
+template <typename TIO> struct Vec8;
+
+template <> struct Vec8<__bf16> {
+    static __device__ __forceinline__ void load(const __bf16 *p, float (&v)[8]) {
+        uint4 u = *reinterpret_cast<const uint4 *>(p);
+        uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(__bf16 *p, const float (&v)[8]) {
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = static_cast<__bf16>(v[i]);
+        *reinterpret_cast<bf16x8 *>(p) = b;
+    }
+};
+
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float *p, float (&v)[8]) {
+        float4 a = *reinterpret_cast<const float4 *>(p);
+        float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float (&v)[8]) {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sums v[g] over the whole block (fixed order); red is LDS [MAX_WAVES][G].
+__device__ __forceinline__ void block_sum(float (&v)[G], float *red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = wave_sum(v[g]);
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) red[wave * G + g] = v[g];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float s = 0.f;
+        for (int w = 0; w < nwaves; ++w) s += red[w * G + g];
+        v[g] = s;
+    }
+}
+
+template <int NCH, int NORM, typename TIO>
+__global__ __launch_bounds__(256) void k_psync_norm(
+    int P, int T, int h, int n_s, float s_priv, float eps,
+    const TIO *__restrict__ partials, const TIO *__restrict__ resid,
+    const TIO *__restrict__ gamma, const TIO *__restrict__ beta,
+    TIO *__restrict__ out, TIO *__restrict__ out_resid)
+{
+    // Two reduction buffers, used alternately: a buffer is rewritten only after the
+    // barrier of the reduction in between, so one barrier per reduction suffices.
+    __shared__ float red[2][MAX_WAVES * G];
+    int rbuf = 0;
+
+    const int t = blockIdx.x;
+    const int nchunk = h >> 3;
+    const size_t rank_stride = (size_t)T * h;
+    const size_t row = (size_t)t * h;
+    const float inv_h = 1.0f / (float)h;
+
+    int ch0[NCH];
+    bool valid[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        int c = threadIdx.x + j * blockDim.x;
+        valid[j] = c < nchunk;
+        ch0[j] = c * 8;
+    }
+
+    // Phase A: the partial channel-reduce, S = sum_m partials[m] on shared chunks.
+    float S[NCH][8];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S[j][e] = 0.f;
+    for (int m = 0; m < P; ++m) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (valid[j] && ch0[j] < n_s) {
+                float z[8];
+                Vec8<TIO>::load(partials + m * rank_stride + row + ch0[j], z);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) S[j][e] += z[e];
+            }
+        }
+    }
+
+    // Phase B: per rank group, residual add + normalization.
+    for (int m0 = 0; m0 < P; m0 += G) {
+        float r[G][NCH][8];
+        float acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            acc[g] = 0.f;
+            const int m = m0 + g;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[g][j][e] = 0.f;
+                if (m < P && valid[j]) {
+                    const size_t off = m * rank_stride + row + ch0[j];
+                    float res[8], z[8];
+                    Vec8<TIO>::load(resid + off, res);
+                    if (ch0[j] + 8 > n_s) Vec8<TIO>::load(partials + off, z);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool shared = ch0[j] + e < n_s;
+                        const float zz = shared ? S[j][e] : s_priv * z[e];
+                        r[g][j][e] = res[e] + zz;
+                        acc[g] += r[g][j][e];
+                    }
+                }
+            }
+        }
+        float mean[G], inv[G];
+        if (NORM == CAAT_LAYERNORM) {
+            block_sum(acc, red[rbuf]);
+            rbuf ^= 1;
+#pragma unroll
+            for (int g = 0; g < G; ++g) mean[g] = acc[g] * inv_h;
+            // Second pass over the register-resident row: biased variance.
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float q = 0.f;
+#pragma unroll
+                for (int j = 0; j < NCH; ++j)
+                    if (valid[j])
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float d = r[g][j][e] - mean[g];
+                            q += d * d;
+                        }
+                acc[g] = q;
+            }
+            block_sum(acc, red[rbuf]);
+            rbuf ^= 1;
+#pragma unroll
+            for (int g = 0; g < G; ++g) inv[g] = rsqrtf(acc[g] * inv_h + eps);
+        } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float q = 0.f;
+#pragma unroll
+                for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) q += r[g][j][e] * r[g][j][e];
+                acc[g] = q;
+                mean[g] = 0.f;
+            }
+            block_sum(acc, red[rbuf]);
+            rbuf ^= 1;
+#pragma unroll
+            for (int g = 0; g < G; ++g) inv[g] = rsqrtf(acc[g] * inv_h + eps);
+        }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (!valid[j]) continue;
+            float gm[8], bt[8];
+            Vec8<TIO>::load(gamma + ch0[j], gm);
+            if (NORM == CAAT_LAYERNORM && beta != nullptr) {
+                Vec8<TIO>::load(beta + ch0[j], bt);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bt[e] = 0.f;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int m = m0 + g;
+                if (m >= P) break;
+                const size_t off = m * rank_stride + row + ch0[j];
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = (r[g][j][e] - mean[g]) * inv[g] * gm[e] + bt[e];
+                Vec8<TIO>::store(out + off, o);
+                if (out_resid != nullptr) Vec8<TIO>::store(out_resid + off, r[g][j]);
+            }
+        }
+    }
+}
+
+template <int NORM, typename TIO>
+hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
+    const int nchunk = a.h / 8;
+    int nch = 1;
+    while (nch < 8 && nchunk > nch * 256) nch *= 2;
+    int threads = (nchunk + nch - 1) / nch;
+    threads = (threads + 63) / 64 * 64;
+    dim3 grid(a.T), block(threads);
+    auto P = reinterpret_cast<const TIO *>(a.partials);
+    auto R = reinterpret_cast<const TIO *>(a.resid);
+    auto Gm = reinterpret_cast<const TIO *>(a.gamma);
+    auto B = reinterpret_cast<const TIO *>(a.beta);
+    auto O = reinterpret_cast<TIO *>(a.out);
+    auto OR = reinterpret_cast<TIO *>(a.out_resid);
+#define CAAT_K3(N)                                                                     \
+    hipLaunchKernelGGL((k_psync_norm<N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
+                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR)
+    switch (nch) {
+    case 1: CAAT_K3(1); break;
+    case 2: CAAT_K3(2); break;
+    case 4: CAAT_K3(4); break;
+    default: CAAT_K3(8); break;
+    }
+#undef CAAT_K3
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t psync_norm(const PsyncArgs &a, int dtype, hipStream_t s) {
+    if (dtype == CAAT_BF16)
+        return a.norm == CAAT_LAYERNORM ? launch_t<CAAT_LAYERNORM, __bf16>(a, s)
+                                        : launch_t<CAAT_RMSNORM, __bf16>(a, s);
+    return a.norm == CAAT_LAYERNORM ? launch_t<CAAT_LAYERNORM, float>(a, s)
+                                    : launch_t<CAAT_RMSNORM, float>(a, s);
+}
+
+}  // namespace caat

@@ -1,0 +1,130 @@
+"""Runs a workload (see ``workloads``) through libcaat on the GPU.
+
+Inputs come from ``synth`` (seeded, CPU) and are copied to the device once; a step
+then only enqueues the library's kernels.  No arithmetic of the method happens here.
+
+Input recipe (tensor ids from ``synth``):
+  MLP-only workloads: x ~ N(0,1) [P][T][h] (one draw copied to every rank when the
+    workload says so), W1 ~ N(0, 0.02^2) [P][F1][h], W2 ~ N(0, 0.02^2) [P][h][f_s];
+    the residual is x itself.
+  Pair workloads: H ~ N(0,1) [P][T][h/P] (per-rank head outputs), x0 ~ N(0,1)
+    [P][T][h] (the residual entering the attention sublayer), Wo ~ N(0, 0.02^2)
+    [P][h][h/P]; then the MLP takes the attention output as input and the
+    attention's residual output as residual.
+  gamma = 1, beta = 0 ("unit"), or gamma ~ 1 + N(0, 0.1^2), beta ~ N(0, 0.1^2) ("random").
+"""
+import torch
+
+from . import synth
+from .workloads import ATTN_OUT, MLP, Workload
+from . import Sublayer, caat_column_gemm_act, caat_row_gemm, caat_partial_sync_norm
+
+WEIGHT_STD = 0.02
+
+
+def torch_dtype(w: Workload):
+    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+
+def make_inputs(w: Workload, T=None, norm_params="unit", seed=synth.BASE_SEED):
+    """CPU tensors for one workload (weights do not depend on T)."""
+    T = w.T if T is None else T
+    P, h, fs = w.P, w.h, w.f_s
+    dt = torch_dtype(w)
+    F1 = 2 * fs if w.act == "swiglu" else fs
+    d = {}
+    if ATTN_OUT in w.sublayers:
+        d["ctx"] = synth.normal((P, T, h // P), synth.CTX, dtype=dt, seed=seed)
+        d["x0"] = synth.normal((P, T, h), synth.X0, dtype=dt, seed=seed)
+        d["Wo"] = synth.normal((P, h, h // P), synth.WO, std=WEIGHT_STD, dtype=dt, seed=seed)
+    else:
+        if w.replicated_x:
+            d["x"] = synth.replicated((T, h), P, synth.X, dtype=dt, seed=seed)
+        else:
+            d["x"] = synth.normal((P, T, h), synth.X, dtype=dt, seed=seed)
+    d["W1"] = synth.normal((P, F1, h), synth.W1, std=WEIGHT_STD, dtype=dt, seed=seed)
+    d["W2"] = synth.normal((P, h, fs), synth.W2, std=WEIGHT_STD, dtype=dt, seed=seed)
+    if norm_params == "unit":
+        d["gamma"] = torch.ones(h, dtype=dt)
+        d["beta"] = torch.zeros(h, dtype=dt)
+    else:
+        d["gamma"] = synth.normal((h,), synth.GAMMA, std=0.1, mean=1.0, dtype=dt, seed=seed)
+        d["beta"] = synth.normal((h,), synth.BETA, std=0.1, dtype=dt, seed=seed)
+    return d
+
+
+class Run:
+    """Device-resident inputs, outputs and handles for one workload at one T."""
+
+    def __init__(self, w: Workload, inputs: dict, p=None, s_priv=1.0, device="cuda",
+                 store_resid=True):
+        self.w = w
+        self.p = w.p if p is None else p
+        self.dev = {k: v.to(device) for k, v in inputs.items()}
+        P, h = w.P, w.h
+        self.T = T = (self.dev["ctx"] if "ctx" in self.dev else self.dev["x"]).shape[1]
+        dt = torch_dtype(w)
+        self.attn = None
+        if ATTN_OUT in w.sublayers:
+            self.attn = Sublayer(h, 0, P, self.p, norm=w.norm, act="none", dtype=w.dtype,
+                                 eps=w.eps, s_priv=s_priv)
+            self.attn.workspace(T, device)
+            self.attn_out = torch.empty((P, T, h), dtype=dt, device=device)
+            self.attn_out_resid = torch.empty((P, T, h), dtype=dt, device=device)
+        self.mlp = Sublayer(h, w.ffn, P, self.p, norm=w.norm, act=w.act, dtype=w.dtype,
+                            eps=w.eps, s_priv=s_priv)
+        self.mlp.workspace(T, device)
+        self.out = torch.empty((P, T, h), dtype=dt, device=device)
+        self.out_resid = torch.empty((P, T, h), dtype=dt, device=device) if store_resid else None
+
+    def step(self, stream=None):
+        """One forward of the whole path (out-projection sublayer, then the MLP)."""
+        d = self.dev
+        if self.attn is not None:
+            self.attn.forward(d["ctx"], None, d["Wo"], d["gamma"], self.attn_out, resid=d["x0"],
+                              beta=d["beta"], out_resid=self.attn_out_resid, stream=stream)
+            mlp_in, mlp_resid = self.attn_out, self.attn_out_resid
+        else:
+            mlp_in, mlp_resid = d["x"], d["x"]
+        self.mlp.forward(mlp_in, d["W1"], d["W2"], d["gamma"], self.out, resid=mlp_resid,
+                         beta=d["beta"], out_resid=self.out_resid, stream=stream)
+
+    def outputs(self):
+        o = {"out": self.out}
+        if self.out_resid is not None:
+            o["out_resid"] = self.out_resid
+        if self.attn is not None:
+            o["attn_out"] = self.attn_out
+            o["attn_out_resid"] = self.attn_out_resid
+        return o
+
+    # The three steps of one sublayer, for per-kernel timing.
+    def mlp_steps(self):
+        """Callables for K1, K2 and K3 of the MLP sublayer on its workspace buffers."""
+        d, s = self.dev, self.mlp
+        T, P, h, fs = self.T, self.w.P, self.w.h, self.w.f_s
+        ws = s.workspace(T)
+        es = ws.new_empty(0, dtype=torch_dtype(self.w)).element_size()
+        y_elems = P * T * fs
+        y_bytes = (y_elems * es + 255) // 256 * 256
+        Y = ws[:y_elems * es].view(torch_dtype(self.w)).view(P, T, fs)
+        Z = ws[y_bytes:y_bytes + P * T * h * es].view(torch_dtype(self.w)).view(P, T, h)
+        mlp_in = self.attn_out if self.attn is not None else d["x"]
+        mlp_resid = self.attn_out_resid if self.attn is not None else d["x"]
+        k1 = lambda: caat_column_gemm_act(s.handle, T, mlp_in, d["W1"], Y)
+        k2 = lambda: caat_row_gemm(s.handle, T, Y, d["W2"], Z)
+        k3 = lambda: caat_partial_sync_norm(s.handle, T, Z, mlp_resid, d["gamma"], d["beta"],
+                                            self.out, self.out_resid)
+        return k1, k2, k3
+
+    def attn_steps(self):
+        """Callables for K2 and K3 of the out-projection sublayer."""
+        d, s = self.dev, self.attn
+        T, P, h = self.T, self.w.P, self.w.h
+        ws = s.workspace(T)
+        Z = ws[:P * T * h * ws.new_empty(0, dtype=torch_dtype(self.w)).element_size()]
+        Z = Z.view(torch_dtype(self.w)).view(P, T, h)
+        k2 = lambda: caat_row_gemm(s.handle, T, d["ctx"], d["Wo"], Z)
+        k3 = lambda: caat_partial_sync_norm(s.handle, T, Z, d["x0"], d["gamma"], d["beta"],
+                                            self.attn_out, self.attn_out_resid)
+        return k2, k3

@@ -1,0 +1,127 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the header
+declares, and validates arguments before touching any device (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import partial_activation_sync_amd as caat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "caat.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(caat_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert len(declared) >= 13
+    nm = subprocess.run(["nm", "-D", "--defined-only", caat.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (caat_\w+)", nm))
+    missing = [d for d in declared if d not in exported]
+    assert not missing, missing
+    L = caat.lib()
+    for d in declared:
+        assert getattr(L, d) is not None
+
+
+def test_binding_names_match_header():
+    for d in _declared():
+        assert callable(getattr(caat, d)), d
+
+
+@pytest.mark.parametrize("h,p", [(4096, 0.5), (2048, 0.25), (768, 0.5), (256, 0.5), (104, 0.29),
+                                 (4096, 0.703125), (4096, 1 / 3), (8, 0.0), (8, 1.0), (16, 0.9999999999)])
+def test_shared_channels_agree_with_oracle(h, p):
+    hd = caat.caat_create(h, 8 * 4, 4, p, caat.LAYERNORM, caat.GELU, caat.BF16)
+    try:
+        assert caat.caat_shared_channels(hd) == oracle.shared_channels(h, p)
+    finally:
+        caat.caat_destroy(hd)
+
+
+@pytest.mark.parametrize("args", [
+    (0, 64, 2, 0.5, 0, 0, 1),          # h < 8
+    (100, 64, 2, 0.5, 0, 0, 1),        # h % 8
+    (16392, 64, 2, 0.5, 0, 0, 1),      # h too large
+    (64, 64, 0, 0.5, 0, 0, 1),         # P < 1
+    (64, 64 * 17, 17, 0.5, 0, 0, 1),   # P > 16
+    (64, 64, 2, -0.1, 0, 0, 1),        # p < 0
+    (64, 64, 2, 1.5, 0, 0, 1),         # p > 1
+    (64, 64, 2, float("nan"), 0, 0, 1),
+    (64, 64, 2, 0.5, 2, 0, 1),         # norm
+    (64, 64, 2, 0.5, 0, 4, 1),         # act
+    (64, 64, 2, 0.5, 0, 0, 2),         # dtype
+    (64, 63, 2, 0.5, 0, 0, 1),         # ffn % P
+    (64, 36, 3, 0.5, 0, 0, 1),         # (ffn / P) % 8
+    (64, 0, 3, 0.5, 0, 3, 1),          # out-projection: h % P
+    (24, 0, 2, 0.5, 0, 3, 1),          # out-projection: (h / P) % 8
+])
+def test_create_rejects(args):
+    handle = ctypes.c_void_p()
+    rc = caat.lib().caat_create(ctypes.byref(handle), *args)
+    assert rc == caat.EINVAL
+    assert not handle.value
+
+
+def test_setters_and_workspace_size():
+    hd = caat.caat_create(256, 1024, 2, 0.5, caat.LAYERNORM, caat.SWIGLU, caat.BF16)
+    L = caat.lib()
+    assert L.caat_set_eps(hd, -1.0) == caat.EINVAL
+    assert L.caat_set_eps(hd, float("nan")) == caat.EINVAL
+    assert L.caat_set_private_scale(hd, float("inf")) == caat.EINVAL
+    caat.caat_set_eps(hd, 1e-6)
+    caat.caat_set_private_scale(hd, 2 ** 0.5)
+    # Y [P][T][f_s] + partials [P][T][h], each rounded up to 256 bytes.
+    T = 37
+    y = (2 * T * 512 * 2 + 255) // 256 * 256
+    z = (2 * T * 256 * 2 + 255) // 256 * 256
+    assert caat.caat_workspace_bytes(hd, T) == y + z
+    assert caat.caat_workspace_bytes(hd, 0) == 0
+    assert L.caat_set_workspace(hd, 0x1008, 64) == caat.EINVAL   # misaligned
+    caat.caat_destroy(hd)
+    att = caat.caat_create(256, 0, 2, 0.5, caat.RMSNORM, caat.NONE, caat.F32)
+    assert caat.caat_workspace_bytes(att, T) == (2 * T * 256 * 4 + 255) // 256 * 256
+    caat.caat_destroy(att)
+
+
+def test_forward_checks_before_any_launch():
+    L = caat.lib()
+    hd = caat.caat_create(256, 1024, 2, 0.5, caat.LAYERNORM, caat.GELU, caat.BF16)
+    fake = 0x10000  # aligned, never dereferenced: every call below fails its checks first
+    st = None
+    assert L.caat_forward(None, 4, fake, fake, fake, fake, fake, st) == caat.EINVAL
+    assert L.caat_forward(hd, 0, fake, fake, fake, fake, fake, st) == caat.EINVAL
+    assert L.caat_forward(hd, 4, None, fake, fake, fake, fake, st) == caat.EINVAL
+    assert L.caat_forward(hd, 4, fake + 2, fake, fake, fake, fake, st) == caat.EINVAL
+    assert L.caat_forward(hd, 4, fake, fake, fake, fake, fake, st) == caat.EWORKSPACE
+    caat.caat_set_workspace(hd, fake, 16)
+    assert L.caat_forward(hd, 4, fake, fake, fake, fake, fake, st) == caat.EWORKSPACE
+    assert L.caat_column_gemm_act(hd, 4, fake, None, fake, st) == caat.EINVAL
+    assert L.caat_row_gemm(hd, 0, fake, fake, fake, st) == caat.EINVAL
+    assert L.caat_partial_sync_norm(hd, 4, fake, None, fake, None, fake, None, st) == caat.EINVAL
+    assert L.caat_partial_sync_norm(hd, 4, fake, fake, fake, fake + 4, fake, None, st) == caat.EINVAL
+    caat.caat_destroy(hd)
+    att = caat.caat_create(256, 0, 2, 0.5, caat.RMSNORM, caat.NONE, caat.BF16)
+    assert L.caat_forward(att, 4, fake, fake, fake, fake, fake, st) == caat.EINVAL   # needs _ex
+    assert L.caat_column_gemm_act(att, 4, fake, fake, fake, st) == caat.EINVAL
+    a = caat.caat_args(4, fake, None, None, fake, fake, None, fake, None, None)
+    assert L.caat_forward_ex(att, ctypes.byref(a)) == caat.EINVAL                     # resid needed
+    caat.caat_destroy(att)
+
+
+def test_error_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert caat.caat_error_string(code) != "unknown status"
+    assert caat.caat_error_string(7) == "unknown status"
+    with pytest.raises(caat.CaatError) as e:
+        caat.caat_create(7, 8, 1, 0.5, 0, 0, 1)
+    assert e.value.code == caat.EINVAL

@@ -1,0 +1,218 @@
+"""GPU parity: libcaat (HIP, gfx950) against the fp64 oracle on the same seeded inputs.
+
+Bar (per output tensor): max |gpu - oracle| / max |oracle| <= 1e-4 for fp32 storage,
+<= 2e-2 for bf16 storage.  The channel mask is checked bit-exactly on integer-coded
+partials.  Full-size workloads are compared on sampled token rows (token rows never
+interact, so a row's oracle value does not depend on the others).
+"""
+import math
+
+import pytest
+import torch
+
+import oracle
+import partial_activation_sync_amd as caat
+from partial_activation_sync_amd import runner, synth, workloads as W
+from tests.oracle_ref import TOL, compare, reference
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run_and_compare(w, T=None, p=None, s_priv=1.0, norm_params="unit", rows=None):
+    _say(f"[case] {w.name} T={T or w.T} p={p if p is not None else w.p} s={s_priv} "
+         f"norm_params={norm_params} rows={'all' if rows is None else len(rows)}")
+    inputs = runner.make_inputs(w, T=T, norm_params=norm_params)
+    run = runner.Run(w, inputs, p=p, s_priv=s_priv)
+    run.step()
+    torch.cuda.synchronize()
+    ref = reference(w, inputs, rows=rows, p=p, s_priv=s_priv)
+    errs = compare(w, run.outputs(), ref, rows=rows)
+    _say("   errors:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert {"out", "out_resid"} <= set(errs), errs
+    for k, e in errs.items():
+        assert e <= TOL[w.dtype], (k, e)
+    return run, inputs
+
+
+# ---------------------------------------------------------------------------
+# Workloads at sizes the oracle finishes in seconds: several tiles + a ragged tail
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("s_priv", [1.0, math.sqrt(2.0)])
+@pytest.mark.parametrize("norm_params", ["unit", "random"])
+def test_tiny_mlp_fp32_full(s_priv, norm_params):
+    _run_and_compare(W.TINY_MLP_F32, s_priv=s_priv, norm_params=norm_params)
+
+
+def test_tiny_mlp_fp32_ragged():
+    _run_and_compare(W.TINY_MLP_F32, T=77, norm_params="random")
+
+
+@pytest.mark.parametrize("T", [1, 300])
+def test_130m_pair_ragged(T):
+    _run_and_compare(W.PAIR_130M_BF16, T=T, norm_params="random")
+
+
+@pytest.mark.parametrize("p", W.SWEEP_P_1P1B)
+def test_1p1b_mlp_ragged(p):
+    _run_and_compare(W.MLP_1P1B_BF16, T=300, p=p, norm_params="random")
+
+
+def test_7b_prefill_ragged():
+    _run_and_compare(W.PREFILL_7B_BF16, T=131, norm_params="random")
+
+
+@pytest.mark.parametrize("T", W.DECODE_T)
+def test_7b_decode_full(T):
+    _run_and_compare(W.DECODE_7B_BF16, T=T)
+
+
+# ---------------------------------------------------------------------------
+# Full sizes, in the launch configuration the benchmark times: sampled rows
+# ---------------------------------------------------------------------------
+def test_130m_pair_full_size_sampled():
+    w = W.PAIR_130M_BF16
+    _run_and_compare(w, rows=synth.sample_rows(w.T, 64))
+
+
+@pytest.mark.parametrize("p", W.SWEEP_P_1P1B)
+def test_1p1b_mlp_full_size_sampled(p):
+    w = W.MLP_1P1B_BF16
+    _run_and_compare(w, p=p, rows=synth.sample_rows(w.T, 64))
+
+
+def test_7b_prefill_full_size_sampled():
+    w = W.PREFILL_7B_BF16
+    _run_and_compare(w, rows=synth.sample_rows(w.T, 64))
+
+
+# ---------------------------------------------------------------------------
+# Steps on their own
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wname,T", [("tiny-mlp-fp32", 128), ("1.1b-mlp-bf16", 200),
+                                     ("130m-pair-bf16", 100)])
+def test_partials_match_oracle(wname, T):
+    """K1 + K2 alone: the per-rank partials Zt before any reduction."""
+    w = W.ALL[wname]
+    _say(f"[case] partials {wname} T={T}")
+    inputs = runner.make_inputs(w, T=T)
+    d = {k: v.cuda() for k, v in inputs.items()}
+    s = caat.Sublayer(w.h, w.ffn, w.P, w.p, norm=w.norm, act=w.act, dtype=w.dtype)
+    dt = runner.torch_dtype(w)
+    x = d["x"] if "x" in d else synth.normal((w.P, T, w.h), synth.X, dtype=dt).cuda()
+    Y = torch.empty((w.P, T, w.f_s), dtype=dt, device="cuda")
+    Z = torch.empty((w.P, T, w.h), dtype=dt, device="cuda")
+    caat.caat_column_gemm_act(s.handle, T, x, d["W1"], Y)
+    caat.caat_row_gemm(s.handle, T, Y, d["W2"], Z)
+    torch.cuda.synchronize()
+    act = {"gelu": oracle.GELU, "gelu_tanh": oracle.GELU_TANH, "swiglu": oracle.SWIGLU}[w.act]
+    _, _, zt = oracle.sublayer(x.cpu(), inputs["W1"], inputs["W2"], inputs["gamma"], act=act,
+                               norm=oracle.RMSNORM, n_s=0, want_partials=True)
+    err = (Z.double().cpu().numpy() - zt).__abs__().max() / abs(zt).max()
+    _say(f"   partials error {err:.2e}")
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh", "swiglu"])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_activation_and_norm_variants(act, norm):
+    w = W.with_(W.MLP_1P1B_BF16, act=act, norm=norm, P=4, h=512, ffn=4 * 264, T=260, p=0.3)
+    _run_and_compare(w, norm_params="random", s_priv=2.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("P,h,ffn,T", [(1, 8, 8, 1), (16, 128, 16 * 8, 5), (3, 264, 3 * 40, 67),
+                                       (5, 200, 5 * 48, 129)])
+def test_edge_shapes(dtype, P, h, ffn, T):
+    for act in ("gelu", "swiglu"):
+        w = W.with_(W.TINY_MLP_F32, dtype=dtype, P=P, h=h, ffn=ffn, T=T, p=0.37, act=act,
+                    norm="layernorm", replicated_x=False)
+        _run_and_compare(w, norm_params="random")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_out_projection_edge_shapes(dtype):
+    w = W.with_(W.PAIR_130M_BF16, dtype=dtype, P=2, h=272, ffn=2 * 136, T=45, p=0.61)
+    _run_and_compare(w, norm_params="random")
+
+
+# ---------------------------------------------------------------------------
+# The channel mask, bit-exact; cross-rank identity at p = 1; determinism
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("h", [256, 4096])
+def test_mask_bit_exact(dtype, P, h):
+    """Integer-coded partials Zt_m = 2^m, resid = 0: out_resid = 2^P - 1 on shared
+    channels and 2^m * s_priv on private ones, exactly (representable in bf16)."""
+    T = 3
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for n_s in sorted({0, 1, 63, 64, 65, 179, h - 1, h}):
+        p = n_s / h
+        s = caat.Sublayer(h, 8 * P, P, p, norm="rmsnorm", act="gelu", dtype=dtype, s_priv=2.0)
+        assert s.n_s == n_s
+        Z = torch.stack([torch.full((T, h), 2.0 ** m, dtype=dt) for m in range(P)]).cuda()
+        resid = torch.zeros((P, T, h), dtype=dt, device="cuda")
+        gamma = torch.ones(h, dtype=dt, device="cuda")
+        out = torch.empty_like(resid)
+        out_resid = torch.empty_like(resid)
+        caat.caat_partial_sync_norm(s.handle, T, Z, resid, gamma, None, out, out_resid)
+        torch.cuda.synchronize()
+        want = torch.empty((P, T, h), dtype=torch.float64)
+        for m in range(P):
+            want[m, :, :n_s] = 2.0 ** P - 1
+            want[m, :, n_s:] = 2.0 ** m * 2.0
+        assert torch.equal(out_resid.double().cpu(), want), (P, h, n_s)
+
+
+def test_p1_ranks_bitwise_identical():
+    w = W.with_(W.MLP_1P1B_BF16, T=96, replicated_x=True, p=1.0)
+    inputs = runner.make_inputs(w, norm_params="random")
+    run = runner.Run(w, inputs)
+    run.step()
+    torch.cuda.synchronize()
+    for m in range(1, w.P):
+        assert torch.equal(run.out[m], run.out[0])
+        assert torch.equal(run.out_resid[m], run.out_resid[0])
+
+
+def test_p_below_1_ranks_differ_only_in_private_channels():
+    w = W.with_(W.MLP_1P1B_BF16, T=32, replicated_x=True, p=0.25)
+    run = runner.Run(w, runner.make_inputs(w))
+    run.step()
+    torch.cuda.synchronize()
+    n_s = run.mlp.n_s
+    r = run.out_resid
+    for m in range(1, w.P):
+        assert torch.equal(r[m, :, :n_s], r[0, :, :n_s])
+        assert not torch.equal(r[m, :, n_s:], r[0, :, n_s:])
+
+
+def test_run_to_run_deterministic():
+    w = W.with_(W.PREFILL_7B_BF16, T=520)
+    run = runner.Run(w, runner.make_inputs(w, norm_params="random"))
+    run.step()
+    first = {k: v.clone() for k, v in run.outputs().items()}
+    for _ in range(3):
+        run.step()
+    torch.cuda.synchronize()
+    for k, v in run.outputs().items():
+        assert torch.equal(v, first[k]), k
+
+
+def test_forward_plain_entry_point():
+    """caat_forward (residual = input, no out_resid) against the oracle."""
+    w = W.with_(W.MLP_1P1B_BF16, T=70)
+    inputs = runner.make_inputs(w)
+    d = {k: v.cuda() for k, v in inputs.items()}
+    s = caat.Sublayer(w.h, w.ffn, w.P, w.p, norm=w.norm, act=w.act, dtype=w.dtype)
+    s.workspace(w.T)
+    out = torch.empty_like(d["x"])
+    caat.caat_forward(s.handle, w.T, d["x"], d["W1"], d["W2"], d["gamma"], out)
+    torch.cuda.synchronize()
+    ref = reference(w, inputs)
+    errs = compare(w, {"out": out}, ref)
+    assert errs["out"] <= TOL[w.dtype]
