@@ -1,0 +1,217 @@
+"""Benchmark: tokens/s of the CAAT partial-sync sublayer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T] [--p P]
+
+A step is one pass of the whole path over one batch: for a pair workload the
+attention out-projection sublayer (row-parallel GEMM K2, then the fused partial
+channel-reduce + residual + norm K3) followed by the MLP sublayer (K1 column-parallel
+GEMM + activation, K2, K3), all P ranks emulated on the one GPU.  Inputs are resident
+in HBM before the timed region starts.  Each kernel is enqueued through its own C
+entry point with an event between consecutive kernels on the stream the library
+launches on, which yields the step time and every kernel's average duration from the
+same timed steps.
+
+Prints ONE JSON line on stdout (details on stderr).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec per CAAT sublayer fwd (1 GPU, P emulated); % MFMA or HBM roofline"
+PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # MI355X: bf16 dense TFLOP/s, HBM3E GB/s
+DEFAULT_WORKLOAD = "7b-prefill-pair-bf16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(w, T, name, store_resid):
+    """Algorithmic FLOPs and HBM bytes of one launch of a kernel of the path."""
+    P, h, fs = w.P, w.h, w.f_s
+    b = 2 if w.dtype == "bf16" else 4
+    F1 = 2 * fs if w.act == "swiglu" else fs
+    E = P * T * h
+    if name == "mlp.K1":
+        return 2.0 * P * T * h * F1, b * (P * T * h + P * F1 * h + P * T * fs)
+    if name == "mlp.K2":
+        return 2.0 * P * T * fs * h, b * (P * T * fs + P * h * fs + E)
+    if name == "attn.K2":
+        k = h // P
+        return 2.0 * P * T * k * h, b * (P * T * k + P * h * k + E)
+    if name.endswith("K3"):
+        return 0.0, b * (E + E + E + (E if store_resid else 0) + 2 * h)
+    raise KeyError(name)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel_file, kernel_name, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    measurement, if it was taken on the kernel source as it is now (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{workload}:{kernel_name}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha256") != source_sha(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inputs, p, budget_s):
+    """The oracle (fp64 C, OpenMP) on a bounded sample of token rows of the same workload."""
+    import oracle
+    import torch
+    from partial_activation_sync_amd import synth
+    from tests.oracle_ref import reference
+
+    T = inputs["ctx"].shape[1] if "ctx" in inputs else inputs["x"].shape[1]
+    probe = synth.sample_rows(T, min(T, 8))
+    t0 = time.perf_counter()
+    reference(w, inputs, rows=probe, p=p)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(max(8, min(T, budget_s / max(per_row, 1e-9))))
+    rows = synth.sample_rows(T, n)
+    t0 = time.perf_counter()
+    reference(w, inputs, rows=rows, p=p)
+    dt = time.perf_counter() - t0
+    del torch
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {T} token rows of {w.name} (all {w.P} ranks, every "
+                      f"sublayer), fp64, {dt:.1f} s; rows are independent, so tokens/s = rows / s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--T", type=int, default=None)
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: every tensor-parallel rank is emulated on a "
+              f"single device (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", flush=True)
+        sys.exit(2)
+
+    import torch
+    from partial_activation_sync_amd import runner
+    from partial_activation_sync_amd import workloads as W
+
+    w = W.ALL[args.workload]
+    T = args.T or w.T
+    p = w.p if args.p is None else args.p
+    torch.cuda.set_device(0)
+    log(f"[bench] {w.name} T={T} p={p} P={w.P} h={w.h} ffn={w.ffn} act={w.act} norm={w.norm}")
+    t0 = time.perf_counter()
+    inputs = runner.make_inputs(w, T=T)
+    run = runner.Run(w, inputs, p=p, store_resid=True)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    kernels = []
+    if run.attn is not None:
+        k2, k3 = run.attn_steps()
+        kernels += [("attn.K2", k2), ("attn.K3", k3)]
+    k1, k2, k3 = run.mlp_steps()
+    kernels += [("mlp.K1", k1), ("mlp.K2", k2), ("mlp.K3", k3)]
+
+    def step():
+        for _, k in kernels:
+            k()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    nk = len(kernels)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record()
+        for i, (_, k) in enumerate(kernels):
+            k()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = sum(ev[s][0].elapsed_time(ev[s][nk]) for s in range(K)) / K
+    span_ms = ev[0][0].elapsed_time(ev[K - 1][nk]) / K
+    kern_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
+               for i, (name, _) in enumerate(kernels)}
+    ms_per_step = span_ms
+    value = T / (ms_per_step / 1e3)
+    log(f"[bench] {K} steps: {ms_per_step:.3f} ms/step (events), wall {wall / K * 1e3:.3f} ms/step")
+
+    detail = {}
+    for name, ms in kern_ms.items():
+        flops, nbytes = kernel_work(w, T, name, store_resid=True)
+        d = {"ms": round(ms, 4), "share": round(ms / step_ms, 3)}
+        if flops:
+            d["TFLOP/s"] = round(flops / ms / 1e9, 1)
+            d["mfma_frac"] = round(flops / ms / 1e9 / PEAK["mfma"], 3)
+        d["GB/s"] = round(nbytes / ms / 1e6, 1)
+        d["hbm_frac"] = round(nbytes / ms / 1e6 / PEAK["hbm"], 3)
+        detail[name] = d
+        log(f"[bench]   {name:8s} {ms:8.4f} ms  {d}")
+
+    dom = max(kern_ms, key=kern_ms.get)
+    flops, nbytes = kernel_work(w, T, dom, store_resid=True)
+    src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
+                       "psync_norm.hip" if dom.endswith("K3") else "gemm_bf16.hip")
+    if flops:
+        achieved = flops / kern_ms[dom] / 1e9
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK["mfma"],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma"], 4)}
+    else:
+        achieved = nbytes / kern_ms[dom] / 1e6
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"],
+                "unit": "GB/s", "frac": round(achieved / PEAK["hbm"], 4)}
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = flops if flops else nbytes
+    roof["traffic"] = traffic_for(src, dom, w.name)
+
+    base = None
+    if args.cpu_budget > 0:
+        log("[bench] timing the oracle on host cores ...")
+        base = cpu_baseline(w, inputs, p, args.cpu_budget)
+        log(f"[bench] cpu baseline: {base}")
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic: seeded N(0,1) activations, N(0,0.02^2) weights",
+        "config": {"workload": w.name, "P": w.P, "h": w.h, "ffn": w.ffn, "T": T, "p": p,
+                   "n_s": run.mlp.n_s, "act": w.act, "norm": w.norm,
+                   "sublayers": list(w.sublayers),
+                   "parallelism": f"tp{w.P} emulated on 1 GPU"},
+        "roofline": roof,
+        "cpu_baseline": base,
+        "kernels": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,6 +36,8 @@ def _load():
         lib = ctypes.CDLL(_build.LIB)
         dp = ctypes.POINTER(ctypes.c_double)
         fp = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_shared_channels.argtypes = [ctypes.c_int, ctypes.c_double]
         lib.oracle_shared_channels.restype = ctypes.c_int
         lib.oracle_activation.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
@@ -70,6 +72,11 @@ def _dptr(a):
     if a is None:
         return ctypes.POINTER(ctypes.c_double)()
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return _load().oracle_threads()
 
 
 def shared_channels(h: int, p: float) -> int:

@@ -45,9 +45,22 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { ORACLE_GELU = 0, ORACLE_GELU_TANH = 1, ORACLE_SWIGLU = 2, ORACLE_NONE = 3 };
 enum { ORACLE_LAYERNORM = 0, ORACLE_RMSNORM = 1 };
+
+/* Threads the OpenMP loops below use. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Number of shared channels (§3: "the first h*p channels"; App. A.2, Eq. 22:
  * channel l is reduced iff l < floor(h p)).  An h*p that fp64 puts a hair below an
