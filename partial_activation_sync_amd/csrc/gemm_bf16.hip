@@ -10,18 +10,37 @@
 // (output channels n), the column operand the activations (tokens t), so each lane's
 // accumulator holds 4 consecutive output channels of one token and stores 8 bytes.
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid; a BN x BT (channels x tokens)
-// tile, K stepped by 64.  Global -> registers (buffer loads; out-of-range rows and the
-// K tail read as zero from the buffer descriptor's range check) -> LDS, double
-// buffered with one barrier per K step; the next K step's loads are in flight while
-// the MFMAs of this one run.  LDS rows are 128 B (64 bf16) split in eight 16-byte
-// chunks stored at chunk ^ f(row), which keeps both the 16-byte writes and the 16-byte
-// fragment reads free of bank conflicts.
+// Pipeline (one workgroup per BN x BT tile, K stepped by 64):
+//   * global -> LDS with buffer loads that write LDS directly (no staging registers,
+//     no ds_write); rows outside the matrices and the K tail read as zero from the
+//     buffer descriptor's range check;
+//   * two LDS stages held in two separate arrays, so the compiler can tell the stage
+//     being filled from the stage being read and waits on the loads only at the
+//     barrier; one barrier per K step; the next step's loads are issued right after
+//     the barrier and fly while this step's MFMAs run;
+//   * within a step, the fragment reads for sub-step kk+1 are interleaved with the
+//     MFMAs of sub-step kk;
+//   * LDS rows are 128 B (64 bf16) split in eight 16-byte chunks stored at
+//     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts.
+// Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
+// range of tiles, which share operand rows.
 //
 // SwiGLU: the W1 tile interleaves 32-row blocks of gate and up rows for the same Y
 // columns ([g0..31, u0..31, g32..63, u32..63, ...]), so every wave holds matching
 // gate/up accumulators in the same lanes and applies silu(g) * u in registers.
 #include "caat_internal.h"
+
+// Scheduling directives and unroll pragmas exist only in the device pass; the host
+// pass only needs the kernel's signature.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define CAAT_UNROLL _Pragma("unroll")
+#define CAAT_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define CAAT_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#else
+#define CAAT_UNROLL
+#define CAAT_SCHED_FENCE()
+#define CAAT_SCHED_GROUP(mask, n)
+#endif
 
 namespace caat {
 namespace {
@@ -31,18 +50,20 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
-constexpr int NT = 256;
-constexpr uint32_t OOB = 0x80000000u;  // byte offset past every buffer's range
+constexpr uint32_t OOB = 0x80000000u;   // byte offset past every buffer's range
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit dword format
+constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              RSRC_WORD3);
 }
 
-// 16-byte slot of (row, chunk) in a [rows][8 chunks] LDS tile.
-__device__ __forceinline__ int swz(int row, int c) {
-    return row * 8 + (c ^ ((row & 7) ^ ((row >> 3) & 1)));
+// 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff,
+                                           uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ float gelu_erf(float v) {
@@ -55,34 +76,37 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // Block index -> tile index.  Workgroups go round-robin to the 8 XCDs; give each XCD
-// one contiguous range of tiles so neighbouring tiles (which share operand rows)
-// meet in the same L2.
+// one contiguous range of tiles.
 __device__ __forceinline__ int xcd_tile(int b, int total) {
     const int xcd = b & 7, idx = b >> 3;
     const int q = total >> 3, r = total & 7;
     return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
-template <int BN, int BT, int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
-void k_gemm_bf16(GemmArgs a, int tilesN, int tilesT)
+template <int BN, int BT, int WGN, int WGT, int EPI>
+__global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int tilesN, int tilesT)
 {
-    constexpr int WN = BN / 2, WT = BT / 2;     // wave tile: channels x tokens
-    constexpr int IB = WN / 32, JB = WT / 32;   // 32 x 32 MFMA blocks per wave
-    constexpr int WCH = BN * 8 / NT;            // W 16-byte chunks per thread per K step
-    constexpr int XCH = BT * 8 / NT;
+    constexpr int NW = WGN * WGT, NTH = 64 * NW;
+    constexpr int WN = BN / WGN, WT = BT / WGT;     // wave tile: channels x tokens
+    constexpr int IB = WN / 32, JB = WT / 32;       // 32 x 32 MFMA blocks per wave
+    constexpr int SLOTS = (BN + BT) * 8;            // 16-byte LDS slots per stage
+    constexpr int LOADS = SLOTS / NTH;              // loads per lane per stage
+    constexpr int WLOADS = BN * 8 / NTH;            // the first WLOADS fill W rows
     constexpr int NCOL = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns per tile
-    static_assert(IB % 2 == 0 || EPI != EPI_SWIGLU, "SwiGLU pairs need an even block count");
+    constexpr int NREAD = IB + JB, NMFMA = IB * JB;
+    static_assert(SLOTS % NTH == 0 && (BN * 8) % NTH == 0, "tile must split evenly");
+    static_assert(EPI != EPI_SWIGLU || IB % 2 == 0, "SwiGLU pairs need an even block count");
+    static_assert(NMFMA >= NREAD, "interleave needs at least one MFMA per fragment read");
 
-    __shared__ __attribute__((aligned(16))) uint4 lds[2][(BN + BT) * 8];
+    __shared__ __attribute__((aligned(16))) uint4 L0[SLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 L1[SLOTS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wt = wave >> 1;
-
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WGN, wt = wave / WGN;
     const int per = tilesN * tilesT;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int m = tile / per;
-    const int rem = tile - m * per;
+    const int m = tile / per, rem = tile - m * per;
     const int tn = rem % tilesN, tt = rem / tilesN;
     const int n0 = tn * NCOL, t0 = tt * BT;
     const int N = a.N, T = a.T, K = a.K;
@@ -93,127 +117,150 @@ void k_gemm_bf16(GemmArgs a, int tilesN, int tilesT)
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wm, (uint32_t)wrows * K * 2u);
     const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xm, (uint32_t)T * K * 2u);
 
-    // Per-thread load descriptors: byte offset at k = 0 (or OOB) and LDS slot.
-    uint32_t woff[WCH], xoff[XCH];
-    int wslot[WCH], xslot[XCH], wk[WCH], xk[XCH];
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-        const int q = tid + i * NT, row = q >> 3, c = q & 7;
-        int wrow;
+    // Load i of a lane fills LDS slot (i*NW + wave)*64 + lane: a 64-slot block is 8
+    // rows, row = 8 * block + lane / 8, and the slot holds chunk c = (lane & 7) ^ f(row)
+    // with f(row) = (row & 7) ^ ((row >> 3) & 1) = (lane >> 3) ^ (block & 1).
+    const int cl = (lane & 7) ^ ((lane >> 3) & 7);
+    uint32_t off[LOADS];
+    CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {
+        const int blk = i * NW + wave;
+        const int c = cl ^ (blk & 1);
+        const int row = blk * 8 + (lane >> 3);
+        uint32_t grow;
         bool ok;
-        if (EPI == EPI_SWIGLU) {
-            const int blk = row >> 5;
-            const int y = n0 + (blk >> 1) * 32 + (row & 31);
-            ok = y < N;
-            wrow = (blk & 1) ? a.up_off + y : y;
+        if (i < WLOADS) {
+            if (EPI == EPI_SWIGLU) {
+                const int b32 = row >> 5, y = n0 + (b32 >> 1) * 32 + (row & 31);
+                ok = y < N;
+                grow = (b32 & 1) ? a.up_off + y : y;
+            } else {
+                grow = n0 + row;
+                ok = (int)grow < N;
+            }
         } else {
-            wrow = n0 + row;
-            ok = wrow < N;
+            grow = t0 + row - BN;
+            ok = (int)grow < T;
         }
-        woff[i] = ok ? ((uint32_t)wrow * K + c * 8) * 2u : OOB;
-        wk[i] = c * 8;
-        wslot[i] = swz(row, c);
+        off[i] = ok ? (grow * (uint32_t)K + c * 8) * 2u : OOB;
     }
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-        const int q = tid + i * NT, row = q >> 3, c = q & 7;
-        const int t = t0 + row;
-        xoff[i] = (t < T) ? ((uint32_t)t * K + c * 8) * 2u : OOB;
-        xk[i] = c * 8;
-        xslot[i] = BN * 8 + swz(row, c);
-    }
-
-    uint4 wreg[WCH], xreg[XCH];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < WCH; ++i) {
-            const uint32_t off = (k0 + wk[i] < K) ? woff[i] + k0 * 2u : OOB;
-            auto v = __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0);
-            wreg[i] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) {
-            const uint32_t off = (k0 + xk[i] < K) ? xoff[i] + k0 * 2u : OOB;
-            auto v = __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0);
-            xreg[i] = make_uint4(v[0], v[1], v[2], v[3]);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < WCH; ++i) lds[buf][wslot[i]] = wreg[i];
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) lds[buf][xslot[i]] = xreg[i];
-    };
 
     f32x16 acc[IB][JB];
-#pragma unroll
-    for (int i = 0; i < IB; ++i)
-#pragma unroll
-        for (int j = 0; j < JB; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    CAAT_UNROLL for (int i = 0; i < IB; ++i)
+        CAAT_UNROLL for (int j = 0; j < JB; ++j)
+            CAAT_UNROLL for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // Fragment slots: a wave block's rows start at a multiple of 32, so f(row) = f(r32).
+    const int r32 = lane & 31, kh = lane >> 5;
+    const int fr = (r32 & 7) ^ ((r32 >> 3) & 1);
+    int aoff[4], boff[4];
+    CAAT_UNROLL for (int kk = 0; kk < 4; ++kk) {
+        aoff[kk] = (wn * WN + r32) * 8 + ((kk * 2 + kh) ^ fr);
+        boff[kk] = BN * 8 + (wt * WT + r32) * 8 + ((kk * 2 + kh) ^ fr);
+    }
 
     const int nk = (K + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int r32 = lane & 31, khalf = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const uint4 *L = lds[kt & 1];
-#pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = kk * 2 + khalf;
-            bf16x8 af[IB], bfr[JB];
-#pragma unroll
-            for (int i = 0; i < IB; ++i)
-                af[i] = __builtin_bit_cast(bf16x8, L[swz(wn * WN + i * 32 + r32, c)]);
-#pragma unroll
-            for (int j = 0; j < JB; ++j)
-                bfr[j] = __builtin_bit_cast(bf16x8, L[BN * 8 + swz(wt * WT + j * 32 + r32, c)]);
-#pragma unroll
-            for (int i = 0; i < IB; ++i)
-#pragma unroll
-                for (int j = 0; j < JB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) sstore((kt + 1) & 1);
+    const bool ktail = (K % BK) != 0;
+
+    // Enqueue the loads of K step k0 into LDS stage Lb.  Only a ragged last step
+    // masks chunks past K (they read as zero).
+#define CAAT_ISSUE(k0, Lb)                                                                 \
+    do {                                                                                   \
+        const int k0_ = (k0);                                                              \
+        if (ktail && k0_ + BK > K) {                                                       \
+            CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {                                  \
+                const int base = (i * NW + wave) * 64;                                     \
+                const int c = cl ^ ((i * NW + wave) & 1);                                  \
+                const uint32_t o = (k0_ + c * 8 < K) ? off[i] : OOB;                       \
+                load_lds16(i < WLOADS ? rW : rX, (Lb) + base, o, k0_ * 2);                 \
+            }                                                                              \
+        } else {                                                                           \
+            CAAT_UNROLL for (int i = 0; i < LOADS; ++i)                                    \
+                load_lds16(i < WLOADS ? rW : rX, (Lb) + (i * NW + wave) * 64, off[i],      \
+                           k0_ * 2);                                                       \
+        }                                                                                  \
+        CAAT_SCHED_FENCE();                                                                \
+    } while (0)
+
+    // MFMAs over one LDS stage; reads for sub-step kk+1 interleave with MFMAs of kk.
+#define CAAT_COMPUTE(Lb)                                                                   \
+    do {                                                                                   \
+        bf16x8 af[2][IB], bfr[2][JB];                                                      \
+        CAAT_UNROLL for (int i = 0; i < IB; ++i)                                           \
+            af[0][i] = __builtin_bit_cast(bf16x8, (Lb)[aoff[0] + i * 256]);                \
+        CAAT_UNROLL for (int j = 0; j < JB; ++j)                                           \
+            bfr[0][j] = __builtin_bit_cast(bf16x8, (Lb)[boff[0] + j * 256]);               \
+        CAAT_UNROLL for (int kk = 0; kk < 4; ++kk) {                                       \
+            const int cur = kk & 1, nxt = cur ^ 1;                                         \
+            if (kk < 3) {                                                                  \
+                CAAT_UNROLL for (int i = 0; i < IB; ++i)                                   \
+                    af[nxt][i] = __builtin_bit_cast(bf16x8, (Lb)[aoff[kk + 1] + i * 256]); \
+                CAAT_UNROLL for (int j = 0; j < JB; ++j)                                   \
+                    bfr[nxt][j] = __builtin_bit_cast(bf16x8, (Lb)[boff[kk + 1] + j * 256]);\
+            }                                                                              \
+            CAAT_UNROLL for (int i = 0; i < IB; ++i)                                       \
+                CAAT_UNROLL for (int j = 0; j < JB; ++j)                                   \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
+                        af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);                      \
+            if (kk < 3) {                                                                  \
+                CAAT_UNROLL for (int r = 0; r < NREAD; ++r) {                              \
+                    CAAT_SCHED_GROUP(SG_MFMA, 1);                                          \
+                    CAAT_SCHED_GROUP(SG_DS_READ, 1);                                       \
+                }                                                                          \
+                if (NMFMA > NREAD) CAAT_SCHED_GROUP(SG_MFMA, NMFMA - NREAD);               \
+            } else {                                                                       \
+                CAAT_SCHED_GROUP(SG_MFMA, NMFMA);                                          \
+            }                                                                              \
+        }                                                                                  \
+    } while (0)
+
+    CAAT_ISSUE(0, L0);
+    int kt = 0;
+    for (; kt + 2 <= nk; kt += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        CAAT_SCHED_FENCE();
+        CAAT_ISSUE((kt + 1) * BK, L1);
+        CAAT_COMPUTE(L0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        CAAT_SCHED_FENCE();
+        if (kt + 2 < nk) CAAT_ISSUE((kt + 2) * BK, L0);
+        CAAT_COMPUTE(L1);
     }
+    if (kt < nk) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        CAAT_COMPUTE(L0);
+    }
+#undef CAAT_ISSUE
+#undef CAAT_COMPUTE
 
     // Epilogue.  Accumulator element v of block (i, j) in lane l is channel row
     // 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.
     __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
-#pragma unroll
-    for (int j = 0; j < JB; ++j) {
+    CAAT_UNROLL for (int j = 0; j < JB; ++j) {
         const int t = t0 + wt * WT + j * 32 + r32;
         if (t >= T) continue;
         __bf16 *orow = O + (size_t)t * N;
         if (EPI == EPI_SWIGLU) {
-#pragma unroll
-            for (int i = 0; i < IB; i += 2) {
+            CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
                 const int yb = n0 + ((wn * IB + i) >> 1) * 32;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int y = yb + 8 * g + 4 * khalf;
+                CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                    const int y = yb + 8 * g + 4 * kh;
                     if (y >= N) continue;
                     bf16x4 o;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
+                    CAAT_UNROLL for (int q = 0; q < 4; ++q)
                         o[q] = static_cast<__bf16>(silu(acc[i][j][4 * g + q]) * acc[i + 1][j][4 * g + q]);
                     *reinterpret_cast<bf16x4 *>(orow + y) = o;
                 }
             }
         } else {
-#pragma unroll
-            for (int i = 0; i < IB; ++i) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * khalf;
+            CAAT_UNROLL for (int i = 0; i < IB; ++i) {
+                CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * kh;
                     if (n >= N) continue;
                     bf16x4 o;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
+                    CAAT_UNROLL for (int q = 0; q < 4; ++q) {
                         float v = acc[i][j][4 * g + q];
                         if (EPI == EPI_GELU) v = gelu_erf(v);
                         if (EPI == EPI_GELU_TANH) v = gelu_tanh(v);
@@ -226,24 +273,24 @@ void k_gemm_bf16(GemmArgs a, int tilesN, int tilesT)
     }
 }
 
-template <int BN, int BT>
+template <int BN, int BT, int WGN, int WGT>
 hipError_t launch(const GemmArgs &a, hipStream_t s) {
     const int ncol = (a.epi == EPI_SWIGLU) ? BN / 2 : BN;
     const int tilesN = (a.N + ncol - 1) / ncol;
     const int tilesT = (a.T + BT - 1) / BT;
-    const dim3 grid(a.P * tilesN * tilesT), block(NT);
+    const dim3 grid(a.P * tilesN * tilesT), block(64 * WGN * WGT);
     switch (a.epi) {
     case EPI_GELU:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, EPI_GELU>), grid, block, 0, s, a, tilesN, tilesT);
+        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_GELU>), grid, block, 0, s, a, tilesN, tilesT);
         break;
     case EPI_GELU_TANH:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, EPI_GELU_TANH>), grid, block, 0, s, a, tilesN, tilesT);
+        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_GELU_TANH>), grid, block, 0, s, a, tilesN, tilesT);
         break;
     case EPI_SWIGLU:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, EPI_SWIGLU>), grid, block, 0, s, a, tilesN, tilesT);
+        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_SWIGLU>), grid, block, 0, s, a, tilesN, tilesT);
         break;
     default:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, EPI_STORE>), grid, block, 0, s, a, tilesN, tilesT);
+        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_STORE>), grid, block, 0, s, a, tilesN, tilesT);
         break;
     }
     return hipGetLastError();
@@ -258,11 +305,17 @@ bool gemm_bf16_supported(const GemmArgs &a) {
            a.N % 8 == 0;
 }
 
+// Tile choice: 256 x 256 when there are at least two full waves of such tiles on the
+// 256 CUs (4 waves per workgroup for long K, 8 for short K, measured on MI355X), else
+// 128 x 128 so that smaller problems still spread over every CU.
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int ncol256 = (a.epi == EPI_SWIGLU) ? 128 : 256;
     const long tiles256 = (long)a.P * ((a.N + ncol256 - 1) / ncol256) * ((a.T + 255) / 256);
-    if (tiles256 >= 512) return launch<256, 256>(a, s);
-    return launch<128, 128>(a, s);
+    if (tiles256 >= 512) {
+        if (a.K >= 2048) return launch<256, 256, 2, 2>(a, s);
+        return launch<256, 256, 2, 4>(a, s);
+    }
+    return launch<128, 128, 2, 2>(a, s);
 }
 
 }  // namespace caat
