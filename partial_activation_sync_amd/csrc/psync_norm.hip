@@ -20,7 +20,8 @@ namespace caat {
 namespace {
 
 constexpr int G = 4;            // ranks normalized per LDS exchange
-constexpr int MAX_WAVES = 4;    // blockDim <= 256
+constexpr int MAX_WAVES = 4;    // blockDim <= 256 (multi-pass kernel)
+constexpr int MAX_WAVES_1P = 8; // blockDim <= 512 (single-pass kernel)
 
 template <typename TIO> struct Vec8;
 
@@ -62,21 +63,22 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Sums v[g] over the whole block (fixed order); red is LDS [MAX_WAVES][G].
-__device__ __forceinline__ void block_sum(float (&v)[G], float *red) {
+// Sums v[g] (g < NV) over the whole block in a fixed order; red is LDS [MAX_WAVES][NV].
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float *red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
 #pragma unroll
-    for (int g = 0; g < G; ++g) v[g] = wave_sum(v[g]);
+    for (int g = 0; g < NV; ++g) v[g] = wave_sum(v[g]);
     if (lane == 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) red[wave * G + g] = v[g];
+        for (int g = 0; g < NV; ++g) red[wave * NV + g] = v[g];
     }
     __syncthreads();
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < NV; ++g) {
         float s = 0.f;
-        for (int w = 0; w < nwaves; ++w) s += red[w * G + g];
+        for (int w = 0; w < nwaves; ++w) s += red[w * NV + g];
         v[g] = s;
     }
 }
@@ -219,6 +221,167 @@ __global__ __launch_bounds__(256) void k_psync_norm(
     }
 }
 
+// Raw 16-byte chunk of 8 values (bf16: one uint4; fp32: two).
+template <typename TIO> struct Raw;
+template <> struct Raw<__bf16> {
+    uint4 u;
+    __device__ __forceinline__ void load(const __bf16 *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void unpack(float (&v)[8]) const {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void unpack(float (&v)[8]) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+// Single-pass variant for P <= PMAX: every load of the token (all ranks' partials and
+// residuals) is issued at once into registers, in their storage format; the shared
+// sum S, the residual rows r = resid + z and the row statistics are then computed
+// from registers (r is recomputed rather than kept, which is a few VALU ops), with one
+// block reduction of a P-vector per statistic.  One memory round trip per token.
+template <int PMAX, int NCH, int NORM, typename TIO>
+__global__ __launch_bounds__(512) void k_psync_norm_1p(
+    int P, int T, int h, int n_s, float s_priv, float eps,
+    const TIO *__restrict__ partials, const TIO *__restrict__ resid,
+    const TIO *__restrict__ gamma, const TIO *__restrict__ beta,
+    TIO *__restrict__ out, TIO *__restrict__ out_resid)
+{
+    __shared__ float red[2][MAX_WAVES_1P * PMAX];
+    const int t = blockIdx.x;
+    const int nchunk = h >> 3;
+    const size_t rank_stride = (size_t)T * h;
+    const size_t row = (size_t)t * h;
+    const float inv_h = 1.0f / (float)h;
+
+    int ch0[NCH];
+    bool valid[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        valid[j] = c < nchunk;
+        ch0[j] = c * 8;
+    }
+
+    Raw<TIO> zr[PMAX][NCH], rr[PMAX][NCH];
+#pragma unroll
+    for (int m = 0; m < PMAX; ++m) {
+        if (m >= P) break;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (!valid[j]) continue;
+            const size_t off = m * rank_stride + row + ch0[j];
+            zr[m][j].load(partials + off);
+            rr[m][j].load(resid + off);
+        }
+    }
+
+    // Partial channel-reduce on the shared chunks (ascending ranks, fp32).
+    float S[NCH][8];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S[j][e] = 0.f;
+        if (valid[j] && ch0[j] < n_s) {
+#pragma unroll
+            for (int m = 0; m < PMAX; ++m) {
+                if (m >= P) break;
+                float z[8];
+                zr[m][j].unpack(z);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) S[j][e] += z[e];
+            }
+        }
+    }
+
+    // r[m][j][e] = resid + (shared ? S : s_priv * partial), recomputed where needed.
+    auto rrow = [&](int m, int j, float (&r)[8]) {
+        float res[8], z[8];
+        rr[m][j].unpack(res);
+        zr[m][j].unpack(z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = res[e] + ((ch0[j] + e < n_s) ? S[j][e] : s_priv * z[e]);
+    };
+
+    float mean[PMAX], inv[PMAX];
+    float acc[PMAX];
+#pragma unroll
+    for (int m = 0; m < PMAX; ++m) {
+        acc[m] = 0.f;
+        mean[m] = 0.f;
+        if (m >= P) continue;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if (!valid[j]) continue;
+            float r[8];
+            rrow(m, j, r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[m] += (NORM == CAAT_LAYERNORM) ? r[e] : r[e] * r[e];
+        }
+    }
+    block_sum<PMAX>(acc, red[0]);
+    if (NORM == CAAT_LAYERNORM) {
+#pragma unroll
+        for (int m = 0; m < PMAX; ++m) mean[m] = acc[m] * inv_h;
+        // Second pass for the biased variance around the mean.
+#pragma unroll
+        for (int m = 0; m < PMAX; ++m) {
+            acc[m] = 0.f;
+            if (m >= P) continue;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                if (!valid[j]) continue;
+                float r[8];
+                rrow(m, j, r);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = r[e] - mean[m];
+                    acc[m] += d * d;
+                }
+            }
+        }
+        block_sum<PMAX>(acc, red[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < PMAX; ++m) inv[m] = rsqrtf(acc[m] * inv_h + eps);
+
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        if (!valid[j]) continue;
+        float gm[8], bt[8];
+        Vec8<TIO>::load(gamma + ch0[j], gm);
+        if (NORM == CAAT_LAYERNORM && beta != nullptr) {
+            Vec8<TIO>::load(beta + ch0[j], bt);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bt[e] = 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < PMAX; ++m) {
+            if (m >= P) break;
+            const size_t off = m * rank_stride + row + ch0[j];
+            float r[8], o[8];
+            rrow(m, j, r);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (r[e] - mean[m]) * inv[m] * gm[e] + bt[e];
+            Vec8<TIO>::store(out + off, o);
+            if (out_resid != nullptr) Vec8<TIO>::store(out_resid + off, r);
+        }
+    }
+}
+
 template <int NORM, typename TIO>
 hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     const int nchunk = a.h / 8;
@@ -233,6 +396,42 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     auto B = reinterpret_cast<const TIO *>(a.beta);
     auto O = reinterpret_cast<TIO *>(a.out);
     auto OR = reinterpret_cast<TIO *>(a.out_resid);
+    // Registers for one token's raw inputs: 2 * PMAX * NCH chunks of 16 (bf16) or 32
+    // (fp32) bytes; the single-pass kernel is used while that stays <= 128 VGPRs.
+    const int pmax = a.P <= 1 ? 1 : a.P <= 2 ? 2 : a.P <= 4 ? 4 : a.P <= 8 ? 8 : 16;
+    const int budget = sizeof(TIO) == 2 ? 16 : 8;
+    // Up to 512 threads per token here: fewer chunks per thread, fewer registers.
+    int nch1 = 1;
+    while (nch1 < 8 && nchunk > nch1 * 512) nch1 *= 2;
+    if (pmax * nch1 <= budget) {
+        const int nch = nch1;
+        int th = (nchunk + nch - 1) / nch;
+        th = (th + 63) / 64 * 64;
+        const dim3 block(th);
+#define CAAT_K3S(PM, N)                                                                           \
+    hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
+                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR)
+        switch (pmax * 16 + nch) {
+        case 1 * 16 + 1: CAAT_K3S(1, 1); break;
+        case 1 * 16 + 2: CAAT_K3S(1, 2); break;
+        case 1 * 16 + 4: CAAT_K3S(1, 4); break;
+        case 1 * 16 + 8: CAAT_K3S(1, 8); break;
+        case 2 * 16 + 1: CAAT_K3S(2, 1); break;
+        case 2 * 16 + 2: CAAT_K3S(2, 2); break;
+        case 2 * 16 + 4: CAAT_K3S(2, 4); break;
+        case 2 * 16 + 8: CAAT_K3S(2, 8); break;
+        case 4 * 16 + 1: CAAT_K3S(4, 1); break;
+        case 4 * 16 + 2: CAAT_K3S(4, 2); break;
+        case 4 * 16 + 4: CAAT_K3S(4, 4); break;
+        case 8 * 16 + 1: CAAT_K3S(8, 1); break;
+        case 8 * 16 + 2: CAAT_K3S(8, 2); break;
+        case 16 * 16 + 1: CAAT_K3S(16, 1); break;
+        default: goto multipass;
+        }
+#undef CAAT_K3S
+        return hipGetLastError();
+    }
+multipass:
 #define CAAT_K3(N)                                                                     \
     hipLaunchKernelGGL((k_psync_norm<N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
                        a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR)
