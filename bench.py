@@ -94,6 +94,22 @@ def cpu_baseline(w, inputs, p, budget_s):
                       f"sublayer), fp64, {dt:.1f} s; rows are independent, so tokens/s = rows / s"}
 
 
+COPY_BYTES = 512 << 20
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES, five times: under rocprofv3 --pmc
+    its FETCH_SIZE / WRITE_SIZE per dispatch give the counters' scale factor."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "dispatches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,7 +120,12 @@ def main():
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
