@@ -83,7 +83,9 @@ caat::GemmArgs row_args(const caat_ctx *c, int T, const void *in, const void *W2
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
     if (c->dtype == CAAT_BF16) {
         if (!caat::gemm_bf16_supported(g)) return CAAT_EUNSUPPORTED;
-        return caat::gemm_bf16(g, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
+        const hipError_t e = caat::gemm_decode_applies(g) ? caat::gemm_decode_bf16(g, s)
+                                                          : caat::gemm_bf16(g, s);
+        return e == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
     }
     return caat::gemm_f32(g, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
 }

@@ -47,6 +47,9 @@ struct GemmArgs {
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs &a, hipStream_t s);
 bool gemm_bf16_supported(const GemmArgs &a);
+// Weight-streaming variant for decode batches (T <= 64), bf16.
+bool gemm_decode_applies(const GemmArgs &a);
+hipError_t gemm_decode_bf16(const GemmArgs &a, hipStream_t s);
 
 struct PsyncArgs {
     int P, T, h, n_s, norm;

@@ -57,10 +57,15 @@ class Run:
     """Device-resident inputs, outputs and handles for one workload at one T."""
 
     def __init__(self, w: Workload, inputs: dict, p=None, s_priv=1.0, device="cuda",
-                 store_resid=True):
+                 store_resid=True, weight_copies=1):
         self.w = w
         self.p = w.p if p is None else p
         self.dev = {k: v.to(device) for k, v in inputs.items()}
+        # Extra copies of the weights, so that a benchmark can rotate through more bytes
+        # than the 256 MB Infinity Cache holds (weight-streaming shapes).
+        self.weight_sets = [{k: self.dev[k] for k in ("W1", "W2", "Wo") if k in self.dev}]
+        for _ in range(1, weight_copies):
+            self.weight_sets.append({k: v.clone() for k, v in self.weight_sets[0].items()})
         P, h = w.P, w.h
         self.T = T = (self.dev["ctx"] if "ctx" in self.dev else self.dev["x"]).shape[1]
         dt = torch_dtype(w)
@@ -99,9 +104,9 @@ class Run:
         return o
 
     # The three steps of one sublayer, for per-kernel timing.
-    def mlp_steps(self):
+    def mlp_steps(self, copy=0):
         """Callables for K1, K2 and K3 of the MLP sublayer on its workspace buffers."""
-        d, s = self.dev, self.mlp
+        d, s = dict(self.dev, **self.weight_sets[copy]), self.mlp
         T, P, h, fs = self.T, self.w.P, self.w.h, self.w.f_s
         ws = s.workspace(T)
         es = ws.new_empty(0, dtype=torch_dtype(self.w)).element_size()
@@ -117,9 +122,9 @@ class Run:
                                             self.out, self.out_resid)
         return k1, k2, k3
 
-    def attn_steps(self):
+    def attn_steps(self, copy=0):
         """Callables for K2 and K3 of the out-projection sublayer."""
-        d, s = self.dev, self.attn
+        d, s = dict(self.dev, **self.weight_sets[copy]), self.attn
         T, P, h = self.T, self.w.P, self.w.h
         ws = s.workspace(T)
         Z = ws[:P * T * h * ws.new_empty(0, dtype=torch_dtype(self.w)).element_size()]
