@@ -32,7 +32,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(w, T, name, store_resid):
+def kernel_work(w, T, name, store_resid, n_s):
     """Algorithmic FLOPs and HBM bytes of one launch of a kernel of the path."""
     P, h, fs = w.P, w.h, w.f_s
     b = 2 if w.dtype == "bf16" else 4
@@ -40,13 +40,16 @@ def kernel_work(w, T, name, store_resid):
     E = P * T * h
     if name == "mlp.K1":
         return 2.0 * P * T * h * F1, b * (P * T * h + P * F1 * h + P * T * fs)
+    # Partials written by K2 and read by K3: all P x T x h values, or, on the fused path
+    # (n_s % 8 == 0 and T > 64), S [T][n_s] once plus the private columns of every rank.
+    part = P * T * (h - n_s) + T * n_s if (n_s % 8 == 0 and T > 64) else E
     if name == "mlp.K2":
-        return 2.0 * P * T * fs * h, b * (P * T * fs + P * h * fs + E)
+        return 2.0 * P * T * fs * h, b * (P * T * fs + P * h * fs + part)
     if name == "attn.K2":
         k = h // P
-        return 2.0 * P * T * k * h, b * (P * T * k + P * h * k + E)
+        return 2.0 * P * T * k * h, b * (P * T * k + P * h * k + part)
     if name.endswith("K3"):
-        return 0.0, b * (E + E + E + (E if store_resid else 0) + 2 * h)
+        return 0.0, b * (part + E + E + (E if store_resid else 0) + 2 * h)
     raise KeyError(name)
 
 
@@ -194,7 +197,7 @@ def main():
 
     detail = {}
     for name, ms in kern_ms.items():
-        flops, nbytes = kernel_work(w, T, name, store_resid=True)
+        flops, nbytes = kernel_work(w, T, name, store_resid=True, n_s=run.mlp.n_s)
         d = {"ms": round(ms, 4), "share": round(ms / step_ms, 3)}
         if flops:
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
@@ -205,7 +208,7 @@ def main():
         log(f"[bench]   {name:8s} {ms:8.4f} ms  {d}")
 
     dom = max(kern_ms, key=kern_ms.get)
-    flops, nbytes = kernel_work(w, T, dom, store_resid=True)
+    flops, nbytes = kernel_work(w, T, dom, store_resid=True, n_s=run.mlp.n_s)
     src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
                        "psync_norm.hip" if dom.endswith("K3") else "gemm_bf16.hip")
     ridge = PEAK["mfma"] * 1e12 / (PEAK["hbm"] * 1e9)   # FLOP per byte where the roofs meet

@@ -97,8 +97,8 @@ int caat_set_private_scale(caat_handle handle, float s);
 /* n_s, the number of shared channels [0, n_s); or CAAT_EINVAL for a NULL handle. */
 int caat_shared_channels(caat_handle handle);
 
-/* Bytes of device workspace a forward over T tokens needs: Y and the partials.
- * Returns 0 for a NULL handle or T < 1. */
+/* Bytes of device workspace a forward over T tokens needs: Y, the partials and (when
+ * n_s % 8 == 0) the reduced shared channels S.  Returns 0 for a NULL handle or T < 1. */
 size_t caat_workspace_bytes(caat_handle handle, int T);
 
 /* Attaches caller-owned device memory as the workspace (16-byte aligned). */
@@ -135,6 +135,25 @@ int caat_column_gemm_act(caat_handle handle, int T, const void *x, const void *W
  * second sum of Eq. 22) or H [P][T][h/P] (out-projection, Eq. 24). */
 int caat_row_gemm(caat_handle handle, int T, const void *in, const void *W2, void *partials,
                   void *stream);
+
+/* Step a2 with the reduce of step a3 folded in (the paper's single-device local
+ * summation, §3.2, done inside the GEMM): the shared channels are summed over the
+ * ranks in the GEMM's fp32 accumulators, as one product whose contraction runs over
+ * every rank's K (Eq. 22: sum over m of Zt_m[l] for l < n_s):
+ *   S [T][n_s]        S[t][l] = sum_m sum_k in_m[t][k] W2_m[l][k],  l < n_s
+ *   partials [P][T][h] columns [n_s, h) only: Zt_m[t][l],            l >= n_s
+ * Columns [0, n_s) of partials are not written.  S may be NULL when n_s == 0 and
+ * partials may be NULL when n_s == h.  Needs n_s % 8 == 0, else CAAT_EUNSUPPORTED.
+ * caat_forward / caat_forward_ex take this path when n_s % 8 == 0 and T > 64. */
+int caat_row_gemm_reduce(caat_handle handle, int T, const void *in, const void *W2, void *S,
+                         void *partials, void *stream);
+
+/* Steps a3-a5 after caat_row_gemm_reduce: shared channels from S [T][n_s], private
+ * channels from columns [n_s, h) of partials (× s_priv), residual add and
+ * normalization (Eq. 9), for every rank.  Same NULL rules and n_s % 8 == 0 rule. */
+int caat_sync_norm(caat_handle handle, int T, const void *S, const void *partials,
+                   const void *resid, const void *gamma, const void *beta, void *out,
+                   void *out_resid, void *stream);
 
 /* Steps a3-a5 alone: partial channel-reduce of the given partials [P][T][h] (Eq. 22 /
  * 24), private scaling, residual add and normalization (Eq. 9).  resid [P][T][h] is

@@ -65,12 +65,14 @@ def lib():
         L.caat_column_gemm_act.argtypes = [vp, i, vp, vp, vp, vp]
         L.caat_row_gemm.argtypes = [vp, i, vp, vp, vp, vp]
         L.caat_partial_sync_norm.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp]
+        L.caat_row_gemm_reduce.argtypes = [vp, i, vp, vp, vp, vp, vp]
+        L.caat_sync_norm.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp]
         L.caat_error_string.argtypes = [i]
         L.caat_error_string.restype = ctypes.c_char_p
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
                      "caat_forward_ex", "caat_column_gemm_act", "caat_row_gemm",
-                     "caat_partial_sync_norm"):
+                     "caat_partial_sync_norm", "caat_row_gemm_reduce", "caat_sync_norm"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -171,6 +173,18 @@ def caat_partial_sync_norm(handle, T, partials, resid, gamma, beta, out, out_res
                                                _ptr(gamma), _ptr(beta), _ptr(out),
                                                _ptr(out_resid), _stream(stream)),
                   "caat_partial_sync_norm")
+
+
+def caat_row_gemm_reduce(handle, T, inp, W2, S, partials, stream=None):
+    return _check(lib().caat_row_gemm_reduce(handle, int(T), _ptr(inp), _ptr(W2), _ptr(S),
+                                             _ptr(partials), _stream(stream)),
+                  "caat_row_gemm_reduce")
+
+
+def caat_sync_norm(handle, T, S, partials, resid, gamma, beta, out, out_resid, stream=None):
+    return _check(lib().caat_sync_norm(handle, int(T), _ptr(S), _ptr(partials), _ptr(resid),
+                                       _ptr(gamma), _ptr(beta), _ptr(out), _ptr(out_resid),
+                                       _stream(stream)), "caat_sync_norm")
 
 
 class Sublayer:

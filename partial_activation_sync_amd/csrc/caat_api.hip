@@ -44,6 +44,17 @@ size_t y_bytes(const caat_ctx *c, int T) {
 size_t partial_bytes(const caat_ctx *c, int T) {
     return align256((size_t)c->P * T * c->h * esize(c));
 }
+// The fused path (shared channels reduced inside the row-parallel GEMM) needs the
+// shared/private boundary on a 16-byte boundary of every row.
+bool fused_ok(const caat_ctx *c) { return c->n_s % 8 == 0; }
+// caat_forward_ex takes it for prefill-sized batches, where it saves the partials'
+// shared columns of every rank (T x n_s x (P - 1) values written and read).  Decode
+// batches (T <= 64) keep the per-rank GEMM: their partials are a few MB, and the
+// single shared GEMM would spread its weight stream over too few workgroups.
+bool fused_for(const caat_ctx *c, int T) { return fused_ok(c) && T > 64; }
+size_t s_bytes(const caat_ctx *c, int T) {
+    return fused_ok(c) ? align256((size_t)T * c->n_s * esize(c)) : 0;
+}
 
 // Shared channels (§3: the first h p channels; Eq. 22: l < floor(h p)).  An h p that
 // lands a rounding error below an integer counts as that integer.
@@ -59,8 +70,9 @@ caat::GemmArgs col_args(const caat_ctx *c, int T, const void *x, const void *W1,
     g.P = c->P; g.N = c->fs; g.T = T; g.K = c->h;
     g.W = W1; g.w_stride = (size_t)c->F1 * c->h;
     g.X = x;  g.x_stride = (size_t)T * c->h;
-    g.out = Y; g.o_stride = (size_t)T * c->fs;
+    g.out = Y; g.o_stride = (size_t)T * c->fs; g.ldo = c->fs;
     g.up_off = c->fs;
+    g.kseg = 1;
     switch (c->act) {
     case CAAT_GELU: g.epi = caat::EPI_GELU; break;
     case CAAT_GELU_TANH: g.epi = caat::EPI_GELU_TANH; break;
@@ -74,10 +86,49 @@ caat::GemmArgs row_args(const caat_ctx *c, int T, const void *in, const void *W2
     g.P = c->P; g.N = c->h; g.T = T; g.K = c->k2;
     g.W = W2; g.w_stride = (size_t)c->h * c->k2;
     g.X = in; g.x_stride = (size_t)T * c->k2;
-    g.out = Z; g.o_stride = (size_t)T * c->h;
+    g.out = Z; g.o_stride = (size_t)T * c->h; g.ldo = c->h;
     g.up_off = 0;
     g.epi = caat::EPI_STORE;
+    g.kseg = 1;
     return g;
+}
+
+// Shared channels [0, n_s): one GEMM whose contraction runs over every rank's K
+// (the ranks' partial products summed in the accumulators): S[t][l] =
+// sum_m sum_k in_m[t][k] W2_m[l][k], written once, [T][n_s].
+caat::GemmArgs shared_args(const caat_ctx *c, int T, const void *in, const void *W2, void *S) {
+    caat::GemmArgs g{};
+    g.P = 1; g.N = c->n_s; g.T = T; g.K = c->k2;
+    g.W = W2; g.w_stride = 0;
+    g.X = in; g.x_stride = 0;
+    g.out = S; g.o_stride = 0; g.ldo = c->n_s;
+    g.up_off = 0;
+    g.epi = caat::EPI_STORE;
+    g.kseg = c->P; g.w_kseg = (size_t)c->h * c->k2; g.x_kseg = (size_t)T * c->k2;
+    return g;
+}
+
+// Private channels [n_s, h): the per-rank partials, written into columns [n_s, h) of
+// partials[m][t][:].
+caat::GemmArgs private_args(const caat_ctx *c, int T, const void *in, const void *W2, void *Z) {
+    caat::GemmArgs g = row_args(c, T, in, W2, Z);
+    g.N = c->h - c->n_s;
+    g.W = reinterpret_cast<const char *>(W2) + (size_t)c->n_s * c->k2 * esize(c);
+    g.out = reinterpret_cast<char *>(Z) + (size_t)c->n_s * esize(c);
+    return g;
+}
+
+int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s);
+
+// Row-parallel GEMM with the shared channels reduced over ranks inside the GEMM.
+int run_row_reduce(const caat_ctx *c, int T, const void *in, const void *W2, void *S, void *Z,
+                   hipStream_t s) {
+    if (c->n_s > 0) {
+        const int rc = run_gemm(c, shared_args(c, T, in, W2, S), s);
+        if (rc != CAAT_OK) return rc;
+    }
+    if (c->n_s < c->h) return run_gemm(c, private_args(c, T, in, W2, Z), s);
+    return CAAT_OK;
 }
 
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
@@ -91,8 +142,10 @@ int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
 }
 
 int run_psync(const caat_ctx *c, int T, const void *partials, const void *resid,
-              const void *gamma, const void *beta, void *out, void *out_resid, hipStream_t s) {
+              const void *gamma, const void *beta, void *out, void *out_resid, hipStream_t s,
+              const void *S = nullptr) {
     caat::PsyncArgs a{};
+    a.S = S; a.s_ld = c->n_s;
     a.P = c->P; a.T = T; a.h = c->h; a.n_s = c->n_s; a.norm = c->norm;
     a.s_priv = c->s_priv; a.eps = c->eps;
     a.partials = partials; a.resid = resid; a.gamma = gamma;
@@ -168,7 +221,7 @@ CAAT_API int caat_shared_channels(caat_handle handle) {
 
 CAAT_API size_t caat_workspace_bytes(caat_handle handle, int T) {
     if (handle == nullptr || T < 1) return 0;
-    return y_bytes(handle, T) + partial_bytes(handle, T);
+    return y_bytes(handle, T) + partial_bytes(handle, T) + s_bytes(handle, T);
 }
 
 CAAT_API int caat_set_workspace(caat_handle handle, void *dev_ptr, size_t bytes) {
@@ -204,11 +257,17 @@ CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
     char *ws = reinterpret_cast<char *>(c->ws);
     void *Y = ws;
     void *Z = ws + y_bytes(c, T);
+    void *S = ws + y_bytes(c, T) + partial_bytes(c, T);
     const void *gemm_in = a->in;
     if (c->act != CAAT_NONE) {
         rc = run_gemm(c, col_args(c, T, a->in, a->W1, Y), s);
         if (rc != CAAT_OK) return rc;
         gemm_in = Y;
+    }
+    if (fused_for(c, T)) {
+        rc = run_row_reduce(c, T, gemm_in, a->W2, S, Z, s);
+        if (rc != CAAT_OK) return rc;
+        return run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s, S);
     }
     rc = run_gemm(c, row_args(c, T, gemm_in, a->W2, Z), s);
     if (rc != CAAT_OK) return rc;
@@ -243,6 +302,36 @@ CAAT_API int caat_row_gemm(caat_handle c, int T, const void *in, const void *W2,
     const int rc = device_check();
     if (rc != CAAT_OK) return rc;
     return run_gemm(c, row_args(c, T, in, W2, partials), reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API int caat_row_gemm_reduce(caat_handle c, int T, const void *in, const void *W2, void *S,
+                                  void *partials, void *stream) {
+    if (c == nullptr) return CAAT_EINVAL;
+    if (T < 1 || !aligned16(in) || !aligned16(W2)) return CAAT_EINVAL;
+    if (c->n_s > 0 && !aligned16(S)) return CAAT_EINVAL;
+    if (c->n_s < c->h && !aligned16(partials)) return CAAT_EINVAL;
+    if (!fused_ok(c) || !t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    return run_row_reduce(c, T, in, W2, S, partials, reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API int caat_sync_norm(caat_handle c, int T, const void *S, const void *partials,
+                            const void *resid, const void *gamma, const void *beta, void *out,
+                            void *out_resid, void *stream) {
+    if (c == nullptr || T < 1) return CAAT_EINVAL;
+    if (c->n_s > 0 && !aligned16(S)) return CAAT_EINVAL;
+    if (c->n_s < c->h && !aligned16(partials)) return CAAT_EINVAL;
+    if (!aligned16(resid) || !aligned16(gamma) || !aligned16(out)) return CAAT_EINVAL;
+    if (!aligned16_or_null(beta) || !aligned16_or_null(out_resid)) return CAAT_EINVAL;
+    if (!fused_ok(c) || !t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    // With n_s == h no private column is read; any aligned pointer stands in.
+    const void *Z = (c->n_s < c->h) ? partials : resid;
+    const void *Sv = (c->n_s > 0) ? S : resid;
+    return run_psync(c, T, Z, resid, gamma, beta, out, out_resid,
+                     reinterpret_cast<hipStream_t>(stream), Sv);
 }
 
 CAAT_API int caat_partial_sync_norm(caat_handle c, int T, const void *partials, const void *resid,

@@ -31,17 +31,21 @@ namespace caat {
 // Epilogues of the GEMM kernels.
 enum Epilogue { EPI_STORE = 0, EPI_GELU = 1, EPI_GELU_TANH = 2, EPI_SWIGLU = 3 };
 
-// One shard-batched "NT" GEMM: for every rank m, token t < T and output column n < N,
-//   acc = sum_{k < K} W[m][row(n)][k] * X[m][t][k]
-// and out[m][t][n] = epilogue(acc).  For EPI_SWIGLU, N counts Y columns and column n
-// uses W rows n (gate) and up_off + n (up): out = silu(gate) * up.
+// One batched "NT" GEMM: for every batch index m < P, token t < T and column n < N,
+//   acc = sum_{g < kseg} sum_{k < K} W[m][g][row(n)][k] * X[m][g][t][k]
+// and out[m][t][n] = epilogue(acc).  kseg > 1 concatenates K segments (the emulated
+// ranks' contractions, summed in the accumulator).  For EPI_SWIGLU, N counts Y columns
+// and column n uses W rows n (gate) and up_off + n (up): out = silu(gate) * up.
 struct GemmArgs {
     int P, N, T, K;
-    const void *W;  size_t w_stride;   // elements between ranks; rows of K elements
-    const void *X;  size_t x_stride;   // elements between ranks; rows of K elements
-    void *out;      size_t o_stride;   // elements between ranks; rows of N elements
+    const void *W;  size_t w_stride;   // elements between batches; rows of K elements
+    const void *X;  size_t x_stride;   // elements between batches; rows of K elements
+    void *out;      size_t o_stride;   // elements between batches
+    int ldo;                           // elements between output rows (tokens)
     int up_off;                        // SwiGLU: W row offset of the up projection
     int epi;
+    int kseg;                          // K segments (>= 1)
+    size_t w_kseg, x_kseg;             // elements between K segments
 };
 
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s);
@@ -51,11 +55,15 @@ bool gemm_bf16_supported(const GemmArgs &a);
 bool gemm_decode_applies(const GemmArgs &a);
 hipError_t gemm_decode_bf16(const GemmArgs &a, hipStream_t s);
 
+// S (nullable): the shared channels already reduced over ranks, [T][s_ld] with
+// s_ld >= n_s; when S is set only the private columns of the partials are read.
 struct PsyncArgs {
     int P, T, h, n_s, norm;
     float s_priv, eps;
     const void *partials, *resid, *gamma, *beta;
     void *out, *out_resid;
+    const void *S;
+    int s_ld;
 };
 
 hipError_t psync_norm(const PsyncArgs &a, int dtype, hipStream_t s);

@@ -114,8 +114,13 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     const __bf16 *Wm = reinterpret_cast<const __bf16 *>(a.W) + (size_t)m * a.w_stride;
     const __bf16 *Xm = reinterpret_cast<const __bf16 *>(a.X) + (size_t)m * a.x_stride;
     const int wrows = (EPI == EPI_SWIGLU) ? a.up_off + N : N;
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wm, (uint32_t)wrows * K * 2u);
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xm, (uint32_t)T * K * 2u);
+    // One descriptor spans every K segment; a segment's offset goes in the scalar
+    // offset of the load, so the per-lane offsets below stay the same for all of them.
+    const int kseg = a.kseg;
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(Wm, (uint32_t)(((size_t)(kseg - 1) * a.w_kseg + (size_t)wrows * K) * 2u));
+    const __amdgpu_buffer_rsrc_t rX =
+        make_rsrc(Xm, (uint32_t)(((size_t)(kseg - 1) * a.x_kseg + (size_t)T * K) * 2u));
 
     // Load i of a lane fills LDS slot (i*NW + wave)*64 + lane: a 64-slot block is 8
     // rows, row = 8 * block + lane / 8, and the slot holds chunk c = (lane & 7) ^ f(row)
@@ -158,25 +163,29 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         boff[kk] = BN * 8 + (wt * WT + r32) * 8 + ((kk * 2 + kh) ^ fr);
     }
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (K + BK - 1) / BK;          // K steps per segment
+    const int nsteps = kseg * nk;              // K steps over all segments
     const bool ktail = (K % BK) != 0;
 
-    // Enqueue the loads of K step k0 into LDS stage Lb.  Only a ragged last step
-    // masks chunks past K (they read as zero).
-#define CAAT_ISSUE(k0, Lb)                                                                 \
+    // Enqueue the loads of combined K step ks (segment ks / nk) into LDS stage Lb.  Only
+    // a ragged last step of a segment masks chunks past K (they read as zero).
+#define CAAT_ISSUE(ks, Lb)                                                                 \
     do {                                                                                   \
-        const int k0_ = (k0);                                                              \
+        const int g_ = (ks) / nk;                                                          \
+        const int k0_ = ((ks) - g_ * nk) * BK;                                             \
+        const uint32_t sw_ = (uint32_t)((g_ * a.w_kseg + k0_) * 2u);                       \
+        const uint32_t sx_ = (uint32_t)((g_ * a.x_kseg + k0_) * 2u);                       \
         if (ktail && k0_ + BK > K) {                                                       \
             CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {                                  \
                 const int base = (i * NW + wave) * 64;                                     \
                 const int c = cl ^ ((i * NW + wave) & 1);                                  \
                 const uint32_t o = (k0_ + c * 8 < K) ? off[i] : OOB;                       \
-                load_lds16(i < WLOADS ? rW : rX, (Lb) + base, o, k0_ * 2);                 \
+                load_lds16(i < WLOADS ? rW : rX, (Lb) + base, o, i < WLOADS ? sw_ : sx_);  \
             }                                                                              \
         } else {                                                                           \
             CAAT_UNROLL for (int i = 0; i < LOADS; ++i)                                    \
                 load_lds16(i < WLOADS ? rW : rX, (Lb) + (i * NW + wave) * 64, off[i],      \
-                           k0_ * 2);                                                       \
+                           i < WLOADS ? sw_ : sx_);                                        \
         }                                                                                  \
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
@@ -215,19 +224,19 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
 
     CAAT_ISSUE(0, L0);
     int kt = 0;
-    for (; kt + 2 <= nk; kt += 2) {
+    for (; kt + 2 <= nsteps; kt += 2) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         CAAT_SCHED_FENCE();
-        CAAT_ISSUE((kt + 1) * BK, L1);
+        CAAT_ISSUE(kt + 1, L1);
         CAAT_COMPUTE(L0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         CAAT_SCHED_FENCE();
-        if (kt + 2 < nk) CAAT_ISSUE((kt + 2) * BK, L0);
+        if (kt + 2 < nsteps) CAAT_ISSUE(kt + 2, L0);
         CAAT_COMPUTE(L1);
     }
-    if (kt < nk) {
+    if (kt < nsteps) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         CAAT_COMPUTE(L0);
@@ -241,7 +250,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     CAAT_UNROLL for (int j = 0; j < JB; ++j) {
         const int t = t0 + wt * WT + j * 32 + r32;
         if (t >= T) continue;
-        __bf16 *orow = O + (size_t)t * N;
+        __bf16 *orow = O + (size_t)t * a.ldo;
         if (EPI == EPI_SWIGLU) {
             CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
                 const int yb = n0 + ((wn * IB + i) >> 1) * 32;
@@ -299,20 +308,24 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 bool gemm_bf16_supported(const GemmArgs &a) {
-    // Byte offsets are 32-bit and must stay below the OOB marker.
+    // Byte offsets (over every K segment) are 32-bit and must stay below the OOB marker.
     const uint64_t wrows = (a.epi == EPI_SWIGLU) ? (uint64_t)a.up_off + a.N : (uint64_t)a.N;
-    return wrows * a.K * 2u < OOB && (uint64_t)a.T * a.K * 2u < OOB && a.K % 8 == 0 &&
-           a.N % 8 == 0;
+    const uint64_t wspan = ((uint64_t)(a.kseg - 1) * a.w_kseg + wrows * a.K) * 2u;
+    const uint64_t xspan = ((uint64_t)(a.kseg - 1) * a.x_kseg + (uint64_t)a.T * a.K) * 2u;
+    return a.kseg >= 1 && wspan < OOB && xspan < OOB && a.K % 8 == 0 && a.N % 8 == 0 &&
+           a.ldo % 8 == 0 && (a.kseg == 1 || a.epi == EPI_STORE);
 }
 
 // Tile choice: 256 x 256 when there are at least two full waves of such tiles on the
-// 256 CUs (4 waves per workgroup for long K, 8 for short K, measured on MI355X), else
-// 128 x 128 so that smaller problems still spread over every CU.
+// 256 CUs, or one full wave with a long contraction; 4 waves per workgroup for long K,
+// 8 for short K (measured on MI355X); else 128 x 128 so that smaller problems still
+// spread over every CU.
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int ncol256 = (a.epi == EPI_SWIGLU) ? 128 : 256;
     const long tiles256 = (long)a.P * ((a.N + ncol256 - 1) / ncol256) * ((a.T + 255) / 256);
-    if (tiles256 >= 512) {
-        if (a.K >= 2048) return launch<256, 256, 2, 2>(a, s);
+    const long ktot = (long)a.K * a.kseg;
+    if (tiles256 >= 512 || (tiles256 >= 256 && ktot >= 4096)) {
+        if (ktot >= 2048) return launch<256, 256, 2, 2>(a, s);
         return launch<256, 256, 2, 4>(a, s);
     }
     return launch<128, 128, 2, 2>(a, s);

@@ -69,8 +69,11 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN
     const __bf16 *Wm = reinterpret_cast<const __bf16 *>(a.W) + (size_t)m * a.w_stride;
     const __bf16 *Xm = reinterpret_cast<const __bf16 *>(a.X) + (size_t)m * a.x_stride;
     const int wrows = (EPI == EPI_SWIGLU) ? a.up_off + N : N;
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(Wm, (uint32_t)wrows * K * 2u);
-    const __amdgpu_buffer_rsrc_t rX = make_rsrc(Xm, (uint32_t)T * K * 2u);
+    // One descriptor spans every K segment (the emulated ranks' contractions).
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(Wm, (uint32_t)(((size_t)(a.kseg - 1) * a.w_kseg + (size_t)wrows * K) * 2u));
+    const __amdgpu_buffer_rsrc_t rX =
+        make_rsrc(Xm, (uint32_t)(((size_t)(a.kseg - 1) * a.x_kseg + (size_t)T * K) * 2u));
 
     // Fragment rows: lane l holds row l % 16 and K values 8 (l / 16) .. + 8 of a step.
     // Weight block i covers output columns n0 + 16 (i % RB) + [0, 16); for SwiGLU the
@@ -87,8 +90,10 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN
         boff[j] = (t < T) ? ((uint32_t)t * K + kq) * 2u : OOB;
     }
 
-    // This wave's K range, in whole steps, processed in batches of U steps.
-    const int nsteps = (K + KSTEP - 1) / KSTEP;
+    // This wave's range of combined K steps (segment st / ksteps, step st % ksteps),
+    // processed in batches of U steps.
+    const int ksteps = (K + KSTEP - 1) / KSTEP;
+    const int nsteps = a.kseg * ksteps;
     const int per = (nsteps + KS - 1) / KS;
     const int s0 = wave * per;
     const int s1 = min(nsteps, s0 + per);
@@ -105,12 +110,15 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN
     do {                                                                                     \
         CAAT_UNROLL for (int u = 0; u < U; ++u) {                                            \
             const int st = s0 + (b) * U + u;                                                 \
-            const int k = st * KSTEP;                                                        \
+            const int g = st / ksteps;                                                       \
+            const int k = (st - g * ksteps) * KSTEP;                                         \
             const bool in = (st < s1) && (k + kq < K);                                       \
+            const uint32_t gw = (uint32_t)((g * a.w_kseg + k) * 2u);                         \
+            const uint32_t gx = (uint32_t)((g * a.x_kseg + k) * 2u);                         \
             CAAT_UNROLL for (int i = 0; i < NA; ++i)                                         \
-                fa[q][u][i] = load16(rW, in ? aoff[i] + k * 2u : OOB);                       \
+                fa[q][u][i] = load16(rW, in ? aoff[i] + gw : OOB);                           \
             CAAT_UNROLL for (int j = 0; j < JB; ++j)                                         \
-                fb[q][u][j] = load16(rX, in ? boff[j] + k * 2u : OOB);                       \
+                fb[q][u][j] = load16(rX, in ? boff[j] + gx : OOB);                           \
         }                                                                                    \
     } while (0)
 #define CAAT_DMMA(q)                                                                         \
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN
                 if (EPI == EPI_SWIGLU) v = silu(v) * acc[RB + rb][j][q];
                 o[q] = static_cast<__bf16>(v);
             }
-            *reinterpret_cast<bf16x4 *>(O + (size_t)t * N + n) = o;
+            *reinterpret_cast<bf16x4 *>(O + (size_t)t * a.ldo + n) = o;
         }
     }
 }

@@ -3,9 +3,9 @@
 //
 // "Tensor-Parallelism with Partially Synchronized Activations", App. A.2, Eq. 22 / 24.
 //
-// 64 tokens x 64 output columns per workgroup, K in steps of 16 through LDS; thread
-// (tx, ty) owns tokens ty*4 + i and columns tx + 16 j.  SwiGLU keeps a gate and an up
-// accumulator per output.  Ragged edges are masked on load (zero) and on store.
+// 64 tokens x 64 output columns per workgroup, K in steps of 16 through LDS (over every
+// K segment in turn); thread (tx, ty) owns tokens ty*4 + i and columns tx + 16 j.
+// SwiGLU keeps a gate and an up accumulator per output.  Ragged edges are masked on load (zero) and on store.
 #include "caat_internal.h"
 
 namespace caat {
@@ -28,36 +28,40 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a)
     const int N = a.N, T = a.T, K = a.K;
 
     float acc[4][4] = {}, accu[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += BKF) {
+    for (int g = 0; g < a.kseg; ++g) {
+        const float *Xg = Xm + (size_t)g * a.x_kseg;
+        const float *Wg = Wm + (size_t)g * a.w_kseg;
+        for (int k0 = 0; k0 < K; k0 += BKF) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = threadIdx.x + i * 256, r = idx >> 4, kk = idx & 15;
-            const int k = k0 + kk;
-            const int t = t0 + r, n = n0 + r;
-            Xs[kk][r] = (t < T && k < K) ? Xm[(size_t)t * K + k] : 0.f;
-            Ws[kk][r] = (n < N && k < K) ? Wm[(size_t)n * K + k] : 0.f;
-            if (GLU) Us[kk][r] = (n < N && k < K) ? Wm[(size_t)(a.up_off + n) * K + k] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < BKF; ++kk) {
-            float xv[4], wv[4], uv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = Xs[kk][ty * 4 + i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                wv[j] = Ws[kk][tx + 16 * j];
-                if (GLU) uv[j] = Us[kk][tx + 16 * j];
+            for (int i = 0; i < 4; ++i) {
+                const int idx = threadIdx.x + i * 256, r = idx >> 4, kk = idx & 15;
+                const int k = k0 + kk;
+                const int t = t0 + r, n = n0 + r;
+                Xs[kk][r] = (t < T && k < K) ? Xg[(size_t)t * K + k] : 0.f;
+                Ws[kk][r] = (n < N && k < K) ? Wg[(size_t)n * K + k] : 0.f;
+                if (GLU) Us[kk][r] = (n < N && k < K) ? Wg[(size_t)(a.up_off + n) * K + k] : 0.f;
             }
+            __syncthreads();
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int kk = 0; kk < BKF; ++kk) {
+                float xv[4], wv[4], uv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[i] = Xs[kk][ty * 4 + i];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
-                    if (GLU) accu[i][j] = fmaf(xv[i], uv[j], accu[i][j]);
+                    wv[j] = Ws[kk][tx + 16 * j];
+                    if (GLU) uv[j] = Us[kk][tx + 16 * j];
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+                        if (GLU) accu[i][j] = fmaf(xv[i], uv[j], accu[i][j]);
+                    }
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     float *O = reinterpret_cast<float *>(a.out) + (size_t)m * a.o_stride;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a)
             if (EPI == EPI_GELU_TANH)
                 v = 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
             if (EPI == EPI_SWIGLU) v = v / (1.0f + expf(-v)) * accu[i][j];
-            O[(size_t)t * N + n] = v;
+            O[(size_t)t * a.ldo + n] = v;
         }
     }
 }

@@ -14,6 +14,11 @@
 // Every partial element is read exactly once (shared part in A, private part in B),
 // the channel mask is a per-element integer compare in registers, and the reduction
 // order is fixed (no atomics), so results are run-to-run deterministic.
+//
+// Fused mode: when the row-parallel GEMM has already summed the shared channels over
+// the ranks in its accumulators (the K-concatenated product of all ranks, §3.2's local
+// summation done in one GEMM), S [T][s_ld] holds them and only the private columns of
+// the partials are read.
 #include "caat_internal.h"
 
 namespace caat {
@@ -88,7 +93,8 @@ __global__ __launch_bounds__(256) void k_psync_norm(
     int P, int T, int h, int n_s, float s_priv, float eps,
     const TIO *__restrict__ partials, const TIO *__restrict__ resid,
     const TIO *__restrict__ gamma, const TIO *__restrict__ beta,
-    TIO *__restrict__ out, TIO *__restrict__ out_resid)
+    TIO *__restrict__ out, TIO *__restrict__ out_resid,
+    const TIO *__restrict__ Sg, int s_ld)
 {
     // Two reduction buffers, used alternately: a buffer is rewritten only after the
     // barrier of the reduction in between, so one barrier per reduction suffices.
@@ -116,14 +122,21 @@ __global__ __launch_bounds__(256) void k_psync_norm(
     for (int j = 0; j < NCH; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) S[j][e] = 0.f;
-    for (int m = 0; m < P; ++m) {
+    if (Sg != nullptr) {
+        // Already reduced over ranks (inside the row-parallel GEMM's accumulators).
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            if (valid[j] && ch0[j] < n_s) {
-                float z[8];
-                Vec8<TIO>::load(partials + m * rank_stride + row + ch0[j], z);
+        for (int j = 0; j < NCH; ++j)
+            if (valid[j] && ch0[j] < n_s) Vec8<TIO>::load(Sg + (size_t)t * s_ld + ch0[j], S[j]);
+    } else {
+        for (int m = 0; m < P; ++m) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) S[j][e] += z[e];
+            for (int j = 0; j < NCH; ++j) {
+                if (valid[j] && ch0[j] < n_s) {
+                    float z[8];
+                    Vec8<TIO>::load(partials + m * rank_stride + row + ch0[j], z);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) S[j][e] += z[e];
+                }
             }
         }
     }
@@ -226,6 +239,7 @@ template <typename TIO> struct Raw;
 template <> struct Raw<__bf16> {
     uint4 u;
     __device__ __forceinline__ void load(const __bf16 *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
     __device__ __forceinline__ void unpack(float (&v)[8]) const {
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -237,6 +251,7 @@ template <> struct Raw<__bf16> {
 };
 template <> struct Raw<float> {
     float4 a, b;
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
     __device__ __forceinline__ void load(const float *p) {
         a = *reinterpret_cast<const float4 *>(p);
         b = *reinterpret_cast<const float4 *>(p + 4);
@@ -257,7 +272,8 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
     int P, int T, int h, int n_s, float s_priv, float eps,
     const TIO *__restrict__ partials, const TIO *__restrict__ resid,
     const TIO *__restrict__ gamma, const TIO *__restrict__ beta,
-    TIO *__restrict__ out, TIO *__restrict__ out_resid)
+    TIO *__restrict__ out, TIO *__restrict__ out_resid,
+    const TIO *__restrict__ Sg, int s_ld)
 {
     __shared__ float red[2][MAX_WAVES_1P * PMAX];
     const int t = blockIdx.x;
@@ -275,7 +291,11 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
         ch0[j] = c * 8;
     }
 
-    Raw<TIO> zr[PMAX][NCH], rr[PMAX][NCH];
+    // With S given, a chunk reads the partials only if it holds a private channel.
+    Raw<TIO> zr[PMAX][NCH], rr[PMAX][NCH], sr[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+        if (Sg != nullptr && valid[j] && ch0[j] < n_s) sr[j].load(Sg + (size_t)t * s_ld + ch0[j]);
 #pragma unroll
     for (int m = 0; m < PMAX; ++m) {
         if (m >= P) break;
@@ -283,18 +303,22 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
         for (int j = 0; j < NCH; ++j) {
             if (!valid[j]) continue;
             const size_t off = m * rank_stride + row + ch0[j];
-            zr[m][j].load(partials + off);
+            if (Sg == nullptr || ch0[j] + 8 > n_s) zr[m][j].load(partials + off);
+            else zr[m][j].zero();
             rr[m][j].load(resid + off);
         }
     }
 
-    // Partial channel-reduce on the shared chunks (ascending ranks, fp32).
+    // Partial channel-reduce on the shared chunks (ascending ranks, fp32), unless S
+    // came already reduced.
     float S[NCH][8];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) S[j][e] = 0.f;
-        if (valid[j] && ch0[j] < n_s) {
+        if (Sg != nullptr) {
+            if (valid[j] && ch0[j] < n_s) sr[j].unpack(S[j]);
+        } else if (valid[j] && ch0[j] < n_s) {
 #pragma unroll
             for (int m = 0; m < PMAX; ++m) {
                 if (m >= P) break;
@@ -396,6 +420,7 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     auto B = reinterpret_cast<const TIO *>(a.beta);
     auto O = reinterpret_cast<TIO *>(a.out);
     auto OR = reinterpret_cast<TIO *>(a.out_resid);
+    auto Sp = reinterpret_cast<const TIO *>(a.S);
     // Registers for one token's raw inputs: 2 * PMAX * NCH chunks of 16 (bf16) or 32
     // (fp32) bytes; the single-pass kernel is used while that stays <= 128 VGPRs.
     const int pmax = a.P <= 1 ? 1 : a.P <= 2 ? 2 : a.P <= 4 ? 4 : a.P <= 8 ? 8 : 16;
@@ -410,7 +435,7 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
         const dim3 block(th);
 #define CAAT_K3S(PM, N)                                                                           \
     hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
-                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR)
+                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
         switch (pmax * 16 + nch) {
         case 1 * 16 + 1: CAAT_K3S(1, 1); break;
         case 1 * 16 + 2: CAAT_K3S(1, 2); break;
@@ -434,7 +459,7 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
 multipass:
 #define CAAT_K3(N)                                                                     \
     hipLaunchKernelGGL((k_psync_norm<N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
-                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR)
+                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
     switch (nch) {
     case 1: CAAT_K3(1); break;
     case 2: CAAT_K3(2); break;

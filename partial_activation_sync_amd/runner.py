@@ -17,7 +17,8 @@ import torch
 
 from . import synth
 from .workloads import ATTN_OUT, MLP, Workload
-from . import Sublayer, caat_column_gemm_act, caat_row_gemm, caat_partial_sync_norm
+from . import (Sublayer, caat_column_gemm_act, caat_partial_sync_norm, caat_row_gemm,
+               caat_row_gemm_reduce, caat_sync_norm)
 
 WEIGHT_STD = 0.02
 
@@ -103,33 +104,50 @@ class Run:
             o["attn_out_resid"] = self.attn_out_resid
         return o
 
-    # The three steps of one sublayer, for per-kernel timing.
+    # The steps of each sublayer as separate calls, for per-kernel timing.  They are the
+    # calls caat_forward_ex makes: K1, the row-parallel GEMM with the shared channels
+    # reduced inside it (when n_s % 8 == 0 and T > 64; else the plain one), and K3.
+    def _buffers(self, sub, kin):
+        key = id(sub)
+        if not hasattr(self, "_bufs"):
+            self._bufs = {}
+        if key not in self._bufs:
+            P, T, h, dt = self.w.P, self.T, self.w.h, torch_dtype(self.w)
+            dev = self.out.device
+            self._bufs[key] = {
+                "Y": torch.empty((P, T, kin), dtype=dt, device=dev) if kin else None,
+                "Z": torch.empty((P, T, h), dtype=dt, device=dev),
+                "S": torch.empty((T, max(sub.n_s, 8)), dtype=dt, device=dev),
+            }
+        return self._bufs[key]
+
+    def _row_and_norm(self, sub, inp, W2, resid, gamma, beta, out, out_resid, b):
+        T = self.T
+        if sub.n_s % 8 == 0 and T > 64:   # the path caat_forward_ex takes
+            S = b["S"] if sub.n_s > 0 else None
+            Z = b["Z"] if sub.n_s < self.w.h else None
+            k2 = lambda: caat_row_gemm_reduce(sub.handle, T, inp, W2, S, Z)
+            k3 = lambda: caat_sync_norm(sub.handle, T, S, Z, resid, gamma, beta, out, out_resid)
+        else:
+            Z = b["Z"]
+            k2 = lambda: caat_row_gemm(sub.handle, T, inp, W2, Z)
+            k3 = lambda: caat_partial_sync_norm(sub.handle, T, Z, resid, gamma, beta, out, out_resid)
+        return k2, k3
+
     def mlp_steps(self, copy=0):
-        """Callables for K1, K2 and K3 of the MLP sublayer on its workspace buffers."""
+        """Callables for K1, K2 and K3 of the MLP sublayer."""
         d, s = dict(self.dev, **self.weight_sets[copy]), self.mlp
-        T, P, h, fs = self.T, self.w.P, self.w.h, self.w.f_s
-        ws = s.workspace(T)
-        es = ws.new_empty(0, dtype=torch_dtype(self.w)).element_size()
-        y_elems = P * T * fs
-        y_bytes = (y_elems * es + 255) // 256 * 256
-        Y = ws[:y_elems * es].view(torch_dtype(self.w)).view(P, T, fs)
-        Z = ws[y_bytes:y_bytes + P * T * h * es].view(torch_dtype(self.w)).view(P, T, h)
+        b = self._buffers(s, self.w.f_s)
         mlp_in = self.attn_out if self.attn is not None else d["x"]
         mlp_resid = self.attn_out_resid if self.attn is not None else d["x"]
-        k1 = lambda: caat_column_gemm_act(s.handle, T, mlp_in, d["W1"], Y)
-        k2 = lambda: caat_row_gemm(s.handle, T, Y, d["W2"], Z)
-        k3 = lambda: caat_partial_sync_norm(s.handle, T, Z, mlp_resid, d["gamma"], d["beta"],
-                                            self.out, self.out_resid)
+        k1 = lambda: caat_column_gemm_act(s.handle, self.T, mlp_in, d["W1"], b["Y"])
+        k2, k3 = self._row_and_norm(s, b["Y"], d["W2"], mlp_resid, d["gamma"], d["beta"],
+                                    self.out, self.out_resid, b)
         return k1, k2, k3
 
     def attn_steps(self, copy=0):
         """Callables for K2 and K3 of the out-projection sublayer."""
         d, s = dict(self.dev, **self.weight_sets[copy]), self.attn
-        T, P, h = self.T, self.w.P, self.w.h
-        ws = s.workspace(T)
-        Z = ws[:P * T * h * ws.new_empty(0, dtype=torch_dtype(self.w)).element_size()]
-        Z = Z.view(torch_dtype(self.w)).view(P, T, h)
-        k2 = lambda: caat_row_gemm(s.handle, T, d["ctx"], d["Wo"], Z)
-        k3 = lambda: caat_partial_sync_norm(s.handle, T, Z, d["x0"], d["gamma"], d["beta"],
-                                            self.attn_out, self.attn_out_resid)
-        return k2, k3
+        b = self._buffers(s, 0)
+        return self._row_and_norm(s, d["ctx"], d["Wo"], d["x0"], d["gamma"], d["beta"],
+                                  self.attn_out, self.attn_out_resid, b)

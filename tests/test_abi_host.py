@@ -80,17 +80,25 @@ def test_setters_and_workspace_size():
     assert L.caat_set_private_scale(hd, float("inf")) == caat.EINVAL
     caat.caat_set_eps(hd, 1e-6)
     caat.caat_set_private_scale(hd, 2 ** 0.5)
-    # Y [P][T][f_s] + partials [P][T][h], each rounded up to 256 bytes.
+    # Y [P][T][f_s] + partials [P][T][h] + S [T][n_s] (n_s = 128, a multiple of 8),
+    # each rounded up to 256 bytes.
     T = 37
     y = (2 * T * 512 * 2 + 255) // 256 * 256
     z = (2 * T * 256 * 2 + 255) // 256 * 256
-    assert caat.caat_workspace_bytes(hd, T) == y + z
+    sh = (T * 128 * 2 + 255) // 256 * 256
+    assert caat.caat_workspace_bytes(hd, T) == y + z + sh
     assert caat.caat_workspace_bytes(hd, 0) == 0
     assert L.caat_set_workspace(hd, 0x1008, 64) == caat.EINVAL   # misaligned
     caat.caat_destroy(hd)
     att = caat.caat_create(256, 0, 2, 0.5, caat.RMSNORM, caat.NONE, caat.F32)
-    assert caat.caat_workspace_bytes(att, T) == (2 * T * 256 * 4 + 255) // 256 * 256
+    assert caat.caat_workspace_bytes(att, T) == ((2 * T * 256 * 4 + 255) // 256 * 256
+                                                 + (T * 128 * 4 + 255) // 256 * 256)
     caat.caat_destroy(att)
+    # n_s not a multiple of 8: no S buffer (the unfused path)
+    odd = caat.caat_create(256, 1024, 2, 0.37, caat.LAYERNORM, caat.GELU, caat.BF16)
+    assert caat.caat_shared_channels(odd) == 94
+    assert caat.caat_workspace_bytes(odd, T) == y + z
+    caat.caat_destroy(odd)
 
 
 def test_forward_checks_before_any_launch():
@@ -116,6 +124,29 @@ def test_forward_checks_before_any_launch():
     a = caat.caat_args(4, fake, None, None, fake, fake, None, fake, None, None)
     assert L.caat_forward_ex(att, ctypes.byref(a)) == caat.EINVAL                     # resid needed
     caat.caat_destroy(att)
+
+
+def test_fused_steps_check_before_any_launch():
+    L = caat.lib()
+    fake = 0x10000
+    odd = caat.caat_create(256, 1024, 2, 0.37, caat.LAYERNORM, caat.GELU, caat.BF16)  # n_s 94
+    assert L.caat_row_gemm_reduce(odd, 4, fake, fake, fake, fake, None) == caat.EUNSUPPORTED
+    assert L.caat_sync_norm(odd, 4, fake, fake, fake, fake, None, fake, None, None) == caat.EUNSUPPORTED
+    caat.caat_destroy(odd)
+    hd = caat.caat_create(256, 1024, 2, 0.5, caat.LAYERNORM, caat.GELU, caat.BF16)
+    assert L.caat_row_gemm_reduce(hd, 4, fake, fake, None, fake, None) == caat.EINVAL   # S needed
+    assert L.caat_row_gemm_reduce(hd, 4, fake, fake, fake, None, None) == caat.EINVAL   # partials
+    assert L.caat_row_gemm_reduce(hd, 0, fake, fake, fake, fake, None) == caat.EINVAL
+    assert L.caat_sync_norm(hd, 4, fake, fake, None, fake, None, fake, None, None) == caat.EINVAL
+    caat.caat_destroy(hd)
+    full = caat.caat_create(256, 1024, 2, 1.0, caat.LAYERNORM, caat.GELU, caat.BF16)   # n_s = h
+    none = caat.caat_create(256, 1024, 2, 0.0, caat.LAYERNORM, caat.GELU, caat.BF16)   # n_s = 0
+    # (a NULL partials with n_s = h, or a NULL S with n_s = 0, passes the checks; those
+    # calls would launch, so they are exercised on the GPU only)
+    assert L.caat_row_gemm_reduce(full, 4, fake, fake, None, None, None) == caat.EINVAL
+    assert L.caat_row_gemm_reduce(none, 4, fake, fake, None, None, None) == caat.EINVAL
+    caat.caat_destroy(full)
+    caat.caat_destroy(none)
 
 
 def test_error_strings():

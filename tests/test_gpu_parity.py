@@ -7,6 +7,7 @@ interact, so a row's oracle value does not depend on the others).
 """
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -216,3 +217,88 @@ def test_forward_plain_entry_point():
     ref = reference(w, inputs)
     errs = compare(w, {"out": out}, ref)
     assert errs["out"] <= TOL[w.dtype]
+
+
+# ---------------------------------------------------------------------------
+# The fused path: shared channels reduced inside the row-parallel GEMM
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wname,T,p", [("tiny-mlp-fp32", 77, 0.5), ("1.1b-mlp-bf16", 200, 0.25),
+                                       ("1.1b-mlp-bf16", 33, 1.0), ("1.1b-mlp-bf16", 40, 0.0),
+                                       ("130m-pair-bf16", 300, 0.5), ("7b-decode-pair-bf16", 8, 0.5)])
+def test_row_gemm_reduce_matches_oracle(wname, T, p):
+    """S [T][n_s] = sum over ranks of the shared partial columns, and the private
+    columns of every rank's partials, against the oracle's per-rank partials."""
+    w = W.ALL[wname]
+    _say(f"[case] row_gemm_reduce {wname} T={T} p={p}")
+    inputs = runner.make_inputs(w, T=T)
+    d = {k: v.cuda() for k, v in inputs.items()}
+    dt = runner.torch_dtype(w)
+    act_name = "none" if "ctx" in d else w.act
+    s = caat.Sublayer(w.h, w.ffn, w.P, p, norm=w.norm, act=act_name, dtype=w.dtype)
+    n_s = s.n_s
+    if act_name == "none":
+        inp, W2 = d["ctx"], d["Wo"]
+    else:
+        Y = torch.empty((w.P, T, w.f_s), dtype=dt, device="cuda")
+        caat.caat_column_gemm_act(s.handle, T, d["x"], d["W1"], Y)
+        inp, W2 = Y, d["W2"]
+    S = torch.full((T, max(n_s, 8)), float("nan"), dtype=dt, device="cuda")
+    Z = torch.full((w.P, T, w.h), float("nan"), dtype=dt, device="cuda")
+    caat.caat_row_gemm_reduce(s.handle, T, inp, W2, S if n_s else None, Z if n_s < w.h else None)
+    torch.cuda.synchronize()
+    if act_name == "none":
+        _, _, zt = oracle.sublayer(inputs["ctx"], None, inputs["Wo"], inputs["gamma"],
+                                   resid=inputs["x0"], act=oracle.NONE, norm=oracle.RMSNORM,
+                                   n_s=0, want_partials=True)
+    else:
+        act = {"gelu": oracle.GELU, "gelu_tanh": oracle.GELU_TANH, "swiglu": oracle.SWIGLU}[w.act]
+        _, _, zt = oracle.sublayer(inputs["x"], inputs["W1"], inputs["W2"], inputs["gamma"],
+                                   act=act, norm=oracle.RMSNORM, n_s=0, want_partials=True)
+    if n_s:
+        ref = zt[:, :, :n_s].sum(0)
+        err = np.abs(S[:, :n_s].double().cpu().numpy() - ref).max() / np.abs(ref).max()
+        _say(f"   S error {err:.2e}")
+        assert err <= TOL[w.dtype]
+    if n_s < w.h:
+        ref = zt[:, :, n_s:]
+        err = np.abs(Z[:, :, n_s:].double().cpu().numpy() - ref).max() / np.abs(ref).max()
+        _say(f"   private partials error {err:.2e}")
+        assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("P,h,T,p", [(8, 4096, 5, 0.5), (4, 768, 33, 0.25), (2, 256, 64, 1.0),
+                                     (3, 264, 7, 0.0)])
+def test_sync_norm_matches_oracle(dtype, P, h, T, p):
+    """K3 on a given S and private partials equals the oracle's reduce + norm on partials
+    whose shared columns hold S on rank 0 and zeros on the other ranks."""
+    _say(f"[case] sync_norm {dtype} P={P} h={h} T={T} p={p}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s = caat.Sublayer(h, 8 * P, P, p, norm="layernorm", act="gelu", dtype=dtype, s_priv=1.5)
+    n_s = s.n_s
+    Sv = synth.normal((T, max(n_s, 8)), synth.PARTIALS, std=2.0, dtype=dt)
+    Z = synth.normal((P, T, h), synth.PARTIALS + 100, dtype=dt)
+    R = synth.normal((P, T, h), synth.RESID, dtype=dt)
+    gamma = synth.normal((h,), synth.GAMMA, std=0.1, mean=1.0, dtype=dt)
+    beta = synth.normal((h,), synth.BETA, std=0.1, dtype=dt)
+    out = torch.empty((P, T, h), dtype=dt, device="cuda")
+    out_resid = torch.empty_like(out)
+    caat.caat_sync_norm(s.handle, T, Sv.cuda() if n_s else None, Z.cuda() if n_s < h else None,
+                        R.cuda(), gamma.cuda(), beta.cuda(), out, out_resid)
+    torch.cuda.synchronize()
+    zo = Z.float().clone()
+    zo[:, :, :n_s] = 0
+    zo[0, :, :n_s] = Sv[:, :n_s].float()
+    ref_out, ref_res = oracle.partial_sync_norm(zo, R, gamma, beta=beta, norm=oracle.LAYERNORM,
+                                                n_s=n_s, s_priv=1.5)
+    tol = TOL[dtype]
+    from tests.oracle_ref import rel_err
+    e1, e2 = rel_err(out, ref_out), rel_err(out_resid, ref_res)
+    _say(f"   errors out {e1:.2e} out_resid {e2:.2e}")
+    assert e1 <= tol and e2 <= tol
+
+
+def test_forward_p0_and_p1_fused():
+    for p in (0.0, 1.0):
+        w = W.with_(W.PREFILL_7B_BF16, T=70, p=p)
+        _run_and_compare(w, norm_params="random")
