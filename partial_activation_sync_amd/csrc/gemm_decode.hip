@@ -8,18 +8,18 @@
 // MFMA v_mfma_f32_16x16x32_bf16 with the weight rows as the row operand (16 output
 // channels per block) and the tokens as the column operand (16 per block, JB blocks).
 // A workgroup owns 16 or 32 output columns of one rank (for SwiGLU also the matching
-// up rows) and its KS waves split K; each wave streams its weight slice with buffer
-// loads straight into MFMA fragments (four lanes read 64 contiguous bytes of a row per
-// instruction), one batch of k-steps in flight while the previous batch is multiplied.  The activations are
-// small and read through the caches.  The KS partial accumulators are summed through
+// up rows) and its KS waves split K.  The KS partial accumulators are summed through
 // LDS in a fixed order, then the epilogue (GeLU / SwiGLU / plain store) runs in wave 0.
 // Tokens beyond T and the K tail read as zero through the buffer range check.
 #include "caat_internal.h"
 
 #if defined(__HIP_DEVICE_COMPILE__)
 #define CAAT_UNROLL _Pragma("unroll")
+// Keeps the scheduler from moving instructions across this point.
+#define CAAT_FENCE() __builtin_amdgcn_sched_barrier(0)
 #else
 #define CAAT_UNROLL
+#define CAAT_FENCE()
 #endif
 
 namespace caat {
@@ -37,6 +37,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              RSRC_WORD3);
 }
+// 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff,
+                                           uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
 __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -48,17 +54,26 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 }
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// RB: 16-column output blocks per workgroup; NA = RB (x2 for SwiGLU: gate, up) weight
-// row blocks; JB: 16-token blocks; KS: waves splitting K; U: k-steps per load batch.
-// Batches are double-buffered: the loads of batch b+1 are issued before the MFMAs of
-// batch b, so every wave keeps one batch of loads in flight while it computes.
+// Weight stream through wave-private LDS.  A wave's weight rows are copied into its own
+// LDS region with buffer loads that write LDS directly, each instruction reading 1 KB of
+// contiguous weights (4 rows x 256 B: 64 lanes x 16 B), in stages of KST = 128 K values;
+// MFMA fragments are then read from LDS.  The global side picks, for LDS slot (row, j),
+// the chunk j ^ (row % 16), so the fragment reads (16 rows at one chunk) hit 16 distinct
+// bank groups.  Every wave reads only the rows it loaded itself, so no workgroup barrier
+// is needed in the K loop; the two stages live in two LDS arrays so the compiler's
+// per-wave wait before a fragment read covers the stage being read and leaves the next
+// stage's loads in flight.  The JB token blocks (16 tokens each) are read from memory
+// (they are small and stay in the caches) and each weight fragment feeds JB MFMAs.
 template <int EPI, int RB, int JB, int KS>
-__global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN)
+__global__ __launch_bounds__(64 * KS) void k_gemm_decode_lds(GemmArgs a, int blocksN)
 {
     constexpr int NA = (EPI == EPI_SWIGLU) ? 2 * RB : RB;
-    constexpr int FR = NA + JB;                        // fragments per k-step
-    constexpr int U = (16 / FR) >= 4 ? 4 : (16 / FR) >= 2 ? 2 : 1;
-    __shared__ f32x4 red[KS > 1 ? KS : 1][NA][JB][64];
+    constexpr int ROWS = NA * 16;
+    constexpr int KST = 128, CH = KST / 8;          // K values and 16-byte chunks per stage
+    constexpr int DMAS = ROWS * CH / 64;            // LDS-load instructions per stage
+    static_assert(JB <= 4, "the KS x NA x JB reduction tiles must fit in one stage array");
+    __shared__ __attribute__((aligned(16))) uint4 L0[KS][ROWS * CH];
+    __shared__ __attribute__((aligned(16))) uint4 L1[KS][ROWS * CH];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -69,99 +84,121 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN
     const __bf16 *Wm = reinterpret_cast<const __bf16 *>(a.W) + (size_t)m * a.w_stride;
     const __bf16 *Xm = reinterpret_cast<const __bf16 *>(a.X) + (size_t)m * a.x_stride;
     const int wrows = (EPI == EPI_SWIGLU) ? a.up_off + N : N;
-    // One descriptor spans every K segment (the emulated ranks' contractions).
     const __amdgpu_buffer_rsrc_t rW =
         make_rsrc(Wm, (uint32_t)(((size_t)(a.kseg - 1) * a.w_kseg + (size_t)wrows * K) * 2u));
     const __amdgpu_buffer_rsrc_t rX =
         make_rsrc(Xm, (uint32_t)(((size_t)(a.kseg - 1) * a.x_kseg + (size_t)T * K) * 2u));
 
-    // Fragment rows: lane l holds row l % 16 and K values 8 (l / 16) .. + 8 of a step.
-    // Weight block i covers output columns n0 + 16 (i % RB) + [0, 16); for SwiGLU the
-    // blocks i >= RB are the matching up rows.
-    const int r16 = lane & 15, kq = (lane >> 4) * 8;
-    uint32_t aoff[NA], boff[JB];
-    CAAT_UNROLL for (int i = 0; i < NA; ++i) {
-        const int n = n0 + 16 * (i % RB) + r16;
-        const int row = (i >= RB) ? a.up_off + n : n;
-        aoff[i] = (n < N) ? ((uint32_t)row * K + kq) * 2u : OOB;
+    // LDS-load d of a stage covers local rows 4d .. 4d+3; lane i fills slot (row, i % 16)
+    // with global chunk (i % 16) ^ (row % 16) of that row.
+    uint32_t roff[DMAS];
+    int rchunk[DMAS];
+    CAAT_UNROLL for (int d = 0; d < DMAS; ++d) {
+        const int row = 4 * d + (lane >> 4);           // local row: block row / 16, r = row % 16
+        const int blk = row >> 4, r = row & 15;
+        const int n = n0 + 16 * (blk % RB) + r;
+        const int grow = (blk >= RB) ? a.up_off + n : n;
+        rchunk[d] = (lane & 15) ^ r;
+        roff[d] = (n < N) ? ((uint32_t)grow * K + rchunk[d] * 8) * 2u : OOB;
     }
+    // Token fragments straight from memory: lane l holds token 16 j + l % 16, K chunk l / 16.
+    const int r16 = lane & 15, kq = (lane >> 4) * 8;
+    uint32_t boff[JB];
     CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-        const int t = j * 16 + r16;
+        const int t = 16 * j + r16;
         boff[j] = (t < T) ? ((uint32_t)t * K + kq) * 2u : OOB;
     }
 
-    // This wave's range of combined K steps (segment st / ksteps, step st % ksteps),
-    // processed in batches of U steps.
-    const int ksteps = (K + KSTEP - 1) / KSTEP;
-    const int nsteps = a.kseg * ksteps;
-    const int per = (nsteps + KS - 1) / KS;
-    const int s0 = wave * per;
-    const int s1 = min(nsteps, s0 + per);
-    const int nb = (s1 > s0) ? (s1 - s0 + U - 1) / U : 0;
+    // This wave's stages (segment st / kst, K offset (st % kst) * KST).
+    const int kst = (K + KST - 1) / KST;
+    const int nst = a.kseg * kst;
+    const int per = (nst + KS - 1) / KS;
+    const int s0 = wave * per, s1 = min(nst, s0 + per);
 
     f32x4 acc[NA][JB];
     CAAT_UNROLL for (int i = 0; i < NA; ++i)
         CAAT_UNROLL for (int j = 0; j < JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8 fa[2][U][NA], fb[2][U][JB];
-    // Loads of batch b into buffer q.  A step past this wave's range, or a chunk past
-    // K, reads as zero.
-#define CAAT_DLOAD(q, b)                                                                     \
-    do {                                                                                     \
-        CAAT_UNROLL for (int u = 0; u < U; ++u) {                                            \
-            const int st = s0 + (b) * U + u;                                                 \
-            const int g = st / ksteps;                                                       \
-            const int k = (st - g * ksteps) * KSTEP;                                         \
-            const bool in = (st < s1) && (k + kq < K);                                       \
-            const uint32_t gw = (uint32_t)((g * a.w_kseg + k) * 2u);                         \
-            const uint32_t gx = (uint32_t)((g * a.x_kseg + k) * 2u);                         \
-            CAAT_UNROLL for (int i = 0; i < NA; ++i)                                         \
-                fa[q][u][i] = load16(rW, in ? aoff[i] + gw : OOB);                           \
-            CAAT_UNROLL for (int j = 0; j < JB; ++j)                                         \
-                fb[q][u][j] = load16(rX, in ? boff[j] + gx : OOB);                           \
-        }                                                                                    \
-    } while (0)
-#define CAAT_DMMA(q)                                                                         \
-    do {                                                                                     \
-        CAAT_UNROLL for (int u = 0; u < U; ++u)                                              \
-            CAAT_UNROLL for (int i = 0; i < NA; ++i)                                         \
-                CAAT_UNROLL for (int j = 0; j < JB; ++j)                                     \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                     \
-                        fa[q][u][i], fb[q][u][j], acc[i][j], 0, 0, 0);                       \
-    } while (0)
+    // Loads of stage st: its token fragments into registers, then its weights into LDS.
+    // Everything stage st needs is issued before anything of stage st + 1, so the wait
+    // before computing stage st (loads return in order) leaves stage st + 1 in flight.
+    typedef bf16x8 XFrag[KST / 32][JB];
+    auto issue = [&](int st, uint4 *Lw, XFrag &xb) {
+        const int g = st / kst, k0 = (st - g * kst) * KST;
+        const uint32_t sx = (uint32_t)((g * a.x_kseg + k0) * 2u);
+        CAAT_UNROLL for (int u = 0; u < KST / 32; ++u)
+            CAAT_UNROLL for (int j = 0; j < JB; ++j)
+                xb[u][j] = load16(rX, (k0 + u * 32 + kq < K) ? boff[j] + sx + u * 64u : OOB);
+        const uint32_t so = (uint32_t)((g * a.w_kseg + k0) * 2u);
+        CAAT_UNROLL for (int d = 0; d < DMAS; ++d) {
+            const uint32_t o = (k0 + rchunk[d] * 8 < K) ? roff[d] : OOB;
+            load_lds16(rW, Lw + d * 64, o, so);
+        }
+    };
+    auto compute = [&](const uint4 *Lw, const XFrag &xb) {
+        CAAT_UNROLL for (int u = 0; u < KST / 32; ++u) {
+            const int c = u * 4 + (lane >> 4);          // logical chunk of this step
+            CAAT_UNROLL for (int i = 0; i < NA; ++i) {
+                const bf16x8 af = __builtin_bit_cast(bf16x8, Lw[(i * 16 + r16) * CH + (c ^ r16)]);
+                CAAT_UNROLL for (int j = 0; j < JB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, xb[u][j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
 
-    if (nb > 0) CAAT_DLOAD(0, 0);
-    int b = 0;
-    for (; b + 2 <= nb; b += 2) {
-        CAAT_DLOAD(1, b + 1);
-        CAAT_DMMA(0);
-        if (b + 2 < nb) CAAT_DLOAD(0, b + 2);
-        CAAT_DMMA(1);
+    // The loop body issues unconditionally (a branch around loads would make the
+    // compiler wait for all of them where the paths join); the last one or two stages
+    // are finished after it.
+    uint4 *W0 = L0[wave], *W1 = L1[wave];
+    XFrag x0, x1;
+    if (s0 < s1) issue(s0, W0, x0);
+    int st = s0;
+    // Each issue is fenced, so the fragment reads of the stage being computed stay
+    // behind the loads of the next stage.
+    for (; st + 3 <= s1; st += 2) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage-1 reads done
+        issue(st + 1, W1, x1);
+        CAAT_FENCE();
+        compute(W0, x0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage-0 reads done
+        issue(st + 2, W0, x0);
+        CAAT_FENCE();
+        compute(W1, x1);
     }
-    if (b < nb) CAAT_DMMA(0);
-#undef CAAT_DLOAD
-#undef CAAT_DMMA
+    if (st + 2 == s1) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(st + 1, W1, x1);
+        CAAT_FENCE();
+        compute(W0, x0);
+        compute(W1, x1);
+    } else if (st + 1 == s1) {
+        compute(W0, x0);
+    }
 
+    // Sum the KS partial accumulators through LDS (stage-0 array reused), fixed order.
+    f32x4 *red = reinterpret_cast<f32x4 *>(&L0[0][0]);
+    __syncthreads();
     if (KS > 1) {
         CAAT_UNROLL for (int i = 0; i < NA; ++i)
-            CAAT_UNROLL for (int j = 0; j < JB; ++j) red[wave][i][j][lane] = acc[i][j];
+            CAAT_UNROLL for (int j = 0; j < JB; ++j)
+                red[((wave * NA + i) * JB + j) * 64 + lane] = acc[i][j];
         __syncthreads();
         if (wave != 0) return;
         CAAT_UNROLL for (int i = 0; i < NA; ++i)
             CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-                f32x4 v = red[0][i][j][lane];
-                CAAT_UNROLL for (int w = 1; w < KS; ++w) v += red[w][i][j][lane];
+                f32x4 v = red[(i * JB + j) * 64 + lane];
+                CAAT_UNROLL for (int w = 1; w < KS; ++w) v += red[((w * NA + i) * JB + j) * 64 + lane];
                 acc[i][j] = v;
             }
     }
 
-    // Accumulator element v of lane l is output row 4 (l / 16) + v, token l % 16.
+    // Accumulator element v of lane l is output row 4 (l / 16) + v, token 16 j + l % 16.
     __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
     CAAT_UNROLL for (int rb = 0; rb < RB; ++rb) {
         const int n = n0 + 16 * rb + 4 * (lane >> 4);
         if (n >= N) continue;
         CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-            const int t = j * 16 + r16;
+            const int t = 16 * j + r16;
             if (t >= T) continue;
             bf16x4 o;
             CAAT_UNROLL for (int q = 0; q < 4; ++q) {
@@ -177,49 +214,44 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode(GemmArgs a, int blocksN
 }
 
 template <int RB, int JB, int KS>
-hipError_t launch(const GemmArgs &a, hipStream_t s) {
+hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
     const int blocksN = (a.N + 16 * RB - 1) / (16 * RB);
     const dim3 grid(a.P * blocksN), block(64 * KS);
     switch (a.epi) {
     case EPI_GELU:
-        hipLaunchKernelGGL((k_gemm_decode<EPI_GELU, RB, JB, KS>), grid, block, 0, s, a, blocksN);
+        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_GELU, RB, JB, KS>), grid, block, 0, s, a, blocksN);
         break;
     case EPI_GELU_TANH:
-        hipLaunchKernelGGL((k_gemm_decode<EPI_GELU_TANH, RB, JB, KS>), grid, block, 0, s, a, blocksN);
+        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_GELU_TANH, RB, JB, KS>), grid, block, 0, s, a, blocksN);
         break;
     case EPI_SWIGLU:
-        hipLaunchKernelGGL((k_gemm_decode<EPI_SWIGLU, RB, JB, KS>), grid, block, 0, s, a, blocksN);
+        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_SWIGLU, RB, JB, KS>), grid, block, 0, s, a, blocksN);
         break;
     default:
-        hipLaunchKernelGGL((k_gemm_decode<EPI_STORE, RB, JB, KS>), grid, block, 0, s, a, blocksN);
+        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_STORE, RB, JB, KS>), grid, block, 0, s, a, blocksN);
         break;
     }
     return hipGetLastError();
-}
-
-// K is split over KS waves so that many waves per SIMD stream weights at once; 8-wave
-// workgroups (at most 256 registers per lane) only for one-block workgroups.
-template <int RB, int JB>
-hipError_t launch_ks(const GemmArgs &a, hipStream_t s) {
-    const long units = (long)a.P * ((a.N + 16 * RB - 1) / (16 * RB));
-    if constexpr (RB == 1) {
-        if (units < 1024) return launch<RB, JB, 8>(a, s);
-    }
-    if (units < 4096) return launch<RB, JB, 4>(a, s);
-    return launch<RB, JB, 2>(a, s);
 }
 
 }  // namespace
 
 bool gemm_decode_applies(const GemmArgs &a) { return a.T <= 64; }
 
-// One 16-column block per workgroup for up to 16 tokens; two above that, so each
-// activation fragment read feeds twice the weight bytes.
+// One 16-row weight block (32 rows for SwiGLU: gate and up) per wave with K split over
+// 4 waves while the token blocks are few and K is long enough for every wave to keep
+// two stages in flight; otherwise two blocks per wave (each token fragment read then
+// feeds twice the weight bytes) and one wave per workgroup.
 hipError_t gemm_decode_bf16(const GemmArgs &a, hipStream_t s) {
-    if (a.T <= 16) return launch_ks<1, 1>(a, s);
-    if (a.T <= 32) return launch_ks<2, 2>(a, s);
-    if (a.T <= 48) return launch_ks<2, 3>(a, s);
-    return launch_ks<2, 4>(a, s);
+    const int tmax = (a.epi == EPI_SWIGLU) ? 16 : 8;
+    const int jb = (a.T + 15) / 16;
+    if (a.K >= 1024 && a.T <= tmax) return launch_lds<1, 1, 4>(a, s);
+    switch (jb) {
+    case 1: return launch_lds<2, 1, 1>(a, s);
+    case 2: return launch_lds<2, 2, 1>(a, s);
+    case 3: return launch_lds<2, 3, 1>(a, s);
+    default: return launch_lds<2, 4, 1>(a, s);
+    }
 }
 
 }  // namespace caat

@@ -406,6 +406,92 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
     }
 }
 
+// Small-batch variant (T <= 64): one workgroup per (token, rank), so a decode batch
+// spreads over P x T workgroups instead of T.  Each workgroup reads the shared columns
+// of every rank (or S) and only its own rank's private columns and residual; the
+// shared columns are thereby read P times, which is a few MB at these sizes.
+template <int NCH, int NORM, typename TIO>
+__global__ __launch_bounds__(512) void k_psync_norm_rank(
+    int P, int T, int h, int n_s, float s_priv, float eps,
+    const TIO *__restrict__ partials, const TIO *__restrict__ resid,
+    const TIO *__restrict__ gamma, const TIO *__restrict__ beta,
+    TIO *__restrict__ out, TIO *__restrict__ out_resid,
+    const TIO *__restrict__ Sg, int s_ld)
+{
+    __shared__ float red[2][MAX_WAVES_1P];
+    const int t = blockIdx.x, m = blockIdx.y;
+    const int nchunk = h >> 3;
+    const size_t rank_stride = (size_t)T * h;
+    const size_t row = (size_t)t * h;
+    const size_t own = m * rank_stride + row;
+    const float inv_h = 1.0f / (float)h;
+
+    float r[NCH][8];
+    float acc[1] = {0.f};
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        const int ch0 = c * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[j][e] = 0.f;
+        if (c >= nchunk) continue;
+        float S[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, z[8], res[8];
+        if (ch0 < n_s) {
+            if (Sg != nullptr) {
+                Vec8<TIO>::load(Sg + (size_t)t * s_ld + ch0, S);
+            } else {
+                for (int q = 0; q < P; ++q) {
+                    Vec8<TIO>::load(partials + q * rank_stride + row + ch0, z);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) S[e] += z[e];
+                }
+            }
+        }
+        if (ch0 + 8 > n_s) Vec8<TIO>::load(partials + own + ch0, z);
+        Vec8<TIO>::load(resid + own + ch0, res);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            r[j][e] = res[e] + ((ch0 + e < n_s) ? S[e] : s_priv * z[e]);
+            acc[0] += (NORM == CAAT_LAYERNORM) ? r[j][e] : r[j][e] * r[j][e];
+        }
+    }
+    block_sum<1>(acc, red[0]);
+    float mean = 0.f;
+    if (NORM == CAAT_LAYERNORM) {
+        mean = acc[0] * inv_h;
+        acc[0] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            if ((int)(threadIdx.x + j * blockDim.x) >= nchunk) continue;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = r[j][e] - mean;
+                acc[0] += d * d;
+            }
+        }
+        block_sum<1>(acc, red[1]);
+    }
+    const float inv = rsqrtf(acc[0] * inv_h + eps);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        if (c >= nchunk) continue;
+        const int ch0 = c * 8;
+        float gm[8], bt[8], o[8];
+        Vec8<TIO>::load(gamma + ch0, gm);
+        if (NORM == CAAT_LAYERNORM && beta != nullptr) {
+            Vec8<TIO>::load(beta + ch0, bt);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bt[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = (r[j][e] - mean) * inv * gm[e] + bt[e];
+        Vec8<TIO>::store(out + own + ch0, o);
+        if (out_resid != nullptr) Vec8<TIO>::store(out_resid + own + ch0, r[j]);
+    }
+}
+
 template <int NORM, typename TIO>
 hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     const int nchunk = a.h / 8;
@@ -421,6 +507,25 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     auto O = reinterpret_cast<TIO *>(a.out);
     auto OR = reinterpret_cast<TIO *>(a.out_resid);
     auto Sp = reinterpret_cast<const TIO *>(a.S);
+    if (a.T <= 64 && a.P > 1) {
+        int nchr = 1;
+        while (nchr < 4 && nchunk > nchr * 512) nchr *= 2;
+        if (nchunk <= nchr * 512) {
+            int th = (nchunk + nchr - 1) / nchr;
+            th = (th + 63) / 64 * 64;
+            const dim3 grid_r(a.T, a.P), block_r(th);
+#define CAAT_K3R(N)                                                                          \
+    hipLaunchKernelGGL((k_psync_norm_rank<N, NORM, TIO>), grid_r, block_r, 0, s, a.P, a.T, a.h, \
+                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
+            switch (nchr) {
+            case 1: CAAT_K3R(1); break;
+            case 2: CAAT_K3R(2); break;
+            default: CAAT_K3R(4); break;
+            }
+#undef CAAT_K3R
+            return hipGetLastError();
+        }
+    }
     // Registers for one token's raw inputs: 2 * PMAX * NCH chunks of 16 (bf16) or 32
     // (fp32) bytes; the single-pass kernel is used while that stays <= 128 VGPRs.
     const int pmax = a.P <= 1 ? 1 : a.P <= 2 ? 2 : a.P <= 4 ? 4 : a.P <= 8 ? 8 : 16;

@@ -71,6 +71,13 @@ def test_7b_decode_full(T):
     _run_and_compare(W.DECODE_7B_BF16, T=T)
 
 
+# Decode batch sizes between the benchmarked ones: each weight-streaming launch shape
+# (one or two weight blocks per wave, 1 to 4 token blocks, ragged last block).
+@pytest.mark.parametrize("T", [9, 16, 17, 40])
+def test_7b_decode_launch_shapes(T):
+    _run_and_compare(W.DECODE_7B_BF16, T=T, norm_params="random")
+
+
 # ---------------------------------------------------------------------------
 # Full sizes, in the launch configuration the benchmark times: sampled rows
 # ---------------------------------------------------------------------------
@@ -302,3 +309,27 @@ def test_forward_p0_and_p1_fused():
     for p in (0.0, 1.0):
         w = W.with_(W.PREFILL_7B_BF16, T=70, p=p)
         _run_and_compare(w, norm_params="random")
+
+
+def test_graph_replay_matches_eager():
+    """One decode step captured as a HIP graph: every replay (with eager work between
+    replays) reproduces the eager outputs bitwise."""
+    w = W.with_(W.DECODE_7B_BF16, T=8)
+    run = runner.Run(w, runner.make_inputs(w, norm_params="random"))
+    steps = list(run.attn_steps()) + list(run.mlp_steps())
+    for k in steps:
+        k()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in run.outputs().items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in steps:
+            k()
+    for rep in range(3):
+        for v in run.outputs().values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in run.outputs().items():
+            assert torch.equal(v, eager[k]), (rep, k)
