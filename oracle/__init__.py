@@ -1,4 +1,4 @@
-"""Oracle for the CAAT partial-sync sublayer forward.
+"""Oracle for the CAAT partial-sync sublayer forward and backward.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library and its
@@ -7,11 +7,14 @@ Python binding never import it, and the two share no code.
 The arithmetic lives in ``caat_oracle.c`` (plain C, fp64, OpenMP over rank and
 token rows); this module only converts arrays and calls it.  Source of the method:
 "Tensor-Parallelism with Partially Synchronized Activations", App. A.2 Eq. 22 and 24,
-§3.2 (logical devices), §4 Eq. 9 and "Private channel scaling".
+§3.2 (logical devices), §4 Eq. 9 and "Private channel scaling"; the backward follows
+§4 "Forward-backward mismatch" (Eq. 10-13) and App. B (Eq. 26-30).
 
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-against closed forms, library routines on special cases, the page's P = 2 block
-form (Eq. 8 / Eq. 19), a hand-derived worked example and brute force on tiny shapes.
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_backward_pins.py`` against closed forms, library routines on
+special cases, the page's P = 2 block form (Eq. 8 / Eq. 19), a hand-derived worked
+example, brute force on tiny shapes and (backward) central finite differences of
+the forward.
 The bf16 roundings of the GPU path (intermediate activations, partials, outputs)
 are not modelled: the page fixes none of them, and the tolerance absorbs them.
 """
@@ -50,6 +53,10 @@ def _load():
             [ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_double]
             + [fp] * 4 + [dp] * 2)
         lib.oracle_partial_sync_norm.restype = ctypes.c_int
+        lib.oracle_sublayer_backward.argtypes = (
+            [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double]
+            + [fp] * 7 + [dp] * 6)
+        lib.oracle_sublayer_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -140,3 +147,43 @@ def partial_sync_norm(partials, resid, gamma, *, norm, n_s, beta=None, s_priv=1.
     if rc != 0:
         raise ValueError("oracle_partial_sync_norm rejected its arguments")
     return out, out_resid
+
+
+def sublayer_backward(x, W1, W2, gamma, dout, *, act, norm, n_s, resid=None, dres=None,
+                      s_priv=1.0, eps=1e-5):
+    """Backward of one CAAT sublayer for every rank, in fp64 (§4, App. B).
+
+    Forward inputs as for ``sublayer``; dout [P][T][h] is the gradient of the loss
+    w.r.t. out and dres [P][T][h] (None: zero) w.r.t. out_resid.  Returns a dict of
+    float64 arrays: dx [P][T][kin] (with resid=None the residual gradient is included),
+    dresid [P][T][h], dW1 [P][F1][h] (None for act=NONE), dW2 [P][h][k2], dgamma [h],
+    dbeta [h] (zero for RMSNorm).
+    """
+    x = _f32(x)
+    W2 = _f32(W2)
+    P, T, kin = x.shape
+    h, k2 = W2.shape[1], W2.shape[2]
+    if act == NONE:
+        W1 = None
+        ffn, F1 = 0, 0
+    else:
+        W1 = _f32(W1)
+        ffn = k2 * P
+        F1 = W1.shape[1]
+    gamma, resid, dout, dres = _f32(gamma), _f32(resid), _f32(dout), _f32(dres)
+    res = {
+        "dx": np.empty((P, T, kin), np.float64),
+        "dresid": np.empty((P, T, h), np.float64),
+        "dW1": np.empty((P, F1, h), np.float64) if act != NONE else None,
+        "dW2": np.empty((P, h, k2), np.float64),
+        "dgamma": np.empty((h,), np.float64),
+        "dbeta": np.empty((h,), np.float64),
+    }
+    rc = _load().oracle_sublayer_backward(
+        P, T, h, ffn, act, norm, n_s, float(s_priv), float(eps),
+        _fptr(x), _fptr(resid), _fptr(W1), _fptr(W2), _fptr(gamma), _fptr(dout), _fptr(dres),
+        _dptr(res["dx"]), _dptr(res["dresid"]), _dptr(res["dW1"]), _dptr(res["dW2"]),
+        _dptr(res["dgamma"]), _dptr(res["dbeta"]))
+    if rc != 0:
+        raise ValueError("oracle_sublayer_backward rejected its arguments")
+    return res

@@ -1,5 +1,5 @@
 /*
- * CAAT partial-sync sublayer forward: the ORACLE.
+ * CAAT partial-sync sublayer forward and backward: the ORACLE.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, fp64 CPU statement of
  * what one CAAT tensor-parallel sublayer computes.  Only the test suite, the smoke
@@ -21,6 +21,9 @@
  *   - Residual add and normalization after the reduce, per rank: §4, Eq. 9, and
  *     App. B, Eq. 25 (the residual splits off before the normalization).
  *   - Private channel scaling by sqrt(r): §4, "Private channel scaling", Eq. 14-15.
+ *   - Backward: §4 "Forward-backward mismatch" (Eq. 9-13) and App. B (Eq. 25-30):
+ *     the reduce over ranks comes after the norm derivative, and the norm
+ *     parameters' gradients are summed over ranks.
  *
  * Readings where the page is silent (each one is listed in the design notes):
  *   - n_s = floor(h*p), where an h*p within 1e-9*h of an integer k counts as k.
@@ -275,5 +278,280 @@ int oracle_partial_sync_norm(int P, int T, int h, int norm, int n_s, double s_pr
     reduce_residual_norm(P, T, h, n_s, s_priv, eps, norm, zt, resid, gamma, beta,
                          out, out_resid);
     free(zt);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------------
+ * Backward of the sublayer (§4 "Forward-backward mismatch", Eq. 9-13; App. B,
+ * Eq. 25-30).  The loss reaches the sublayer through out = Norm(r) (upstream
+ * gradient dout) and through the residual stream r itself (upstream gradient dres,
+ * the gradient of whatever the next sublayer adds r into).  Per rank m:
+ *   g_m = dres_m + (dNorm/dr at r_m)^T dout_m      -- the norm derivative first, per
+ *                                                   rank (the 'h' placement of §4)
+ *   dZt_q[l] = sum_m g_m[l]      for l < n_s      -- the reduce after the norm
+ *   dZt_q[l] = s_priv * g_q[l]   for l >= n_s        derivative (Eq. 26-28)
+ *   dresid_m = g_m                                   (the residual term of Eq. 26)
+ *   dgamma = sum_{m,t} dout * nhat, dbeta = sum_{m,t} dout   (Eq. 12, 29: the norm
+ *                                                   parameters reduced over ranks)
+ * then the chain rule through the two GEMMs and the nonlinearity of Eq. 22 / 24.
+ */
+
+/* d sigma / d a for the one-input activations (GeLU forms). */
+static double act_grad(int act, double a)
+{
+    if (act == ORACLE_GELU) {
+        /* d/da [a Phi(a)] = Phi(a) + a phi(a) */
+        const double Phi = 0.5 * erfc(-a / sqrt(2.0));
+        const double phi = exp(-0.5 * a * a) / sqrt(2.0 * 3.14159265358979323846);
+        return Phi + a * phi;
+    }
+    if (act == ORACLE_GELU_TANH) {
+        const double c = sqrt(2.0 / 3.14159265358979323846);
+        const double u = c * (a + 0.044715 * a * a * a);
+        const double th = tanh(u);
+        return 0.5 * (1.0 + th) + 0.5 * a * (1.0 - th * th) * c * (1.0 + 3.0 * 0.044715 * a * a);
+    }
+    return 1.0;
+}
+
+/* Returns 0, or -1 on bad arguments.  Outputs (fp64, all overwritten):
+ *   dx     [P][T][kin]  gradient of the loss w.r.t. x (when resid is NULL, i.e.
+ *                       resid = x, the residual gradient is included)
+ *   dresid [P][T][h]    gradient w.r.t. resid (may be NULL)
+ *   dW1    [P][F1][h]   (NULL for act = NONE), dW2 [P][h][k2]
+ *   dgamma [h], dbeta [h] (dbeta is zero for RMSNorm)
+ * dres NULL means zero.  zt and the norm statistics are recomputed here. */
+int oracle_sublayer_backward(int P, int T, int h, int ffn, int act, int norm, int n_s,
+                             double s_priv, double eps,
+                             const float *x, const float *resid, const float *W1,
+                             const float *W2, const float *gamma,
+                             const float *dout, const float *dres,
+                             double *dx, double *dresid, double *dW1, double *dW2,
+                             double *dgamma, double *dbeta)
+{
+    if (check_common(P, T, h, n_s, norm) || act < ORACLE_GELU || act > ORACLE_NONE)
+        return -1;
+    int fs = 0, kin, F1 = 0;
+    if (act == ORACLE_NONE) {
+        if (h % P)
+            return -1;
+        kin = h / P;
+    } else {
+        if (ffn % P)
+            return -1;
+        fs = ffn / P;
+        F1 = (act == ORACLE_SWIGLU) ? 2 * fs : fs;
+        kin = h;
+    }
+    const int resid_is_x = (resid == NULL);
+    if (resid_is_x) {
+        if (act == ORACLE_NONE)
+            return -1;
+        resid = x;
+    }
+    const int k2 = (act == ORACLE_NONE) ? kin : fs;
+    const size_t rows = (size_t)P * T;
+    double *a = (double *)calloc(rows * (size_t)(F1 > 0 ? F1 : 1), sizeof(double));
+    double *y = (double *)calloc(rows * (size_t)k2, sizeof(double));
+    double *zt = (double *)calloc(rows * (size_t)h, sizeof(double));
+    double *nh = (double *)calloc(rows * (size_t)h, sizeof(double));
+    double *g = (double *)calloc(rows * (size_t)h, sizeof(double));
+    double *dzt = (double *)calloc(rows * (size_t)h, sizeof(double));
+    double *da = (double *)calloc(rows * (size_t)(F1 > 0 ? F1 : 1), sizeof(double));
+    if (!a || !y || !zt || !nh || !g || !dzt || !da) {
+        free(a); free(y); free(zt); free(nh); free(g); free(dzt); free(da);
+        return -1;
+    }
+
+    /* Forward recompute: pre-activations a, activations y (the GEMM-2 input) and the
+     * partials zt of every rank (Eq. 22 / 24). */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int m = 0; m < P; ++m)
+        for (int t = 0; t < T; ++t) {
+            const size_t row = (size_t)m * T + t;
+            const float *xr = x + row * kin;
+            double *ar = a + row * (size_t)(F1 > 0 ? F1 : 1), *yr = y + row * k2;
+            if (act == ORACLE_NONE) {
+                for (int j = 0; j < kin; ++j)
+                    yr[j] = (double)xr[j];
+            } else {
+                const float *W1m = W1 + (size_t)m * F1 * h;
+                for (int k = 0; k < F1; ++k) {
+                    double s = 0.0;
+                    for (int j = 0; j < h; ++j)
+                        s += (double)xr[j] * (double)W1m[(size_t)k * h + j];
+                    ar[k] = s;
+                }
+                for (int k = 0; k < fs; ++k)
+                    yr[k] = oracle_activation(act, ar[k], act == ORACLE_SWIGLU ? ar[fs + k] : 0.0);
+            }
+            const float *W2m = W2 + (size_t)m * h * k2;
+            for (int l = 0; l < h; ++l) {
+                double s = 0.0;
+                for (int k = 0; k < k2; ++k)
+                    s += yr[k] * (double)W2m[(size_t)l * k2 + k];
+                zt[row * h + l] = s;
+            }
+        }
+
+    /* Per token: forward reduce + residual + statistics, then the norm derivative of
+     * every rank (before any reduction), then the backward reduce. */
+#pragma omp parallel
+    {
+        double *r = (double *)malloc(sizeof(double) * (size_t)h);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            for (int m = 0; m < P; ++m) {
+                const size_t row = ((size_t)m * T + t) * h;
+                for (int l = 0; l < h; ++l) {
+                    double z;
+                    if (l < n_s) {
+                        z = 0.0;
+                        for (int q = 0; q < P; ++q)
+                            z += zt[((size_t)q * T + t) * h + l];
+                    } else {
+                        z = s_priv * zt[row + l];
+                    }
+                    r[l] = (double)resid[row + l] + z;
+                }
+                double mean = 0.0, inv;
+                if (norm == ORACLE_LAYERNORM) {
+                    for (int l = 0; l < h; ++l)
+                        mean += r[l];
+                    mean /= (double)h;
+                    double var = 0.0;
+                    for (int l = 0; l < h; ++l)
+                        var += (r[l] - mean) * (r[l] - mean);
+                    inv = 1.0 / sqrt(var / (double)h + eps);
+                } else {
+                    double ms = 0.0;
+                    for (int l = 0; l < h; ++l)
+                        ms += r[l] * r[l];
+                    inv = 1.0 / sqrt(ms / (double)h + eps);
+                }
+                /* nhat = (r - mean) inv; dnhat = dout * gamma;
+                 * LN:  dr = inv (dnhat - mean(dnhat) - nhat mean(dnhat nhat))
+                 * RMS: dr = inv (dnhat - nhat mean(dnhat nhat)) */
+                double s1 = 0.0, s2 = 0.0;
+                for (int l = 0; l < h; ++l) {
+                    const double n = (r[l] - mean) * inv;
+                    const double dn = (double)dout[row + l] * (double)gamma[l];
+                    nh[row + l] = n;
+                    s1 += dn;
+                    s2 += dn * n;
+                }
+                s1 /= (double)h;
+                s2 /= (double)h;
+                for (int l = 0; l < h; ++l) {
+                    const double dn = (double)dout[row + l] * (double)gamma[l];
+                    double dr = dn - nh[row + l] * s2;
+                    if (norm == ORACLE_LAYERNORM)
+                        dr -= s1;
+                    g[row + l] = inv * dr + (dres ? (double)dres[row + l] : 0.0);
+                }
+            }
+            /* The reduce after the norm derivative: shared channels of every rank's
+             * partial receive the sum over ranks of g; private ones their own g. */
+            for (int m = 0; m < P; ++m) {
+                const size_t row = ((size_t)m * T + t) * h;
+                for (int l = 0; l < h; ++l) {
+                    double d;
+                    if (l < n_s) {
+                        d = 0.0;
+                        for (int q = 0; q < P; ++q)
+                            d += g[((size_t)q * T + t) * h + l];
+                    } else {
+                        d = s_priv * g[row + l];
+                    }
+                    dzt[row + l] = d;
+                }
+            }
+        }
+        free(r);
+    }
+
+    /* Norm parameters: summed over ranks and tokens (Eq. 12, 29). */
+#pragma omp parallel for schedule(static)
+    for (int l = 0; l < h; ++l) {
+        double sg = 0.0, sb = 0.0;
+        for (size_t row = 0; row < rows; ++row) {
+            sg += (double)dout[row * h + l] * nh[row * h + l];
+            sb += (double)dout[row * h + l];
+        }
+        dgamma[l] = sg;
+        dbeta[l] = (norm == ORACLE_LAYERNORM) ? sb : 0.0;
+    }
+
+    /* Second GEMM (Eq. 22 second sum / Eq. 24): dW2 = dzt^T y, dy = dzt W2; then the
+     * nonlinearity and the first GEMM: da = dy * sigma'(a), dW1 = da^T x, dx = da W1. */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int m = 0; m < P; ++m)
+        for (int l = 0; l < h; ++l)
+            for (int k = 0; k < k2; ++k) {
+                double s = 0.0;
+                for (int t = 0; t < T; ++t) {
+                    const size_t row = (size_t)m * T + t;
+                    s += dzt[row * h + l] * y[row * k2 + k];
+                }
+                dW2[((size_t)m * h + l) * k2 + k] = s;
+            }
+#pragma omp parallel
+    {
+        double *dy = (double *)malloc(sizeof(double) * (size_t)(k2 > 0 ? k2 : 1));
+#pragma omp for collapse(2) schedule(static)
+        for (int m = 0; m < P; ++m)
+            for (int t = 0; t < T; ++t) {
+                const size_t row = (size_t)m * T + t;
+                const float *W2m = W2 + (size_t)m * h * k2;
+                for (int k = 0; k < k2; ++k) {
+                    double s = 0.0;
+                    for (int l = 0; l < h; ++l)
+                        s += dzt[row * h + l] * (double)W2m[(size_t)l * k2 + k];
+                    dy[k] = s;
+                }
+                if (act == ORACLE_NONE) {
+                    for (int j = 0; j < kin; ++j)
+                        dx[row * kin + j] = dy[j];
+                    continue;
+                }
+                double *ar = a + row * F1, *dar = da + row * F1;
+                for (int k = 0; k < fs; ++k) {
+                    if (act == ORACLE_SWIGLU) {
+                        /* y = silu(g) u: dg = dy u silu'(g), du = dy silu(g),
+                         * silu'(g) = sig(g) (1 + g (1 - sig(g))) */
+                        const double gg = ar[k], uu = ar[fs + k];
+                        const double sg = 1.0 / (1.0 + exp(-gg));
+                        dar[k] = dy[k] * uu * sg * (1.0 + gg * (1.0 - sg));
+                        dar[fs + k] = dy[k] * gg * sg;
+                    } else {
+                        dar[k] = dy[k] * act_grad(act, ar[k]);
+                    }
+                }
+                const float *W1m = W1 + (size_t)m * F1 * h;
+                for (int j = 0; j < h; ++j) {
+                    double s = 0.0;
+                    for (int k = 0; k < F1; ++k)
+                        s += dar[k] * (double)W1m[(size_t)k * h + j];
+                    dx[row * kin + j] = s + (resid_is_x ? g[row * h + j] : 0.0);
+                }
+            }
+        free(dy);
+    }
+    if (act != ORACLE_NONE) {
+#pragma omp parallel for collapse(2) schedule(static)
+        for (int m = 0; m < P; ++m)
+            for (int k = 0; k < F1; ++k)
+                for (int j = 0; j < h; ++j) {
+                    double s = 0.0;
+                    for (int t = 0; t < T; ++t) {
+                        const size_t row = (size_t)m * T + t;
+                        s += da[row * F1 + k] * (double)x[row * kin + j];
+                    }
+                    dW1[((size_t)m * F1 + k) * h + j] = s;
+                }
+    }
+    if (dresid)
+        memcpy(dresid, g, sizeof(double) * rows * (size_t)h);
+    free(a); free(y); free(zt); free(nh); free(g); free(dzt); free(da);
     return 0;
 }
