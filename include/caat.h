@@ -162,6 +162,63 @@ int caat_partial_sync_norm(caat_handle handle, int T, const void *partials, cons
                            const void *gamma, const void *beta, void *out, void *out_resid,
                            void *stream);
 
+/* ------------------------------------------------------------------------------
+ * Backward of the sublayer: §4 "Forward-backward mismatch" (Eq. 9-13) and App. B
+ * (Eq. 25-30).  The loss reaches the sublayer through out (gradient dout) and through
+ * the residual stream out_resid = r (gradient dres, from whatever later adds r in).
+ * Per rank m and token:
+ *   g_m = dres_m + (dNorm/dr at r_m)^T dout_m      (the norm derivative comes first)
+ *   dZt_m[l] = sum over ranks q of g_q[l]  for l < n_s   (the reduce after the norm
+ *   dZt_m[l] = s_priv * g_m[l]             for l >= n_s   derivative, Eq. 26-28)
+ *   dresid_m = g_m
+ *   dgamma = sum over ranks and tokens of dout * nhat, dbeta = sum of dout (LayerNorm;
+ *   zero for RMSNorm): the norm parameters reduced over ranks (Eq. 12, 29).
+ * Then the chain rule through the row-parallel GEMM, the activation and the
+ * column-parallel GEMM (Eq. 22 / 24).  The sum over ranks and every contraction
+ * accumulate in fp32 (§4: 32-bit accumulation of the reduced gradients); dgamma and
+ * dbeta are fp32 outputs, every other tensor is in the handle's dtype.
+ * Statistics are recomputed from out_resid as stored by the forward.
+ * ------------------------------------------------------------------------------ */
+
+/* Bytes of device workspace caat_backward needs for T tokens (0 for a NULL handle or
+ * T < 1).  caat_partial_sync_norm_backward needs 8 * h * min(T, 1024) + 512 bytes of it. */
+size_t caat_backward_workspace_bytes(caat_handle handle, int T);
+
+typedef struct {
+    int T;
+    const void *in;         /* the forward's input: x [P][T][h], or H [P][T][h/P] */
+    const void *W1;         /* [P][F1][h]; ignored for CAAT_NONE */
+    const void *W2;         /* [P][h][k2] */
+    const void *gamma;      /* [h] */
+    const void *out_resid;  /* r [P][T][h] from the forward (required) */
+    const void *dout;       /* dL/d out [P][T][h] */
+    const void *dres;       /* dL/d out_resid [P][T][h]; NULL means zero */
+    void *din;              /* dL/d in [P][T][h] or [P][T][h/P] */
+    void *dresid;           /* dL/d resid [P][T][h]; NULL (MLP only): the forward's
+                               residual was `in`, and its gradient is added into din */
+    void *dW1;              /* [P][F1][h]; ignored for CAAT_NONE */
+    void *dW2;              /* [P][h][k2] */
+    float *dgamma;          /* [h], fp32 */
+    float *dbeta;           /* [h], fp32, or NULL */
+    void *workspace;        /* caller-owned device memory, 16-byte aligned */
+    size_t workspace_bytes; /* >= caat_backward_workspace_bytes(T) */
+    void *stream;
+} caat_bwd_args;
+
+/* The whole backward of one sublayer for every rank.  Returns CAAT_EWORKSPACE for a
+ * missing or short workspace, CAAT_EINVAL for bad pointers (a NULL dresid with
+ * CAAT_NONE included).  The workspace is overwritten. */
+int caat_backward(caat_handle handle, const caat_bwd_args *args);
+
+/* The norm derivative and the reduce over ranks alone (the first step of
+ * caat_backward): out_resid, dout [P][T][h], dres (NULL: zero) -> dpartials = dZt
+ * [P][T][h], dresid [P][T][h] (NULL: not stored), dgamma [h] and dbeta [h] (NULL: not
+ * stored), both fp32. */
+int caat_partial_sync_norm_backward(caat_handle handle, int T, const void *out_resid,
+                                    const void *dout, const void *dres, const void *gamma,
+                                    void *dpartials, void *dresid, float *dgamma, float *dbeta,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a caat_status. */
 const char *caat_error_string(int code);
 

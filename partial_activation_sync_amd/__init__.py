@@ -42,6 +42,16 @@ class caat_args(ctypes.Structure):
                 ("out_resid", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
 
 
+class caat_bwd_args(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("in_", ctypes.c_void_p), ("W1", ctypes.c_void_p),
+                ("W2", ctypes.c_void_p), ("gamma", ctypes.c_void_p),
+                ("out_resid", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+                ("dres", ctypes.c_void_p), ("din", ctypes.c_void_p), ("dresid", ctypes.c_void_p),
+                ("dW1", ctypes.c_void_p), ("dW2", ctypes.c_void_p), ("dgamma", ctypes.c_void_p),
+                ("dbeta", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+
+
 def lib():
     """The loaded libcaat.so.  torch is imported first so that the library binds to the
     HIP runtime torch already uses (one runtime, shared streams)."""
@@ -67,12 +77,17 @@ def lib():
         L.caat_partial_sync_norm.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp]
         L.caat_row_gemm_reduce.argtypes = [vp, i, vp, vp, vp, vp, vp]
         L.caat_sync_norm.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.caat_backward_workspace_bytes.argtypes = [vp, i]
+        L.caat_backward_workspace_bytes.restype = sz
+        L.caat_backward.argtypes = [vp, ctypes.POINTER(caat_bwd_args)]
+        L.caat_partial_sync_norm_backward.argtypes = [vp, i] + [vp] * 9 + [sz, vp]
         L.caat_error_string.argtypes = [i]
         L.caat_error_string.restype = ctypes.c_char_p
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
                      "caat_forward_ex", "caat_column_gemm_act", "caat_row_gemm",
-                     "caat_partial_sync_norm", "caat_row_gemm_reduce", "caat_sync_norm"):
+                     "caat_partial_sync_norm", "caat_row_gemm_reduce", "caat_sync_norm",
+                     "caat_backward", "caat_partial_sync_norm_backward"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -187,6 +202,28 @@ def caat_sync_norm(handle, T, S, partials, resid, gamma, beta, out, out_resid, s
                                        _stream(stream)), "caat_sync_norm")
 
 
+def caat_backward_workspace_bytes(handle, T) -> int:
+    return int(lib().caat_backward_workspace_bytes(handle, int(T)))
+
+
+def caat_backward(handle, T, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgamma,
+                  workspace, dW1=None, dres=None, dresid=None, dbeta=None, stream=None):
+    a = caat_bwd_args(int(T), _ptr(inp), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(out_resid),
+                      _ptr(dout), _ptr(dres), _ptr(din), _ptr(dresid), _ptr(dW1), _ptr(dW2),
+                      _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(stream))
+    return _check(lib().caat_backward(handle, ctypes.byref(a)), "caat_backward")
+
+
+def caat_partial_sync_norm_backward(handle, T, out_resid, dout, dres, gamma, dpartials, dresid,
+                                    dgamma, dbeta, workspace, stream=None):
+    return _check(lib().caat_partial_sync_norm_backward(
+        handle, int(T), _ptr(out_resid), _ptr(dout), _ptr(dres), _ptr(gamma), _ptr(dpartials),
+        _ptr(dresid), _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)),
+        "caat_partial_sync_norm_backward")
+
+
 class Sublayer:
     """One sublayer handle plus a torch-allocated workspace; checks tensor shapes and
     dtypes, then calls the C entry points (no arithmetic here)."""
@@ -249,3 +286,32 @@ class Sublayer:
         self.workspace(T, inp.device)
         return caat_forward_ex(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
                                out, resid=resid, beta=beta, out_resid=out_resid, stream=stream)
+
+    def backward(self, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgamma, dW1=None,
+                 dres=None, dresid=None, dbeta=None, stream=None):
+        """Gradients of one sublayer (shape and dtype checks, then caat_backward)."""
+        import torch
+        P, h = self.P, self.h
+        T = inp.shape[1]
+        self._expect(inp, (P, T, self.kin), "in")
+        self._expect(din, (P, T, self.kin), "din")
+        k2 = self.f_s if self.act != NONE else self.kin
+        self._expect(W2, (P, h, k2), "W2")
+        self._expect(dW2, (P, h, k2), "dW2")
+        if self.act != NONE:
+            F1 = 2 * self.f_s if self.act == SWIGLU else self.f_s
+            self._expect(W1, (P, F1, h), "W1")
+            self._expect(dW1, (P, F1, h), "dW1")
+        for name, t in (("out_resid", out_resid), ("dout", dout), ("dres", dres),
+                        ("dresid", dresid)):
+            self._expect(t, (P, T, h), name)
+        self._expect(gamma, (h,), "gamma")
+        for name, t in (("dgamma", dgamma), ("dbeta", dbeta)):
+            if t is not None and (tuple(t.shape) != (h,) or t.dtype != torch.float32):
+                raise ValueError(f"{name}: expected float32 [{h}]")
+        nbytes = caat_backward_workspace_bytes(self.handle, T)
+        if getattr(self, "_bws", None) is None or self._bws.numel() < nbytes:
+            self._bws = torch.empty(nbytes, dtype=torch.uint8, device=inp.device)
+        return caat_backward(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
+                             out_resid, dout, din, dW2, dgamma, self._bws, dW1=dW1, dres=dres,
+                             dresid=dresid, dbeta=dbeta, stream=stream)

@@ -348,6 +348,178 @@ CAAT_API int caat_partial_sync_norm(caat_handle c, int T, const void *partials, 
                      reinterpret_cast<hipStream_t>(stream));
 }
 
+// ---------------------------------------------------------------------------------
+// Backward (§4 "Forward-backward mismatch", Eq. 10-13; App. B, Eq. 26-30).
+
+namespace {
+
+size_t round8(size_t n) { return (n + 7) & ~(size_t)7; }
+
+// Workspace of the backward, in this order (each part 256-byte aligned).  Tp = T
+// rounded up to a multiple of 8: the transposed activations are the operands of the
+// weight-gradient GEMMs, whose contraction runs over tokens.
+struct BwdLayout {
+    size_t dzt, dres, gpart, bpart, W2T, dY, dztT, YT, A, da, Y, W1T, xT, daT, total;
+};
+
+BwdLayout bwd_layout(const caat_ctx *c, int T) {
+    BwdLayout L{};
+    const size_t E = esize(c), P = c->P, h = c->h, k2 = c->k2, F1 = c->F1, fs = c->fs;
+    const size_t Tp = round8(T), NB = caat::psync_bwd_blocks(T);
+    size_t off = 0;
+    auto take = [&](size_t n) { const size_t o = off; off += align256(n); return o; };
+    L.dzt = take(P * T * h * E);
+    L.dres = take(P * T * h * E);
+    L.gpart = take(NB * h * 4);
+    L.bpart = take(NB * h * 4);
+    L.W2T = take(P * k2 * h * E);
+    L.dY = take(P * T * k2 * E);
+    L.dztT = take(P * h * Tp * E);
+    L.YT = take(P * k2 * Tp * E);
+    if (c->act != CAAT_NONE) {
+        L.A = take(P * T * F1 * E);
+        L.da = take(P * T * F1 * E);
+        L.Y = take(P * T * fs * E);
+        L.W1T = take(P * h * F1 * E);
+        L.xT = take(P * h * Tp * E);
+        L.daT = take(P * F1 * Tp * E);
+    }
+    L.total = off;
+    return L;
+}
+
+// B3's share of the workspace (the per-workgroup norm-parameter partials).
+size_t bwd_norm_bytes(const caat_ctx *c, int T) {
+    return 2 * align256((size_t)caat::psync_bwd_blocks(T) * c->h * 4);
+}
+
+bool t_ok_bwd(const caat_ctx *c, int T) {
+    if (!t_ok(c, T)) return false;
+    const uint64_t widest = (uint64_t)(c->h > c->F1 ? c->h : c->F1);
+    return (uint64_t)round8(T) * widest * esize(c) < 0x80000000ull;
+}
+
+// One plain NT GEMM: out[m][t][n] = sum_k W[m][n][k] X[m][t][k], row stride ldo = N.
+caat::GemmArgs plain_args(const caat_ctx *c, int rows, int N, int K, const void *W,
+                          const void *X, void *out) {
+    caat::GemmArgs g{};
+    g.P = c->P; g.N = N; g.T = rows; g.K = K;
+    g.W = W; g.w_stride = (size_t)N * K;
+    g.X = X; g.x_stride = (size_t)rows * K;
+    g.out = out; g.o_stride = (size_t)rows * N; g.ldo = N;
+    g.up_off = 0;
+    g.epi = caat::EPI_STORE;
+    g.kseg = 1;
+    return g;
+}
+
+int run_psync_bwd(const caat_ctx *c, int T, const void *r, const void *dout, const void *dres,
+                  const void *gamma, void *dzt, void *dresid, float *dgamma, float *dbeta,
+                  char *ws, hipStream_t s) {
+    caat::PsyncBwdArgs b{};
+    b.P = c->P; b.T = T; b.h = c->h; b.n_s = c->n_s; b.norm = c->norm;
+    b.s_priv = c->s_priv; b.eps = c->eps;
+    b.r = r; b.dout = dout; b.dres = dres; b.gamma = gamma;
+    b.dzt = dzt; b.dresid = dresid;
+    b.nblk = caat::psync_bwd_blocks(T);
+    b.gpart = reinterpret_cast<float *>(ws);
+    b.bpart = reinterpret_cast<float *>(ws + bwd_norm_bytes(c, T) / 2);
+    if (caat::psync_norm_bwd(b, c->dtype, s) != hipSuccess) return CAAT_EDEVICE;
+    if (caat::colsum_f32(b.gpart, b.nblk, c->h, dgamma, s) != hipSuccess) return CAAT_EDEVICE;
+    if (dbeta != nullptr) {
+        // RMSNorm has no beta: its gradient is written as zero (a sum over no rows).
+        const int rows = (c->norm == CAAT_LAYERNORM) ? b.nblk : 0;
+        if (caat::colsum_f32(b.bpart, rows, c->h, dbeta, s) != hipSuccess) return CAAT_EDEVICE;
+    }
+    return CAAT_OK;
+}
+
+}  // namespace
+
+CAAT_API size_t caat_backward_workspace_bytes(caat_handle handle, int T) {
+    if (handle == nullptr || T < 1) return 0;
+    return bwd_layout(handle, T).total;
+}
+
+CAAT_API int caat_partial_sync_norm_backward(caat_handle c, int T, const void *out_resid,
+                                             const void *dout, const void *dres,
+                                             const void *gamma, void *dpartials, void *dresid,
+                                             float *dgamma, float *dbeta, void *workspace,
+                                             size_t workspace_bytes, void *stream) {
+    if (c == nullptr || T < 1) return CAAT_EINVAL;
+    if (!aligned16(out_resid) || !aligned16(dout) || !aligned16(gamma) || !aligned16(dpartials) ||
+        !aligned16(dgamma))
+        return CAAT_EINVAL;
+    if (!aligned16_or_null(dres) || !aligned16_or_null(dresid) || !aligned16_or_null(dbeta))
+        return CAAT_EINVAL;
+    if (!t_ok(c, T)) return CAAT_EUNSUPPORTED;
+    if (!aligned16(workspace) || workspace_bytes < bwd_norm_bytes(c, T)) return CAAT_EWORKSPACE;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    return run_psync_bwd(c, T, out_resid, dout, dres, gamma, dpartials, dresid, dgamma, dbeta,
+                         reinterpret_cast<char *>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
+    if (c == nullptr || a == nullptr) return CAAT_EINVAL;
+    const int T = a->T;
+    if (T < 1) return CAAT_EINVAL;
+    const bool mlp = c->act != CAAT_NONE;
+    if (!aligned16(a->in) || !aligned16(a->W2) || !aligned16(a->gamma) ||
+        !aligned16(a->out_resid) || !aligned16(a->dout) || !aligned16(a->din) ||
+        !aligned16(a->dW2) || !aligned16(a->dgamma))
+        return CAAT_EINVAL;
+    if (mlp && (!aligned16(a->W1) || !aligned16(a->dW1))) return CAAT_EINVAL;
+    if (!aligned16_or_null(a->dres) || !aligned16_or_null(a->dresid) ||
+        !aligned16_or_null(a->dbeta))
+        return CAAT_EINVAL;
+    if (a->dresid == nullptr && !mlp) return CAAT_EINVAL;  // H is not a residual
+    if (!t_ok_bwd(c, T)) return CAAT_EUNSUPPORTED;
+    const BwdLayout L = bwd_layout(c, T);
+    if (!aligned16(a->workspace) || a->workspace_bytes < L.total) return CAAT_EWORKSPACE;
+    int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(a->stream);
+    char *ws = reinterpret_cast<char *>(a->workspace);
+    const int P = c->P, h = c->h, k2 = c->k2, F1 = c->F1, fs = c->fs, Tp = (int)round8(T);
+    void *dzt = ws + L.dzt;
+    void *dresid = a->dresid ? a->dresid : ws + L.dres;
+#define CAAT_TRY(call) do { const int rc_ = (call); if (rc_ != CAAT_OK) return rc_; } while (0)
+#define CAAT_HIP(call) do { if ((call) != hipSuccess) return CAAT_EDEVICE; } while (0)
+    // Norm derivative per rank, then the reduce over ranks of the shared channels.
+    CAAT_TRY(run_psync_bwd(c, T, a->out_resid, a->dout, a->dres, a->gamma, dzt, dresid,
+                           a->dgamma, a->dbeta, ws + L.gpart, s));
+    // Second GEMM: dY = dZt W2 (per rank), through W2^T [k2][h].
+    CAAT_HIP(caat::transpose(a->W2, ws + L.W2T, P, h, k2, h, c->dtype, s));
+    void *dY = mlp ? ws + L.dY : a->din;   // out-projection: dY is dH
+    CAAT_TRY(run_gemm(c, plain_args(c, T, k2, h, ws + L.W2T, dzt, dY), s));
+    const void *y_in = a->in;              // the second GEMM's input (H for the out-projection)
+    if (mlp) {
+        // Recompute the pre-activation, then da = dY * sigma'(a) and Y = sigma(a).
+        CAAT_TRY(run_gemm(c, plain_args(c, T, F1, h, a->W1, a->in, ws + L.A), s));
+        CAAT_HIP(caat::act_backward(c->act, c->dtype, (size_t)P * T, fs, ws + L.A, dY, ws + L.da,
+                                    ws + L.Y, s));
+        y_in = ws + L.Y;
+        // First GEMM: dx = da W1, through W1^T [h][F1].
+        CAAT_HIP(caat::transpose(a->W1, ws + L.W1T, P, F1, h, F1, c->dtype, s));
+        CAAT_TRY(run_gemm(c, plain_args(c, T, h, F1, ws + L.W1T, ws + L.da, a->din), s));
+        if (a->dresid == nullptr)
+            CAAT_HIP(caat::add_inplace(a->din, dresid, (size_t)P * T * h, c->dtype, s));
+        // dW1 = da^T x: contraction over tokens, both operands transposed.
+        CAAT_HIP(caat::transpose(ws + L.da, ws + L.daT, P, T, F1, Tp, c->dtype, s));
+        CAAT_HIP(caat::transpose(a->in, ws + L.xT, P, T, h, Tp, c->dtype, s));
+        CAAT_TRY(run_gemm(c, plain_args(c, F1, h, Tp, ws + L.xT, ws + L.daT, a->dW1), s));
+    }
+    // dW2 = dZt^T Y (or dZt^T H): contraction over tokens.
+    CAAT_HIP(caat::transpose(y_in, ws + L.YT, P, T, k2, Tp, c->dtype, s));
+    CAAT_HIP(caat::transpose(dzt, ws + L.dztT, P, T, h, Tp, c->dtype, s));
+    CAAT_TRY(run_gemm(c, plain_args(c, h, k2, Tp, ws + L.YT, ws + L.dztT, a->dW2), s));
+#undef CAAT_TRY
+#undef CAAT_HIP
+    return CAAT_OK;
+}
+
 CAAT_API const char *caat_error_string(int code) {
     switch (code) {
     case CAAT_OK: return "success";

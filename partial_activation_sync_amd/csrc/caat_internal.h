@@ -69,3 +69,40 @@ struct PsyncArgs {
 hipError_t psync_norm(const PsyncArgs &a, int dtype, hipStream_t s);
 
 }  // namespace caat
+
+// ---------------------------------------------------------------------------------
+// Backward of the sublayer.
+namespace caat {
+
+// B3: the norm derivative of every rank, then the reduce over ranks of the shared
+// channels of the result (the placement after the norm derivative), per token; the
+// norm parameters' gradients are accumulated per workgroup into gpart / bpart
+// [nblk][h] (fp32) and summed by colsum_f32.
+struct PsyncBwdArgs {
+    int P, T, h, n_s, norm;
+    float s_priv, eps;
+    const void *r;       // [P][T][h] forward out_resid (r = R + Z)
+    const void *dout;    // [P][T][h]
+    const void *dres;    // [P][T][h] or NULL (zero)
+    const void *gamma;   // [h]
+    void *dzt;           // [P][T][h] gradient of the partials
+    void *dresid;        // [P][T][h] or NULL
+    float *gpart, *bpart;
+    int nblk;
+};
+int psync_bwd_blocks(int T);
+hipError_t psync_norm_bwd(const PsyncBwdArgs &a, int dtype, hipStream_t s);
+// out[l] = sum over r < rows (ascending) of part[r][l], fp32.
+hipError_t colsum_f32(const float *part, int rows, int h, float *out, hipStream_t s);
+// dst[b][c][r] = src[b][r][c] for r < R, 0 for R <= r < Rp (Rp % 8 == 0, Rp >= R).
+hipError_t transpose(const void *src, void *dst, int B, int R, int C, int Rp, int dtype,
+                     hipStream_t s);
+// Activation backward over rows of the pre-activation A [rows][F1]:
+//   da = dY * sigma'(A) ([rows][F1]; SwiGLU: gate and up halves), Y = sigma(A)
+//   ([rows][fs]).
+hipError_t act_backward(int act, int dtype, size_t rows, int fs, const void *A, const void *dY,
+                        void *da, void *Y, hipStream_t s);
+// dst[i] += src[i], n % 8 == 0.
+hipError_t add_inplace(void *dst, const void *src, size_t n, int dtype, hipStream_t s);
+
+}  // namespace caat

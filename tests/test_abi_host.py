@@ -149,6 +149,52 @@ def test_fused_steps_check_before_any_launch():
     caat.caat_destroy(none)
 
 
+def test_backward_workspace_and_checks_before_any_launch():
+    L = caat.lib()
+    fake = 0x10000
+    P, h, ffn, T = 2, 256, 1024, 37
+    hd = caat.caat_create(h, ffn, P, 0.5, caat.LAYERNORM, caat.SWIGLU, caat.BF16)
+    fs, F1, Tp, NB = ffn // P, 2 * ffn // P, 40, T
+    a256 = lambda n: (n + 255) // 256 * 256
+    parts = [P * T * h * 2, P * T * h * 2, NB * h * 4, NB * h * 4, P * fs * h * 2,
+             P * T * fs * 2, P * h * Tp * 2, P * fs * Tp * 2,
+             P * T * F1 * 2, P * T * F1 * 2, P * T * fs * 2, P * h * F1 * 2, P * h * Tp * 2,
+             P * F1 * Tp * 2]
+    assert caat.caat_backward_workspace_bytes(hd, T) == sum(a256(n) for n in parts)
+    assert caat.caat_backward_workspace_bytes(hd, 0) == 0
+    assert caat.caat_backward_workspace_bytes(None, T) == 0
+    need = caat.caat_backward_workspace_bytes(hd, T)
+    args = lambda **kw: caat.caat_bwd_args(*[kw.get(k, d) for k, d in (
+        ("T", T), ("in_", fake), ("W1", fake), ("W2", fake), ("gamma", fake),
+        ("out_resid", fake), ("dout", fake), ("dres", None), ("din", fake), ("dresid", None),
+        ("dW1", fake), ("dW2", fake), ("dgamma", fake), ("dbeta", None), ("workspace", fake),
+        ("workspace_bytes", need), ("stream", None))])
+    assert L.caat_backward(None, ctypes.byref(args())) == caat.EINVAL
+    assert L.caat_backward(hd, None) == caat.EINVAL
+    assert L.caat_backward(hd, ctypes.byref(args(T=0))) == caat.EINVAL
+    assert L.caat_backward(hd, ctypes.byref(args(dout=None))) == caat.EINVAL
+    assert L.caat_backward(hd, ctypes.byref(args(out_resid=None))) == caat.EINVAL
+    assert L.caat_backward(hd, ctypes.byref(args(dW1=None))) == caat.EINVAL
+    assert L.caat_backward(hd, ctypes.byref(args(dgamma=fake + 4))) == caat.EINVAL
+    assert L.caat_backward(hd, ctypes.byref(args(workspace_bytes=need - 1))) == caat.EWORKSPACE
+    assert L.caat_backward(hd, ctypes.byref(args(workspace=None))) == caat.EWORKSPACE
+    small = 2 * a256(NB * h * 4)
+    assert L.caat_partial_sync_norm_backward(hd, T, fake, fake, None, fake, fake, None, fake,
+                                             None, fake, small - 1, None) == caat.EWORKSPACE
+    assert L.caat_partial_sync_norm_backward(hd, T, fake, None, None, fake, fake, None, fake,
+                                             None, fake, small, None) == caat.EINVAL
+    caat.caat_destroy(hd)
+    att = caat.caat_create(h, 0, P, 0.5, caat.RMSNORM, caat.NONE, caat.BF16)
+    need = caat.caat_backward_workspace_bytes(att, T)
+    k2 = h // P
+    assert need == sum(a256(n) for n in [P * T * h * 2, P * T * h * 2, NB * h * 4, NB * h * 4,
+                                        P * k2 * h * 2, P * T * k2 * 2, P * h * Tp * 2,
+                                        P * k2 * Tp * 2])
+    # the out-projection's residual is not its input: dresid is required
+    assert L.caat_backward(att, ctypes.byref(args(W1=None, dW1=None, workspace_bytes=need))) == caat.EINVAL
+    caat.caat_destroy(att)
+
+
 def test_error_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert caat.caat_error_string(code) != "unknown status"

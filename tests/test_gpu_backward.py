@@ -1,0 +1,162 @@
+"""GPU parity of the sublayer backward: libcaat (HIP, gfx950) against the fp64 oracle.
+
+"Tensor-Parallelism with Partially Synchronized Activations", §4 "Forward-backward
+mismatch" (Eq. 10-13) and App. B (Eq. 26-30): the norm derivative per rank, then the
+reduce over ranks of the shared channels, the norm parameters' gradients summed over
+ranks, then the two GEMMs and the activation.  The GPU runs its own forward first
+(the backward reads the forward's out_resid); the oracle recomputes everything from
+the same seeded inputs in fp64.  Bar per gradient tensor: max |gpu - oracle| /
+max |oracle| <= 1e-4 (fp32 storage), <= 2e-2 (bf16 storage).  The mask of the
+backward reduce is checked bit-exactly on integer-coded gradients.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import partial_activation_sync_amd as caat
+from partial_activation_sync_amd import synth
+from tests.oracle_ref import ACT, NORM, TOL, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _inputs(P, T, h, ffn, act, dtype, resid_given, dres_given, seed=synth.BASE_SEED):
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    none = act == "none"
+    fs = 0 if none else ffn // P
+    kin = h // P if none else h
+    F1 = 2 * fs if act == "swiglu" else fs
+    k2 = kin if none else fs
+    d = {
+        "x": synth.normal((P, T, kin), synth.CTX if none else synth.X, dtype=dt, seed=seed),
+        "W1": None if none else synth.normal((P, F1, h), synth.W1, std=0.02, dtype=dt, seed=seed),
+        "W2": synth.normal((P, h, k2), synth.WO if none else synth.W2, std=0.02, dtype=dt,
+                           seed=seed),
+        "gamma": synth.normal((h,), synth.GAMMA, std=0.1, mean=1.0, dtype=dt, seed=seed),
+        "beta": synth.normal((h,), synth.BETA, std=0.1, dtype=dt, seed=seed),
+        "resid": synth.normal((P, T, h), synth.X0, dtype=dt, seed=seed) if resid_given else None,
+        "dout": synth.normal((P, T, h), synth.DOUT, dtype=dt, seed=seed),
+        "dres": synth.normal((P, T, h), synth.DRES, dtype=dt, seed=seed) if dres_given else None,
+    }
+    return d
+
+
+def _run(P, T, h, ffn, act, norm, p, dtype, s_priv=1.0, resid_given=True, dres_given=True):
+    _say(f"[case] backward P={P} T={T} h={h} ffn={ffn} act={act} norm={norm} p={p} "
+         f"{dtype} s={s_priv:.3f} resid={resid_given} dres={dres_given}")
+    d = _inputs(P, T, h, ffn, act, dtype, resid_given, dres_given)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+    sub = caat.Sublayer(h, ffn, P, p, norm=norm, act=act, dtype=dtype, eps=1e-5, s_priv=s_priv)
+    dt = sub.torch_dtype
+    out = torch.empty((P, T, h), dtype=dt, device="cuda")
+    out_resid = torch.empty_like(out)
+    sub.forward(dev["x"], dev["W1"], dev["W2"], dev["gamma"], out, resid=dev["resid"],
+                beta=dev["beta"], out_resid=out_resid)
+    g = {
+        "dx": torch.full_like(dev["x"], float("nan")),
+        "dresid": torch.full((P, T, h), float("nan"), dtype=dt, device="cuda") if resid_given else None,
+        "dW1": torch.full_like(dev["W1"], float("nan")) if act != "none" else None,
+        "dW2": torch.full_like(dev["W2"], float("nan")),
+        "dgamma": torch.full((h,), float("nan"), dtype=torch.float32, device="cuda"),
+        "dbeta": torch.full((h,), float("nan"), dtype=torch.float32, device="cuda"),
+    }
+    sub.backward(dev["x"], dev["W1"], dev["W2"], dev["gamma"], out_resid, dev["dout"], g["dx"],
+                 g["dW2"], g["dgamma"], dW1=g["dW1"], dres=dev["dres"], dresid=g["dresid"],
+                 dbeta=g["dbeta"])
+    torch.cuda.synchronize()
+    ref = oracle.sublayer_backward(
+        d["x"], d["W1"], d["W2"], d["gamma"], d["dout"],
+        act=oracle.NONE if act == "none" else ACT[act], norm=NORM[norm],
+        n_s=sub.n_s, resid=d["resid"], dres=d["dres"], s_priv=s_priv, eps=1e-5)
+    errs = {}
+    for k, v in g.items():
+        if v is None:
+            continue
+        assert torch.isfinite(v.float()).all(), f"{k} has non-finite values"
+        if k == "dbeta" and norm == "rmsnorm":
+            assert torch.all(v == 0), "dbeta must be zero for RMSNorm"
+            continue
+        errs[k] = rel_err(v, ref[k])
+    _say("   errors:", {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= TOL[dtype], (k, e)
+    return errs
+
+
+def test_backward_tiny_fp32():
+    _run(2, 77, 256, 1024, "gelu", "layernorm", 0.5, "f32")
+
+
+@pytest.mark.parametrize("act,norm,p,s_priv", [
+    ("swiglu", "rmsnorm", 0.3, 2.0),        # n_s = 153: boundary inside a chunk
+    ("gelu", "layernorm", 0.5, 1.0),
+    ("gelu_tanh", "layernorm", 1.0, 1.0),
+    ("swiglu", "layernorm", 0.0, 2.0),
+])
+def test_backward_mlp_bf16(act, norm, p, s_priv):
+    _run(4, 130, 512, 4 * 264, act, norm, p, "bf16", s_priv=s_priv)
+
+
+def test_backward_mlp_residual_is_input():
+    """resid = x: the residual gradient is added into din (dresid not given)."""
+    _run(4, 96, 512, 4 * 264, "swiglu", "rmsnorm", 0.5, "bf16", resid_given=False,
+         dres_given=False)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_out_projection(dtype):
+    _run(4, 100, 512, 0, "none", "layernorm", 0.37, dtype, s_priv=2.0)
+
+
+def test_backward_single_rank_and_small_batch():
+    _run(1, 9, 256, 512, "gelu", "rmsnorm", 0.5, "bf16")
+    _run(8, 3, 256, 8 * 64, "swiglu", "layernorm", 0.25, "bf16")
+
+
+def test_backward_7b_dims():
+    """The 7B shapes (h = 4096, SwiGLU ffn = 11008, P = 8) at a short batch."""
+    _run(8, 72, 4096, 11008, "swiglu", "rmsnorm", 0.5, "bf16")
+
+
+@pytest.mark.parametrize("n_s_p", [0.0, 1.0 / 256, 63 / 256, 0.25, 65 / 256, 179 / 256,
+                                   255 / 256, 1.0])
+def test_backward_reduce_mask_bit_exact(n_s_p):
+    """Integer-coded gradients: dout = 0, dres_m = 2^m.  Then g_m = 2^m exactly, the
+    shared channels of every rank's dZt are 2^P - 1 and the private ones s_priv 2^m."""
+    P, T, h = 3, 5, 256
+    sub = caat.Sublayer(h, 8 * P, P, n_s_p, norm="layernorm", act="gelu", dtype="f32",
+                        s_priv=2.0)
+    n_s = sub.n_s
+    dres = torch.stack([torch.full((T, h), float(2 ** m)) for m in range(P)]).cuda()
+    r = synth.normal((P, T, h), synth.RESID).cuda()
+    dout = torch.zeros((P, T, h), device="cuda")
+    gamma = torch.ones(h, device="cuda")
+    dz = torch.full((P, T, h), float("nan"), device="cuda")
+    dres_out = torch.full_like(dz, float("nan"))
+    dg = torch.full((h,), float("nan"), device="cuda")
+    db = torch.full((h,), float("nan"), device="cuda")
+    ws = torch.empty(caat.caat_backward_workspace_bytes(sub.handle, T), dtype=torch.uint8,
+                     device="cuda")
+    caat.caat_partial_sync_norm_backward(sub.handle, T, r, dout, dres, gamma, dz, dres_out, dg,
+                                         db, ws)
+    torch.cuda.synchronize()
+    want = torch.empty((P, T, h))
+    for m in range(P):
+        want[m, :, :n_s] = float(2 ** P - 1)
+        want[m, :, n_s:] = 2.0 * 2 ** m
+    assert torch.equal(dz.cpu(), want)
+    assert torch.equal(dres_out.cpu(), dres.cpu())
+    assert torch.equal(dg.cpu(), torch.zeros(h)) and torch.equal(db.cpu(), torch.zeros(h))
+
+
+def test_backward_deterministic():
+    a = _run(4, 130, 512, 4 * 264, "swiglu", "rmsnorm", 0.5, "bf16")
+    b = _run(4, 130, 512, 4 * 264, "swiglu", "rmsnorm", 0.5, "bf16")
+    assert a == b
