@@ -1,6 +1,7 @@
 """Benchmark: tokens/s of the CAAT partial-sync sublayer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T] [--p P]
+                    [--pass forward|backward] [--graph]
 
 A step is one pass of the whole path over one batch: for a pair workload the
 attention out-projection sublayer (row-parallel GEMM K2, then the fused partial
@@ -10,6 +11,11 @@ in HBM before the timed region starts.  Each kernel is enqueued through its own 
 entry point with an event between consecutive kernels on the stream the library
 launches on, which yields the step time and every kernel's average duration from the
 same timed steps.
+
+With --pass backward a step is the backward of the whole path instead (the MLP
+sublayer's backward, then the out-projection sublayer's), through caat_backward; the
+library records the caller's events after each of its steps, so every kernel's
+average duration again comes from the timed steps.
 
 Prints ONE JSON line on stdout (details on stderr).
 """
@@ -24,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tokens/sec per CAAT sublayer fwd (1 GPU, P emulated); % MFMA or HBM roofline"
+METRIC_BWD = "tokens/sec per CAAT sublayer bwd (1 GPU, P emulated); % MFMA or HBM roofline"
 PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # MI355X: bf16 dense TFLOP/s, HBM3E GB/s
 DEFAULT_WORKLOAD = "7b-prefill-pair-bf16"
 
@@ -51,6 +58,43 @@ def kernel_work(w, T, name, store_resid, n_s):
     if name.endswith("K3"):
         return 0.0, b * (part + E + E + (E if store_resid else 0) + 2 * h)
     raise KeyError(name)
+
+
+def kernel_work_bwd(w, T, sub, step):
+    """Algorithmic FLOPs and HBM bytes of one backward step of one sublayer (the steps
+    of caat_backward: BWD_STEPS)."""
+    P, h = w.P, w.h
+    b = 2 if w.dtype == "bf16" else 4
+    E = P * T * h
+    Tp = (T + 7) // 8 * 8
+    if sub == "attn":
+        k2, F1, fs = h // P, 0, 0
+    else:
+        fs = w.f_s
+        k2, F1 = fs, (2 * fs if w.act == "swiglu" else fs)
+    if step == "norm":       # read r, dout, dres; write dZt, dresid
+        return 0.0, b * 5 * E
+    if step == "W2T":
+        return 0.0, b * 2 * P * h * k2
+    if step == "dY":
+        return 2.0 * P * T * h * k2, b * (P * k2 * h + E + P * T * k2)
+    if step == "a":
+        return 2.0 * P * T * h * F1, b * (P * F1 * h + E + P * T * F1)
+    if step == "act":
+        return 0.0, b * 2 * (P * T * F1 + P * T * fs)
+    if step == "W1T":
+        return 0.0, b * 2 * P * F1 * h
+    if step == "dx":
+        return 2.0 * P * T * F1 * h, b * (P * h * F1 + P * T * F1 + E)
+    if step == "daT_xT":
+        return 0.0, b * 2 * (P * T * F1 + E)
+    if step == "dW1":
+        return 2.0 * P * F1 * h * Tp, b * (P * h * Tp + P * F1 * Tp + P * F1 * h)
+    if step == "YT_dZtT":
+        return 0.0, b * 2 * (P * T * k2 + E)
+    if step == "dW2":
+        return 2.0 * P * h * k2 * Tp, b * (P * k2 * Tp + P * h * Tp + P * h * k2)
+    raise KeyError(step)
 
 
 def source_sha(path):
@@ -117,6 +161,152 @@ def cpu_baseline(w, inputs, p, budget_s):
                       f"sublayer), fp64, {dt:.1f} s; rows are independent, so tokens/s = rows / s"}
 
 
+def cpu_baseline_backward(w, inputs, p, budget_s):
+    """The oracle backward (fp64 C, OpenMP) of the whole path on a bounded sample of token
+    rows: the oracle forward of the out-projection gives the MLP's input, then the MLP
+    backward, then the out-projection backward fed with the MLP's input gradients."""
+    import oracle
+    import numpy as np
+    from partial_activation_sync_amd import synth
+    from tests.oracle_ref import ACT, NORM
+
+    T = inputs["ctx"].shape[1] if "ctx" in inputs else inputs["x"].shape[1]
+    n_s = oracle.shared_channels(w.h, p)
+    norm = NORM[w.norm]
+    gamma, beta = inputs["gamma"].float(), inputs["beta"].float()
+    W1, W2 = inputs["W1"].float(), inputs["W2"].float()
+    dt = inputs["W1"].dtype
+
+    def one(rows):
+        n = len(rows)
+        dout = synth.normal((w.P, T, w.h), synth.DOUT, dtype=dt)[:, rows].float()
+        dres = synth.normal((w.P, T, w.h), synth.DRES, dtype=dt)[:, rows].float()
+        t0 = time.perf_counter()
+        if "ctx" in inputs:
+            ctx, x0 = inputs["ctx"][:, rows].float(), inputs["x0"][:, rows].float()
+            Wo = inputs["Wo"].float()
+            a_out, a_res = oracle.sublayer(ctx, None, Wo, gamma, beta=beta, resid=x0,
+                                           act=oracle.NONE, norm=norm, n_s=n_s, eps=w.eps)
+            g = oracle.sublayer_backward(a_out, W1, W2, gamma, dout, act=ACT[w.act], norm=norm,
+                                         n_s=n_s, resid=a_res, dres=dres, eps=w.eps)
+            oracle.sublayer_backward(ctx, None, Wo, gamma, g["dx"], act=oracle.NONE, norm=norm,
+                                     n_s=n_s, resid=x0, dres=g["dresid"], eps=w.eps)
+        else:
+            oracle.sublayer_backward(inputs["x"][:, rows].float(), W1, W2, gamma, dout,
+                                     act=ACT[w.act], norm=norm, n_s=n_s, dres=dres, eps=w.eps)
+        return time.perf_counter() - t0
+
+    n = 8
+    dt_s = one(synth.sample_rows(T, n))
+    for _ in range(3):
+        if dt_s >= 0.6 * budget_s or n >= T:
+            break
+        n = int(min(T, max(n + 1, n * budget_s / max(dt_s, 1e-9))))
+        rows = synth.sample_rows(T, n)
+        dt_s = one(rows)
+    return {"value": n / dt_s, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"backward of {n} of {T} token rows of {w.name} (all {w.P} ranks, every "
+                      f"sublayer; weight gradients over the sampled rows), fp64, {dt_s:.1f} s"}
+
+
+def bench_backward(args, w, T, p):
+    import torch
+    import partial_activation_sync_amd as caat
+    from partial_activation_sync_amd import runner
+
+    log(f"[bench] backward {w.name} T={T} p={p} P={w.P} h={w.h} ffn={w.ffn} act={w.act} "
+        f"norm={w.norm}")
+    inputs = runner.make_inputs(w, T=T)
+    run = runner.Run(w, inputs, p=p, store_resid=True, weight_copies=1)
+    br = runner.BackwardRun(run)
+    torch.cuda.synchronize()
+    subs = ["mlp"] + (["attn"] if run.attn is not None else [])
+    steps = caat.BWD_STEPS
+    K = args.steps
+
+    def events(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in ev:             # torch creates the HIP event on its first record
+            e.record()
+        return ev
+
+    start = events(K)
+    ev = {sub: [events(len(steps)) for _ in range(K)] for sub in subs}
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        br.step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(K):
+        start[s].record()
+        br.step(events_mlp=[e.cuda_event for e in ev["mlp"][s]],
+                events_attn=[e.cuda_event for e in ev["attn"][s]] if "attn" in subs else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    last = ev[subs[-1]]
+    span_ms = start[0].elapsed_time(last[K - 1][-1]) / K
+    kern_ms = {}
+    for s in range(K):
+        prev = start[s]
+        for sub in subs:
+            for i, name in enumerate(steps):
+                key = f"{sub}.{name}"
+                kern_ms[key] = kern_ms.get(key, 0.0) + prev.elapsed_time(ev[sub][s][i]) / K
+                prev = ev[sub][s][i]
+    log(f"[bench] {K} backward steps: {span_ms:.4f} ms/step, wall {wall / K * 1e3:.3f} ms/step")
+    detail = {}
+    for key, ms in kern_ms.items():
+        sub, name = key.split(".")
+        flops, nbytes = kernel_work_bwd(w, T, sub, name)
+        if sub == "attn" and name in ("a", "act", "W1T", "dx", "daT_xT", "dW1"):
+            continue          # no first GEMM in the out-projection
+        d = {"ms": round(ms, 4), "share": round(ms / span_ms, 3)}
+        if flops:
+            d["TFLOP/s"] = round(flops / ms / 1e9, 1)
+            d["mfma_frac"] = round(flops / ms / 1e9 / PEAK["mfma"], 3)
+        d["GB/s"] = round(nbytes / ms / 1e6, 1)
+        d["hbm_frac"] = round(nbytes / ms / 1e6 / PEAK["hbm"], 3)
+        detail[key] = d
+        log(f"[bench]   {key:16s} {ms:8.4f} ms  {d}")
+    dom = max(detail, key=lambda k: detail[k]["ms"])
+    sub, name = dom.split(".")
+    flops, nbytes = kernel_work_bwd(w, T, sub, name)
+    ridge = PEAK["mfma"] * 1e12 / (PEAK["hbm"] * 1e9)
+    ms = kern_ms[dom]
+    if flops and flops / nbytes >= ridge:
+        achieved = flops / ms / 1e9
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK["mfma"],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma"], 4)}
+    else:
+        achieved = nbytes / ms / 1e6
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"],
+                "unit": "GB/s", "frac": round(achieved / PEAK["hbm"], 4)}
+    roof["kernel"] = dom
+    roof["algorithmic_per_launch"] = flops if flops else nbytes
+    src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
+                       "backward.hip" if not flops else
+                       ("gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"))
+    roof["traffic"] = traffic_for(src, traffic_key(w.name + ":bwd", T, dom))
+    base = None
+    if args.cpu_budget > 0:
+        log("[bench] timing the oracle backward on host cores ...")
+        base = cpu_baseline_backward(w, inputs, p, args.cpu_budget)
+        log(f"[bench] cpu baseline: {base}")
+    line = {
+        "metric": METRIC_BWD, "value": round(T / (span_ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(span_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) activations and upstream gradients, N(0,0.02^2) weights",
+        "config": {"workload": w.name, "pass": "backward", "P": w.P, "h": w.h, "ffn": w.ffn,
+                   "T": T, "p": p, "n_s": run.mlp.n_s, "act": w.act, "norm": w.norm,
+                   "sublayers": list(w.sublayers), "parallelism": f"tp{w.P} emulated on 1 GPU"},
+        "roofline": roof,
+        "cpu_baseline": base,
+        "kernels": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
 COPY_BYTES = 512 << 20
 
 
@@ -149,6 +339,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as a captured HIP graph (one graph per weight "
                          "copy, replayed); value and ms_per_step then come from the replays")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
+                    help="time the forward (default) or the backward of the path")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
@@ -170,6 +362,8 @@ def main():
     T = args.T or w.T
     p = w.p if args.p is None else args.p
     torch.cuda.set_device(0)
+    if args.pass_ == "backward":
+        return bench_backward(args, w, T, p)
     log(f"[bench] {w.name} T={T} p={p} P={w.P} h={w.h} ffn={w.ffn} act={w.act} norm={w.norm}")
     t0 = time.perf_counter()
     inputs = runner.make_inputs(w, T=T)

@@ -203,7 +203,21 @@ typedef struct {
     void *workspace;        /* caller-owned device memory, 16-byte aligned */
     size_t workspace_bytes; /* >= caat_backward_workspace_bytes(T) */
     void *stream;
+    void *const *events;    /* NULL, or n_events hipEvent_t: event k is recorded on the
+                               stream after step k (see CAAT_BWD_STEPS), for timing */
+    int n_events;
 } caat_bwd_args;
+
+/* The steps of caat_backward, in launch order (for caat_bwd_args.events).  Steps that
+ * do not apply (CAAT_NONE has no first GEMM) launch nothing; their events are still
+ * recorded.
+ *   0 norm derivative + reduce over ranks + dgamma/dbeta    1 transpose of W2
+ *   2 GEMM dY = dZt W2                                       3 GEMM a = x W1^T (recompute)
+ *   4 activation backward (da, Y)                            5 transpose of W1
+ *   6 GEMM dx = da W1 (+ residual gradient when resid = in)  7 transposes of da and x
+ *   8 GEMM dW1 = da^T x                                      9 transposes of Y (or H), dZt
+ *  10 GEMM dW2 = dZt^T Y */
+#define CAAT_BWD_STEPS 11
 
 /* The whole backward of one sublayer for every rank.  Returns CAAT_EWORKSPACE for a
  * missing or short workspace, CAAT_EINVAL for bad pointers (a NULL dresid with

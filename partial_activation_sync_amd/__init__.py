@@ -49,7 +49,11 @@ class caat_bwd_args(ctypes.Structure):
                 ("dres", ctypes.c_void_p), ("din", ctypes.c_void_p), ("dresid", ctypes.c_void_p),
                 ("dW1", ctypes.c_void_p), ("dW2", ctypes.c_void_p), ("dgamma", ctypes.c_void_p),
                 ("dbeta", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int)]
+
+
+BWD_STEPS = ("norm", "W2T", "dY", "a", "act", "W1T", "dx", "daT_xT", "dW1", "YT_dZtT", "dW2")
 
 
 def lib():
@@ -207,11 +211,19 @@ def caat_backward_workspace_bytes(handle, T) -> int:
 
 
 def caat_backward(handle, T, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgamma,
-                  workspace, dW1=None, dres=None, dresid=None, dbeta=None, stream=None):
+                  workspace, dW1=None, dres=None, dresid=None, dbeta=None, stream=None,
+                  events=None):
+    """events: None, or CAAT_BWD_STEPS raw hipEvent_t handles (ints) recorded after
+    each step (see BWD_STEPS)."""
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * len(events))(*events)
     a = caat_bwd_args(int(T), _ptr(inp), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(out_resid),
                       _ptr(dout), _ptr(dres), _ptr(din), _ptr(dresid), _ptr(dW1), _ptr(dW2),
                       _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
-                      workspace.numel() * workspace.element_size(), _stream(stream))
+                      workspace.numel() * workspace.element_size(), _stream(stream),
+                      ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None,
+                      len(events) if events is not None else 0)
     return _check(lib().caat_backward(handle, ctypes.byref(a)), "caat_backward")
 
 
@@ -288,7 +300,7 @@ class Sublayer:
                                out, resid=resid, beta=beta, out_resid=out_resid, stream=stream)
 
     def backward(self, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgamma, dW1=None,
-                 dres=None, dresid=None, dbeta=None, stream=None):
+                 dres=None, dresid=None, dbeta=None, stream=None, events=None):
         """Gradients of one sublayer (shape and dtype checks, then caat_backward)."""
         import torch
         P, h = self.P, self.h
@@ -314,4 +326,4 @@ class Sublayer:
             self._bws = torch.empty(nbytes, dtype=torch.uint8, device=inp.device)
         return caat_backward(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
                              out_resid, dout, din, dW2, dgamma, self._bws, dW1=dW1, dres=dres,
-                             dresid=dresid, dbeta=dbeta, stream=stream)
+                             dresid=dresid, dbeta=dbeta, stream=stream, events=events)

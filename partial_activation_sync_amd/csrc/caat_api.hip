@@ -487,34 +487,55 @@ CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
     void *dresid = a->dresid ? a->dresid : ws + L.dres;
 #define CAAT_TRY(call) do { const int rc_ = (call); if (rc_ != CAAT_OK) return rc_; } while (0)
 #define CAAT_HIP(call) do { if ((call) != hipSuccess) return CAAT_EDEVICE; } while (0)
-    // Norm derivative per rank, then the reduce over ranks of the shared channels.
+    int step = 0;
+    auto mark = [&]() -> int {   // the caller's timing event after each step
+        if (a->events != nullptr && step < a->n_events &&
+            hipEventRecord(reinterpret_cast<hipEvent_t>(a->events[step]), s) != hipSuccess)
+            return CAAT_EDEVICE;
+        ++step;
+        return CAAT_OK;
+    };
+    // 0: norm derivative per rank, then the reduce over ranks of the shared channels.
     CAAT_TRY(run_psync_bwd(c, T, a->out_resid, a->dout, a->dres, a->gamma, dzt, dresid,
                            a->dgamma, a->dbeta, ws + L.gpart, s));
-    // Second GEMM: dY = dZt W2 (per rank), through W2^T [k2][h].
+    CAAT_TRY(mark());
+    // 1, 2: second GEMM, dY = dZt W2 (per rank), through W2^T [k2][h].
     CAAT_HIP(caat::transpose(a->W2, ws + L.W2T, P, h, k2, h, c->dtype, s));
+    CAAT_TRY(mark());
     void *dY = mlp ? ws + L.dY : a->din;   // out-projection: dY is dH
     CAAT_TRY(run_gemm(c, plain_args(c, T, k2, h, ws + L.W2T, dzt, dY), s));
+    CAAT_TRY(mark());
     const void *y_in = a->in;              // the second GEMM's input (H for the out-projection)
     if (mlp) {
-        // Recompute the pre-activation, then da = dY * sigma'(a) and Y = sigma(a).
+        // 3, 4: recompute the pre-activation, then da = dY * sigma'(a) and Y = sigma(a).
         CAAT_TRY(run_gemm(c, plain_args(c, T, F1, h, a->W1, a->in, ws + L.A), s));
+        CAAT_TRY(mark());
         CAAT_HIP(caat::act_backward(c->act, c->dtype, (size_t)P * T, fs, ws + L.A, dY, ws + L.da,
                                     ws + L.Y, s));
+        CAAT_TRY(mark());
         y_in = ws + L.Y;
-        // First GEMM: dx = da W1, through W1^T [h][F1].
+        // 5, 6: first GEMM, dx = da W1, through W1^T [h][F1].
         CAAT_HIP(caat::transpose(a->W1, ws + L.W1T, P, F1, h, F1, c->dtype, s));
+        CAAT_TRY(mark());
         CAAT_TRY(run_gemm(c, plain_args(c, T, h, F1, ws + L.W1T, ws + L.da, a->din), s));
         if (a->dresid == nullptr)
             CAAT_HIP(caat::add_inplace(a->din, dresid, (size_t)P * T * h, c->dtype, s));
-        // dW1 = da^T x: contraction over tokens, both operands transposed.
+        CAAT_TRY(mark());
+        // 7, 8: dW1 = da^T x: contraction over tokens, both operands transposed.
         CAAT_HIP(caat::transpose(ws + L.da, ws + L.daT, P, T, F1, Tp, c->dtype, s));
         CAAT_HIP(caat::transpose(a->in, ws + L.xT, P, T, h, Tp, c->dtype, s));
+        CAAT_TRY(mark());
         CAAT_TRY(run_gemm(c, plain_args(c, F1, h, Tp, ws + L.xT, ws + L.daT, a->dW1), s));
+        CAAT_TRY(mark());
+    } else {
+        for (int k = 3; k <= 8; ++k) CAAT_TRY(mark());
     }
-    // dW2 = dZt^T Y (or dZt^T H): contraction over tokens.
+    // 9, 10: dW2 = dZt^T Y (or dZt^T H): contraction over tokens.
     CAAT_HIP(caat::transpose(y_in, ws + L.YT, P, T, k2, Tp, c->dtype, s));
     CAAT_HIP(caat::transpose(dzt, ws + L.dztT, P, T, h, Tp, c->dtype, s));
+    CAAT_TRY(mark());
     CAAT_TRY(run_gemm(c, plain_args(c, h, k2, Tp, ws + L.YT, ws + L.dztT, a->dW2), s));
+    CAAT_TRY(mark());
 #undef CAAT_TRY
 #undef CAAT_HIP
     return CAAT_OK;

@@ -151,3 +151,45 @@ class Run:
         b = self._buffers(s, 0)
         return self._row_and_norm(s, d["ctx"], d["Wo"], d["x0"], d["gamma"], d["beta"],
                                   self.attn_out, self.attn_out_resid, b)
+
+
+class BackwardRun:
+    """The backward of the whole path after one forward: the MLP sublayer's backward
+    (upstream gradients dout, dres drawn from ``synth``), then, for pair workloads, the
+    out-projection sublayer's backward fed with the gradients of the MLP's input and
+    residual (the chain rule through the pair).  A step only enqueues library calls."""
+
+    def __init__(self, run: Run, seed=synth.BASE_SEED):
+        self.run = run
+        w = run.w
+        P, T, h = w.P, run.T, w.h
+        dt = torch_dtype(w)
+        dev = run.out.device
+        if run.out_resid is None:
+            raise ValueError("the backward needs the forward's out_resid")
+        run.step()
+        self.dout = synth.normal((P, T, h), synth.DOUT, dtype=dt, seed=seed).to(dev)
+        self.dres = synth.normal((P, T, h), synth.DRES, dtype=dt, seed=seed).to(dev)
+        e = lambda shape, dtype=dt: torch.empty(shape, dtype=dtype, device=dev)
+        F1 = 2 * w.f_s if w.act == "swiglu" else w.f_s
+        pair = run.attn is not None
+        self.mlp_g = {"din": e((P, T, h)), "dresid": e((P, T, h)) if pair else None,
+                      "dW1": e((P, F1, h)), "dW2": e((P, h, w.f_s)),
+                      "dgamma": e((h,), torch.float32), "dbeta": e((h,), torch.float32)}
+        self.attn_g = None
+        if pair:
+            self.attn_g = {"din": e((P, T, h // P)), "dresid": e((P, T, h)),
+                           "dW2": e((P, h, h // P)), "dgamma": e((h,), torch.float32),
+                           "dbeta": e((h,), torch.float32)}
+
+    def step(self, events_mlp=None, events_attn=None):
+        run, d, g = self.run, self.run.dev, self.mlp_g
+        mlp_in = run.attn_out if run.attn is not None else d["x"]
+        run.mlp.backward(mlp_in, d["W1"], d["W2"], d["gamma"], run.out_resid, self.dout, g["din"],
+                         g["dW2"], g["dgamma"], dW1=g["dW1"], dres=self.dres, dresid=g["dresid"],
+                         dbeta=g["dbeta"], events=events_mlp)
+        if run.attn is not None:
+            a = self.attn_g
+            run.attn.backward(d["ctx"], None, d["Wo"], d["gamma"], run.attn_out_resid, g["din"],
+                              a["din"], a["dW2"], a["dgamma"], dres=g["dresid"],
+                              dresid=a["dresid"], dbeta=a["dbeta"], events=events_attn)

@@ -168,7 +168,7 @@ def test_backward_workspace_and_checks_before_any_launch():
         ("T", T), ("in_", fake), ("W1", fake), ("W2", fake), ("gamma", fake),
         ("out_resid", fake), ("dout", fake), ("dres", None), ("din", fake), ("dresid", None),
         ("dW1", fake), ("dW2", fake), ("dgamma", fake), ("dbeta", None), ("workspace", fake),
-        ("workspace_bytes", need), ("stream", None))])
+        ("workspace_bytes", need), ("stream", None), ("events", None), ("n_events", 0))])
     assert L.caat_backward(None, ctypes.byref(args())) == caat.EINVAL
     assert L.caat_backward(hd, None) == caat.EINVAL
     assert L.caat_backward(hd, ctypes.byref(args(T=0))) == caat.EINVAL

@@ -160,3 +160,36 @@ def test_backward_deterministic():
     a = _run(4, 130, 512, 4 * 264, "swiglu", "rmsnorm", 0.5, "bf16")
     b = _run(4, 130, 512, 4 * 264, "swiglu", "rmsnorm", 0.5, "bf16")
     assert a == b
+
+
+def test_backward_pair_chain_matches_oracle():
+    """The pair's backward as the benchmark runs it: the MLP sublayer's backward, then
+    the out-projection's backward fed with the MLP's input and residual gradients."""
+    from partial_activation_sync_amd import runner, workloads as W
+    w, T = W.PAIR_130M_BF16, 96
+    _say(f"[case] pair backward chain {w.name} T={T}")
+    inputs = runner.make_inputs(w, T=T, norm_params="random")
+    run = runner.Run(w, inputs)
+    br = runner.BackwardRun(run)
+    br.step()
+    torch.cuda.synchronize()
+    n_s = oracle.shared_channels(w.h, w.p)
+    norm = NORM[w.norm]
+    f = lambda t: t.float()
+    gamma, beta = f(inputs["gamma"]), f(inputs["beta"])
+    a_out, a_res = oracle.sublayer(f(inputs["ctx"]), None, f(inputs["Wo"]), gamma, beta=beta,
+                                   resid=f(inputs["x0"]), act=oracle.NONE, norm=norm, n_s=n_s,
+                                   eps=w.eps)
+    gm = oracle.sublayer_backward(a_out, f(inputs["W1"]), f(inputs["W2"]), gamma, f(br.dout),
+                                  act=ACT[w.act], norm=norm, n_s=n_s, resid=a_res,
+                                  dres=f(br.dres), eps=w.eps)
+    ga = oracle.sublayer_backward(f(inputs["ctx"]), None, f(inputs["Wo"]), gamma, gm["dx"],
+                                  act=oracle.NONE, norm=norm, n_s=n_s, resid=f(inputs["x0"]),
+                                  dres=gm["dresid"], eps=w.eps)
+    names = {"din": "dx", "dresid": "dresid", "dW1": "dW1", "dW2": "dW2", "dgamma": "dgamma",
+             "dbeta": "dbeta"}
+    errs = {f"mlp.{k}": rel_err(v, gm[names[k]]) for k, v in br.mlp_g.items() if v is not None}
+    errs.update({f"attn.{k}": rel_err(v, ga[names[k]]) for k, v in br.attn_g.items()})
+    _say("   errors:", {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, e in errs.items():
+        assert e <= TOL["bf16"], (k, e)
