@@ -181,7 +181,7 @@ int caat_partial_sync_norm(caat_handle handle, int T, const void *partials, cons
  * ------------------------------------------------------------------------------ */
 
 /* Bytes of device workspace caat_backward needs for T tokens (0 for a NULL handle or
- * T < 1).  caat_partial_sync_norm_backward needs 8 * h * min(T, 1024) + 512 bytes of it. */
+ * T < 1).  caat_partial_sync_norm_backward needs 8 * h * min(T, 256) + 512 bytes of it. */
 size_t caat_backward_workspace_bytes(caat_handle handle, int T);
 
 typedef struct {

@@ -23,13 +23,16 @@
 namespace caat {
 namespace {
 
-constexpr int BWD_MAX_BLOCKS = 1024;
+// Workgroups of the norm backward: one per CU is what its registers allow, and each
+// adds one row of norm-parameter partials.
+constexpr int BWD_MAX_BLOCKS = 256;
 constexpr int BWD_MAX_WAVES = 8;
 
 template <int NCH, int GB, int NORM, typename TIO>
 __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
 {
-    __shared__ float red[BWD_MAX_WAVES * 2 * GB];
+    // Two reduction buffers used in turn, so consecutive block sums need one barrier each.
+    __shared__ float red[2][BWD_MAX_WAVES * 2 * GB];
     const int P = a.P, T = a.T, h = a.h, n_s = a.n_s;
     const size_t rs = (size_t)T * h;
     const TIO *Rv = reinterpret_cast<const TIO *>(a.r);
@@ -66,7 +69,8 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
             for (int e = 0; e < 8; ++e) sg[j][e] = 0.f;
 
         for (int g0 = 0; g0 < P; g0 += GB) {
-            float rv[GB][NCH][8], dv[GB][NCH][8];
+            // Every load of the group at once, kept in the storage format.
+            Raw<TIO> rr[GB][NCH], dd[GB][NCH], ee[GB][NCH];
 #pragma unroll
             for (int q = 0; q < GB; ++q) {
                 const int m = g0 + q;
@@ -74,11 +78,13 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
                 for (int j = 0; j < NCH; ++j) {
                     if (m < P && ok[j]) {
                         const size_t off = m * rs + row + c[j] * 8;
-                        Vec8<TIO>::load(Rv + off, rv[q][j]);
-                        Vec8<TIO>::load(Dv + off, dv[q][j]);
+                        rr[q][j].load(Rv + off);
+                        dd[q][j].load(Dv + off);
+                        if (DRv) ee[q][j].load(DRv + off); else ee[q][j].zero();
                     } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) rv[q][j][e] = dv[q][j][e] = 0.f;
+                        rr[q][j].zero();
+                        dd[q][j].zero();
+                        ee[q][j].zero();
                     }
                 }
             }
@@ -90,14 +96,16 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
                 for (int q = 0; q < GB; ++q) {
                     float acc = 0.f;
 #pragma unroll
-                    for (int j = 0; j < NCH; ++j)
+                    for (int j = 0; j < NCH; ++j) {
+                        float v[8];
+                        rr[q][j].unpack(v);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) acc += rv[q][j][e];
+                        for (int e = 0; e < 8; ++e) acc += v[e];
+                    }
                     s[q] = acc;
                 }
                 if (NORM == CAAT_LAYERNORM) {
-                    block_sum<GB>(s, red);
-                    __syncthreads();
+                    block_sum<GB>(s, red[0]);
 #pragma unroll
                     for (int q = 0; q < GB; ++q) mean[q] = s[q] * inv_h;
                 } else {
@@ -111,16 +119,18 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
                 for (int q = 0; q < GB; ++q) {
                     float acc = 0.f;
 #pragma unroll
-                    for (int j = 0; j < NCH; ++j)
+                    for (int j = 0; j < NCH; ++j) {
+                        float v[8];
+                        rr[q][j].unpack(v);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float d = ok[j] ? rv[q][j][e] - mean[q] : 0.f;
+                            const float d = ok[j] ? v[e] - mean[q] : 0.f;
                             acc += d * d;
                         }
+                    }
                     s[q] = acc;
                 }
-                block_sum<GB>(s, red);
-                __syncthreads();
+                block_sum<GB>(s, red[1]);
 #pragma unroll
                 for (int q = 0; q < GB; ++q) inv[q] = rsqrtf(s[q] * inv_h + a.eps);
             }
@@ -130,19 +140,22 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
             for (int q = 0; q < GB; ++q) {
                 float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-                for (int j = 0; j < NCH; ++j)
+                for (int j = 0; j < NCH; ++j) {
+                    float v[8], d[8];
+                    rr[q][j].unpack(v);
+                    dd[q][j].unpack(d);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float dn = dv[q][j][e] * gam[j][e];
-                        const float nh = ok[j] ? (rv[q][j][e] - mean[q]) * inv[q] : 0.f;
+                        const float dn = d[e] * gam[j][e];
+                        const float nh = ok[j] ? (v[e] - mean[q]) * inv[q] : 0.f;
                         s1 += dn;
                         s2 += dn * nh;
                     }
+                }
                 s12[q] = s1;
                 s12[GB + q] = s2;
             }
-            block_sum<2 * GB>(s12, red);
-            __syncthreads();
+            block_sum<2 * GB>(s12, red[0]);
 
 #pragma unroll
             for (int q = 0; q < GB; ++q) {
@@ -155,21 +168,17 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
                     if (!ok[j]) continue;
                     const int l0 = c[j] * 8;
                     const size_t off = m * rs + row + l0;
-                    float dr[8];
-                    if (DRv) {
-                        Vec8<TIO>::load(DRv + off, dr);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) dr[e] = 0.f;
-                    }
-                    float gv[8];
+                    float v[8], d[8], dr[8], gv[8];
+                    rr[q][j].unpack(v);
+                    dd[q][j].unpack(d);
+                    ee[q][j].unpack(dr);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float nh = (rv[q][j][e] - mean[q]) * inv[q];
-                        const float dn = dv[q][j][e] * gam[j][e];
+                        const float nh = (v[e] - mean[q]) * inv[q];
+                        const float dn = d[e] * gam[j][e];
                         gv[e] = inv[q] * (dn - nh * s2 - s1) + dr[e];
-                        gacc[j][e] += dv[q][j][e] * nh;
-                        bacc[j][e] += dv[q][j][e];
+                        gacc[j][e] += d[e] * nh;
+                        bacc[j][e] += d[e];
                     }
                     if (DRES) Vec8<TIO>::store(DRES + off, gv);
                     if (l0 + 8 <= n_s) {
@@ -190,6 +199,8 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
                     }
                 }
             }
+            // red[0] is written again by the next group's first block sum.
+            __syncthreads();
         }
         // Shared channels: every rank's partial receives the sum over ranks.
 #pragma unroll
@@ -236,17 +247,33 @@ hipError_t launch_bwd(const PsyncBwdArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// 64 columns per workgroup; the 4 waves take rows r = wave (mod 4), each lane summing
+// its column in ascending row order, then the 4 partial sums are added in wave order.
 __global__ __launch_bounds__(256) void k_colsum(const float *__restrict__ part, int rows, int h,
                                                 float *__restrict__ out)
 {
-    const int l = blockIdx.x * blockDim.x + threadIdx.x;
-    if (l >= h) return;
+    __shared__ float acc[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l = blockIdx.x * 64 + lane;
     float s = 0.f;
-    for (int r = 0; r < rows; ++r) s += part[(size_t)r * h + l];
-    out[l] = s;
+    if (l < h) {
+        int r = wave;
+        for (; r + 12 < rows; r += 16) {
+            const float a0 = part[(size_t)r * h + l], a1 = part[(size_t)(r + 4) * h + l];
+            const float a2 = part[(size_t)(r + 8) * h + l], a3 = part[(size_t)(r + 12) * h + l];
+            s += a0; s += a1; s += a2; s += a3;
+        }
+        for (; r < rows; r += 4) s += part[(size_t)r * h + l];
+    }
+    acc[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && l < h) out[l] = ((acc[0][lane] + acc[1][lane]) + acc[2][lane]) + acc[3][lane];
 }
 
-// 64 x 64 tiles through LDS; rows past R (up to Rp) are written as zero.
+// 64 x 64 tiles through LDS; rows past R (up to Rp) are written as zero.  bf16 with
+// 16-byte accesses on both sides when the row lengths allow (C % 8 == 0 and Rp % 8 ==
+// 0, always true here): a lane loads 8 consecutive elements of a source row and
+// stores 8 consecutive elements of a destination row, gathered from 8 LDS rows.
 template <typename TIO>
 __global__ __launch_bounds__(256) void k_transpose(const TIO *__restrict__ src, TIO *__restrict__ dst,
                                                    int R, int C, int Rp)
@@ -256,18 +283,33 @@ __global__ __launch_bounds__(256) void k_transpose(const TIO *__restrict__ src, 
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
     const TIO *S = src + (size_t)b * R * C;
     TIO *D = dst + (size_t)b * C * Rp;
+    // Load: 64 rows x 8 chunks of 8 elements; thread i takes chunk i % 8 of rows i / 8
+    // and i / 8 + 32.
+    const int ck = threadIdx.x & 7, rr = threadIdx.x >> 3;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int idx = threadIdx.x + i * 256, r = idx >> 6, cc = idx & 63;
-        const int gr = r0 + r, gc = c0 + cc;
-        tile[r][cc] = (gr < R && gc < C) ? static_cast<float>(S[(size_t)gr * C + gc]) : 0.f;
+    for (int i = 0; i < 2; ++i) {
+        const int r = rr + 32 * i, gr = r0 + r, gc = c0 + ck * 8;
+        float v[8];
+        if (gr < R && gc < C) {
+            Vec8<TIO>::load(S + (size_t)gr * C + gc, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[r][ck * 8 + e] = v[e];
     }
     __syncthreads();
+    // Store: destination row gc = c0 + cc holds tile column cc; thread i writes chunk
+    // i % 8 (8 consecutive r) of columns i / 8 and i / 8 + 32.
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int idx = threadIdx.x + i * 256, cc = idx >> 6, r = idx & 63;
-        const int gr = r0 + r, gc = c0 + cc;
-        if (gc < C && gr < Rp) D[(size_t)gc * Rp + gr] = static_cast<TIO>(tile[r][cc]);
+    for (int i = 0; i < 2; ++i) {
+        const int cc = rr + 32 * i, gc = c0 + cc, gr = r0 + ck * 8;
+        if (gc >= C || gr >= Rp) continue;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[ck * 8 + e][cc];
+        Vec8<TIO>::store(D + (size_t)gc * Rp + gr, v);
     }
 }
 
@@ -372,7 +414,7 @@ hipError_t psync_norm_bwd(const PsyncBwdArgs &a, int dtype, hipStream_t s) {
 }
 
 hipError_t colsum_f32(const float *part, int rows, int h, float *out, hipStream_t s) {
-    hipLaunchKernelGGL(k_colsum, dim3((h + 255) / 256), dim3(256), 0, s, part, rows, h, out);
+    hipLaunchKernelGGL(k_colsum, dim3((h + 63) / 64), dim3(256), 0, s, part, rows, h, out);
     return hipGetLastError();
 }
 
