@@ -15,11 +15,11 @@
 //     no ds_write); rows outside the matrices and the K tail read as zero from the
 //     buffer descriptor's range check;
 //   * two LDS stages held in two separate arrays, so the compiler can tell the stage
-//     being filled from the stage being read and waits on the loads only at the
-//     barrier; one barrier per K step; the next step's loads are issued right after
-//     the barrier and fly while this step's MFMAs run;
-//   * within a step, the fragment reads for sub-step kk+1 are interleaved with the
-//     MFMAs of sub-step kk;
+//     being filled from the stage being read; one barrier per K step, half way through
+//     its last sub-step; the next step's loads are issued at the start of a step and
+//     fly while its MFMAs run;
+//   * the fragment reads for sub-step kk+1 are interleaved with the MFMAs of sub-step
+//     kk, and the next step's first fragments with the last MFMAs of the step;
 //   * LDS rows are 128 B (64 bf16) split in eight 16-byte chunks stored at
 //     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts.
 // Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
@@ -73,7 +73,11 @@ __device__ __forceinline__ float gelu_tanh(float v) {
     // tanh form of GeLU (Hendrycks and Gimpel): c = sqrt(2 / pi), cubic coefficient 0.044715
     return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
 }
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), the division as a hardware reciprocal (1 ulp; the result is
+// rounded to bf16).
+__device__ __forceinline__ float silu(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // Block index -> tile index.  Workgroups go round-robin to the 8 XCDs; give each XCD
 // one contiguous range of tiles.
@@ -190,59 +194,85 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
 
-    // MFMAs over one LDS stage; reads for sub-step kk+1 interleave with MFMAs of kk.
-#define CAAT_COMPUTE(Lb)                                                                   \
+    // Fragment registers: two sets, sub-steps alternate between them, carried across K
+    // steps (the end of a step reads the first fragments of the next).  The reads for
+    // sub-step kk+1 are interleaved with the MFMAs of sub-step kk; each sub-step is a
+    // scheduling region of its own, so the interleave slots can only take the next
+    // sub-step's reads (otherwise the scheduler fills them with the current sub-step's
+    // reads and waits on each one right before its MFMA).
+    bf16x8 af[2][IB], bfr[2][JB];
+#define CAAT_READ(q, Lb, kk)                                                               \
     do {                                                                                   \
-        bf16x8 af[2][IB], bfr[2][JB];                                                      \
         CAAT_UNROLL for (int i = 0; i < IB; ++i)                                           \
-            af[0][i] = __builtin_bit_cast(bf16x8, (Lb)[aoff[0] + i * 256]);                \
+            af[q][i] = __builtin_bit_cast(bf16x8, (Lb)[aoff[kk] + i * 256]);               \
         CAAT_UNROLL for (int j = 0; j < JB; ++j)                                           \
-            bfr[0][j] = __builtin_bit_cast(bf16x8, (Lb)[boff[0] + j * 256]);               \
-        CAAT_UNROLL for (int kk = 0; kk < 4; ++kk) {                                       \
-            const int cur = kk & 1, nxt = cur ^ 1;                                         \
-            if (kk < 3) {                                                                  \
-                CAAT_UNROLL for (int i = 0; i < IB; ++i)                                   \
-                    af[nxt][i] = __builtin_bit_cast(bf16x8, (Lb)[aoff[kk + 1] + i * 256]); \
-                CAAT_UNROLL for (int j = 0; j < JB; ++j)                                   \
-                    bfr[nxt][j] = __builtin_bit_cast(bf16x8, (Lb)[boff[kk + 1] + j * 256]);\
-            }                                                                              \
-            CAAT_UNROLL for (int i = 0; i < IB; ++i)                                       \
-                CAAT_UNROLL for (int j = 0; j < JB; ++j)                                   \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                   \
-                        af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);                      \
-            if (kk < 3) {                                                                  \
-                CAAT_UNROLL for (int r = 0; r < NREAD; ++r) {                              \
-                    CAAT_SCHED_GROUP(SG_MFMA, 1);                                          \
-                    CAAT_SCHED_GROUP(SG_DS_READ, 1);                                       \
-                }                                                                          \
-                if (NMFMA > NREAD) CAAT_SCHED_GROUP(SG_MFMA, NMFMA - NREAD);               \
-            } else {                                                                       \
-                CAAT_SCHED_GROUP(SG_MFMA, NMFMA);                                          \
-            }                                                                              \
+            bfr[q][j] = __builtin_bit_cast(bf16x8, (Lb)[boff[kk] + j * 256]);              \
+    } while (0)
+#define CAAT_MMA(q, i0, i1)                                                                \
+    do {                                                                                   \
+        CAAT_UNROLL for (int i = (i0); i < (i1); ++i)                                      \
+            CAAT_UNROLL for (int j = 0; j < JB; ++j)                                       \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                       \
+                    af[q][i], bfr[q][j], acc[i][j], 0, 0, 0);                              \
+    } while (0)
+    // nm MFMAs with NREAD fragment reads interleaved one to one, then a region fence.
+#define CAAT_INTERLEAVE(nm)                                                                \
+    do {                                                                                   \
+        CAAT_UNROLL for (int r = 0; r < NREAD; ++r) {                                      \
+            if (r < (nm)) CAAT_SCHED_GROUP(SG_MFMA, 1);                                    \
+            CAAT_SCHED_GROUP(SG_DS_READ, 1);                                               \
         }                                                                                  \
+        if ((nm) > NREAD) CAAT_SCHED_GROUP(SG_MFMA, (nm) - NREAD);                         \
+        CAAT_SCHED_FENCE();                                                                \
+    } while (0)
+    // One K step on stage Lb whose sub-step 0 fragments are in set 0; Ln (the other
+    // stage) receives step ks + 1.  The wait and the barrier sit half way through the
+    // last sub-step: by then step ks + 1 has had most of a step to land, and the second
+    // half of the MFMAs covers the reads of its first fragments.  At the barrier every
+    // wave's reads of Lb are complete, so the next step may refill Lb.
+#define CAAT_STEP_MORE(ks, Lb, Ln)                                                         \
+    do {                                                                                   \
+        CAAT_ISSUE(min((ks) + 1, nsteps - 1), Ln);                                         \
+        CAAT_READ(1, Lb, 1); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_READ(0, Lb, 2); CAAT_MMA(1, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_READ(1, Lb, 3); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_MMA(1, 0, IB / 2);                                                            \
+        CAAT_SCHED_FENCE();                                                                \
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                        \
+        __builtin_amdgcn_s_barrier();                                                      \
+        CAAT_SCHED_FENCE();                                                                \
+        CAAT_READ(0, Ln, 0); CAAT_MMA(1, IB / 2, IB); CAAT_INTERLEAVE(NMFMA / 2);          \
+    } while (0)
+    // The last K step: no next step to load or read.
+#define CAAT_STEP_LAST(Lb)                                                                 \
+    do {                                                                                   \
+        CAAT_READ(1, Lb, 1); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_READ(0, Lb, 2); CAAT_MMA(1, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_READ(1, Lb, 3); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_MMA(1, 0, IB);                                                                \
     } while (0)
 
     CAAT_ISSUE(0, L0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    CAAT_READ(0, L0, 0);
+    // Whole pairs of steps in the loop; an odd last step follows it.  With an even
+    // count, the last step of the loop loads its own step again into the idle stage
+    // (the load index is clamped), which nothing reads: one code path reaches the
+    // epilogue from the loop and one from the last step, as few as the accumulators
+    // can take without spilling.
     int kt = 0;
     for (; kt + 2 <= nsteps; kt += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        CAAT_SCHED_FENCE();
-        CAAT_ISSUE(kt + 1, L1);
-        CAAT_COMPUTE(L0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        CAAT_SCHED_FENCE();
-        if (kt + 2 < nsteps) CAAT_ISSUE(kt + 2, L0);
-        CAAT_COMPUTE(L1);
+        CAAT_STEP_MORE(kt, L0, L1);
+        CAAT_STEP_MORE(kt + 1, L1, L0);
     }
-    if (kt < nsteps) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        CAAT_COMPUTE(L0);
-    }
+    if (kt < nsteps) CAAT_STEP_LAST(L0);
+#undef CAAT_READ
+#undef CAAT_MMA
+#undef CAAT_INTERLEAVE
+#undef CAAT_STEP_MORE
+#undef CAAT_STEP_LAST
 #undef CAAT_ISSUE
-#undef CAAT_COMPUTE
 
     // Epilogue.  Accumulator element v of block (i, j) in lane l is channel row
     // 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.

@@ -68,5 +68,34 @@ __device__ __forceinline__ void block_sum(float (&v)[NV], float *red) {
     }
 }
 
+// One 8-element chunk kept in its storage format (4 VGPRs for bf16) and unpacked to fp32
+// where it is used.
+template <typename TIO> struct Raw;
+template <> struct Raw<__bf16> {
+    uint4 u;
+    __device__ __forceinline__ void load(const __bf16 *p) { u = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void unpack(float (&v)[8]) const {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw<float> {
+    float4 a, b;
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void unpack(float (&v)[8]) const {
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
 }  // namespace
 }  // namespace caat
