@@ -57,6 +57,10 @@ def _load():
             [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_double]
             + [fp] * 7 + [dp] * 6)
         lib.oracle_sublayer_backward.restype = ctypes.c_int
+        lib.oracle_linear.argtypes = [ctypes.c_int] * 4 + [fp] * 2 + [dp]
+        lib.oracle_linear.restype = ctypes.c_int
+        lib.oracle_attention.argtypes = [ctypes.c_int] * 5 + [fp] + [dp]
+        lib.oracle_attention.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -187,3 +191,41 @@ def sublayer_backward(x, W1, W2, gamma, dout, *, act, norm, n_s, resid=None, dre
     if rc != 0:
         raise ValueError("oracle_sublayer_backward rejected its arguments")
     return res
+
+
+def linear(x, W):
+    """Per-rank linear layer, fp64: out[m][t][n] = sum_k x[m][t][k] W[m][n][k]."""
+    x, W = _f32(x), _f32(W)
+    P, T, K = x.shape
+    N = W.shape[1]
+    out = np.empty((P, T, N), np.float64)
+    if _load().oracle_linear(P, T, K, N, _fptr(x), _fptr(W), _dptr(out)) != 0:
+        raise ValueError("oracle_linear rejected its arguments")
+    return out
+
+
+def attention(qkv, *, S, nh, d):
+    """Causal self-attention of every head of every rank (App. A, Eq. 16 / 18 / 24), fp64.
+
+    qkv [P][T][3 nh d] (Q, K, V of the rank's heads); T = nseq * S tokens, causal within
+    each sequence of S.  Returns H [P][T][nh d]."""
+    qkv = _f32(qkv)
+    P, T, _ = qkv.shape
+    H = np.empty((P, T, nh * d), np.float64)
+    if _load().oracle_attention(P, T, S, nh, d, _fptr(qkv), _dptr(H)) != 0:
+        raise ValueError("oracle_attention rejected its arguments")
+    return H
+
+
+def block_forward(h_in, r_in, Wqkv, Wo, W1, W2, gamma_a, gamma_m, *, S, nh, d, act, norm, n_s,
+                  beta_a=None, beta_m=None, s_priv=1.0, eps=1e-5):
+    """One transformer block with partially synchronized activations, every rank on one
+    device (§3.2): per rank, QKV projection of the block input h_in, causal attention,
+    then the out-projection sublayer (residual r_in) and the MLP sublayer (Eq. 22 / 24,
+    Eq. 9).  Returns (out, out_resid) of the MLP sublayer: the next block's (h_in, r_in)."""
+    qkv = linear(h_in, Wqkv)
+    H = attention(qkv, S=S, nh=nh, d=d)
+    a_out, a_res = sublayer(H, None, Wo, gamma_a, act=NONE, norm=norm, n_s=n_s, beta=beta_a,
+                            resid=r_in, s_priv=s_priv, eps=eps)
+    return sublayer(a_out, W1, W2, gamma_m, act=act, norm=norm, n_s=n_s, beta=beta_m,
+                    resid=a_res, s_priv=s_priv, eps=eps)

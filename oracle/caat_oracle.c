@@ -555,3 +555,82 @@ int oracle_sublayer_backward(int P, int T, int h, int ffn, int act, int norm, in
     free(a); free(y); free(zt); free(nh); free(g); free(dzt); free(da);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------
+ * The steps either side of the path, for the full block with logical devices
+ * (§3.2; App. A, Eq. 16, 18 and 24).
+ */
+
+/* One linear layer per rank: out[m][t][n] = sum_k x[m][t][k] W[m][n][k] (row n of W is
+ * the weight column of output n), fp64.  Returns 0, or -1 on bad arguments. */
+int oracle_linear(int P, int T, int K, int N, const float *x, const float *W, double *out)
+{
+    if (P < 1 || T < 0 || K < 1 || N < 1)
+        return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int m = 0; m < P; ++m)
+        for (int t = 0; t < T; ++t) {
+            const float *xr = x + ((size_t)m * T + t) * K;
+            const float *Wm = W + (size_t)m * N * K;
+            double *o = out + ((size_t)m * T + t) * N;
+            for (int n = 0; n < N; ++n) {
+                double s = 0.0;
+                for (int k = 0; k < K; ++k)
+                    s += (double)xr[k] * (double)Wm[(size_t)n * K + k];
+                o[n] = s;
+            }
+        }
+    return 0;
+}
+
+/* Causal self-attention of every head of every rank: H_m = Attention(X_m W^Q_m,
+ * X_m W^K_m, X_m W^V_m) (App. A.1 Eq. 16 / 18, App. A.2 Eq. 24), each rank holding nh
+ * heads of width d.  qkv [P][T][3 nh d]: per rank and token, Q of head i in columns
+ * [i d, (i+1) d), K of head i at nh d + i d, V of head i at 2 nh d + i d.  The T tokens
+ * are nseq = T / S sequences of S tokens; token i attends to the tokens j <= i of its
+ * own sequence with weights softmax_j(q_i . k_j / sqrt(d)).  H [P][T][nh d] (fp64),
+ * head i in columns [i d, (i+1) d).  Returns 0, or -1 on bad arguments. */
+int oracle_attention(int P, int T, int S, int nh, int d, const float *qkv, double *H)
+{
+    if (P < 1 || T < 0 || S < 1 || T % S != 0 || nh < 1 || d < 1)
+        return -1;
+    const size_t ld = (size_t)3 * nh * d;
+    const double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)S);
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int m = 0; m < P; ++m)
+            for (int hd = 0; hd < nh; ++hd)
+                for (int t = 0; t < T; ++t) {
+                    const int s0 = (t / S) * S;           /* first token of t's sequence */
+                    const float *q = qkv + ((size_t)m * T + t) * ld + (size_t)hd * d;
+                    double mx = -INFINITY;
+                    for (int j = s0; j <= t; ++j) {
+                        const float *k = qkv + ((size_t)m * T + j) * ld + (size_t)(nh + hd) * d;
+                        double s = 0.0;
+                        for (int e = 0; e < d; ++e)
+                            s += (double)q[e] * (double)k[e];
+                        w[j - s0] = s * scale;
+                        if (w[j - s0] > mx)
+                            mx = w[j - s0];
+                    }
+                    double den = 0.0;
+                    for (int j = s0; j <= t; ++j) {
+                        w[j - s0] = exp(w[j - s0] - mx);
+                        den += w[j - s0];
+                    }
+                    double *o = H + ((size_t)m * T + t) * (size_t)nh * d + (size_t)hd * d;
+                    for (int e = 0; e < d; ++e)
+                        o[e] = 0.0;
+                    for (int j = s0; j <= t; ++j) {
+                        const float *v = qkv + ((size_t)m * T + j) * ld + (size_t)(2 * nh + hd) * d;
+                        const double pj = w[j - s0] / den;
+                        for (int e = 0; e < d; ++e)
+                            o[e] += pj * (double)v[e];
+                    }
+                }
+        free(w);
+    }
+    return 0;
+}
