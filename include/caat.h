@@ -233,6 +233,53 @@ int caat_partial_sync_norm_backward(caat_handle handle, int T, const void *out_r
                                     void *dpartials, void *dresid, float *dgamma, float *dbeta,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------------
+ * The full block with logical devices (§3.2; App. A.1 Eq. 16 / 18, App. A.2 Eq. 24):
+ * per rank m, the QKV projection of the rank's nh heads, causal softmax attention per
+ * head, then the out-projection sublayer and the MLP sublayer above.  bf16 only;
+ * head width d = 64 or 128.
+ * ------------------------------------------------------------------------------ */
+
+/* Bytes of device workspace caat_attention needs (V transposed per head). */
+size_t caat_attention_workspace_bytes(int P, int T, int nh, int d);
+
+/* The attention core alone, bf16: for every rank m < P and head i < nh,
+ *   H[m][t][i d .. i d + d) = sum over j of softmax_j(q_t . k_j / sqrt(d)) v_j,
+ * j running over the tokens of t's sequence up to t (causal).  The T tokens are T / S
+ * sequences of S tokens (T % S == 0, S % 8 == 0).
+ *   qkv [P][T][3 nh d]: Q of head i in columns [i d, i d + d), K at nh d + i d, V at
+ *       2 nh d + i d (the QKV projection's output, rank by rank).
+ *   H   [P][T][nh d].
+ * d must be 64 or 128 (else CAAT_EUNSUPPORTED). */
+int caat_attention(int P, int T, int S, int nh, int d, const void *qkv, void *H,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+typedef struct {
+    int T, S;               /* tokens; sequence length (T % S == 0, S % 8 == 0) */
+    const void *in;         /* block input h [P][T][h] (the previous block's out) */
+    const void *resid;      /* residual stream r [P][T][h] (the previous out_resid) */
+    const void *Wqkv;       /* [P][3 h/P][h]: rows [0, h/P) Q, [h/P, 2h/P) K, then V of
+                               the rank's heads (row n of shard m = column n of W^{Q|K|V}_m) */
+    const void *Wo;         /* [P][h][h/P] (the out-projection's W2) */
+    const void *W1, *W2;    /* the MLP's weights, as for caat_forward_ex */
+    const void *gamma_attn, *beta_attn, *gamma_mlp, *beta_mlp;  /* [h]; betas may be NULL */
+    void *out, *out_resid;  /* [P][T][h]: the next block's in and resid */
+    void *workspace;        /* caat_block_workspace_bytes of it */
+    size_t workspace_bytes;
+    void *stream;
+} caat_block_args;
+
+/* Bytes of block workspace (QKV, V^T, head outputs and the out-projection sublayer's
+ * outputs), 0 if the handles do not form a block: attn must be a CAAT_NONE handle and
+ * mlp an MLP handle with the same h, P and norm, both CAAT_BF16, and h/P must split into
+ * nh heads of width 64 or 128. */
+size_t caat_block_workspace_bytes(caat_handle attn, caat_handle mlp, int nh, int T);
+
+/* One block: QKV projection, attention, out-projection sublayer (residual = resid), MLP
+ * sublayer.  The two handles' own workspaces (caat_set_workspace) must also be set for
+ * T tokens. */
+int caat_block_forward(caat_handle attn, caat_handle mlp, int nh, const caat_block_args *args);
+
 /* Static text for a caat_status. */
 const char *caat_error_string(int code);
 

@@ -53,6 +53,17 @@ class caat_bwd_args(ctypes.Structure):
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int)]
 
 
+class caat_block_args(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("S", ctypes.c_int), ("in_", ctypes.c_void_p),
+                ("resid", ctypes.c_void_p), ("Wqkv", ctypes.c_void_p), ("Wo", ctypes.c_void_p),
+                ("W1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("gamma_attn", ctypes.c_void_p), ("beta_attn", ctypes.c_void_p),
+                ("gamma_mlp", ctypes.c_void_p), ("beta_mlp", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("out_resid", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stream", ctypes.c_void_p)]
+
+
 BWD_STEPS = ("norm", "W2T", "dY", "a", "act", "W1T", "dx", "daT_xT", "dW1", "YT_dZtT", "dW2")
 
 
@@ -85,13 +96,20 @@ def lib():
         L.caat_backward_workspace_bytes.restype = sz
         L.caat_backward.argtypes = [vp, ctypes.POINTER(caat_bwd_args)]
         L.caat_partial_sync_norm_backward.argtypes = [vp, i] + [vp] * 9 + [sz, vp]
+        L.caat_attention_workspace_bytes.argtypes = [i, i, i, i]
+        L.caat_attention_workspace_bytes.restype = sz
+        L.caat_attention.argtypes = [i, i, i, i, i, vp, vp, vp, sz, vp]
+        L.caat_block_workspace_bytes.argtypes = [vp, vp, i, i]
+        L.caat_block_workspace_bytes.restype = sz
+        L.caat_block_forward.argtypes = [vp, vp, i, ctypes.POINTER(caat_block_args)]
         L.caat_error_string.argtypes = [i]
         L.caat_error_string.restype = ctypes.c_char_p
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
                      "caat_forward_ex", "caat_column_gemm_act", "caat_row_gemm",
                      "caat_partial_sync_norm", "caat_row_gemm_reduce", "caat_sync_norm",
-                     "caat_backward", "caat_partial_sync_norm_backward"):
+                     "caat_backward", "caat_partial_sync_norm_backward", "caat_attention",
+                     "caat_block_forward"):
             getattr(L, name).restype = i
         _lib = L
     return _lib
@@ -236,6 +254,30 @@ def caat_partial_sync_norm_backward(handle, T, out_resid, dout, dres, gamma, dpa
         "caat_partial_sync_norm_backward")
 
 
+def caat_attention_workspace_bytes(P, T, nh, d) -> int:
+    return int(lib().caat_attention_workspace_bytes(int(P), int(T), int(nh), int(d)))
+
+
+def caat_attention(P, T, S, nh, d, qkv, H, workspace, stream=None):
+    return _check(lib().caat_attention(int(P), int(T), int(S), int(nh), int(d), _ptr(qkv), _ptr(H),
+                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)), "caat_attention")
+
+
+def caat_block_workspace_bytes(attn, mlp, nh, T) -> int:
+    return int(lib().caat_block_workspace_bytes(attn, mlp, int(nh), int(T)))
+
+
+def caat_block_forward(attn, mlp, nh, T, S, inp, resid, Wqkv, Wo, W1, W2, gamma_attn, gamma_mlp,
+                       out, out_resid, workspace, beta_attn=None, beta_mlp=None, stream=None):
+    a = caat_block_args(int(T), int(S), _ptr(inp), _ptr(resid), _ptr(Wqkv), _ptr(Wo), _ptr(W1),
+                        _ptr(W2), _ptr(gamma_attn), _ptr(beta_attn), _ptr(gamma_mlp),
+                        _ptr(beta_mlp), _ptr(out), _ptr(out_resid), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(stream))
+    return _check(lib().caat_block_forward(attn, mlp, int(nh), ctypes.byref(a)),
+                  "caat_block_forward")
+
+
 class Sublayer:
     """One sublayer handle plus a torch-allocated workspace; checks tensor shapes and
     dtypes, then calls the C entry points (no arithmetic here)."""
@@ -327,3 +369,31 @@ class Sublayer:
         return caat_backward(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
                              out_resid, dout, din, dW2, dgamma, self._bws, dW1=dW1, dres=dres,
                              dresid=dresid, dbeta=dbeta, stream=stream, events=events)
+
+
+class Block:
+    """One transformer block with partially synchronized activations (QKV projection,
+    attention core, out-projection sublayer, MLP sublayer), every rank on this device:
+    two Sublayer handles plus the block workspace, then caat_block_forward."""
+
+    def __init__(self, h, ffn, P, p, heads_per_rank, norm="rmsnorm", act="swiglu", eps=1e-5,
+                 s_priv=1.0):
+        self.attn = Sublayer(h, 0, P, p, norm=norm, act="none", dtype="bf16", eps=eps,
+                             s_priv=s_priv)
+        self.mlp = Sublayer(h, ffn, P, p, norm=norm, act=act, dtype="bf16", eps=eps, s_priv=s_priv)
+        self.h, self.P, self.nh = int(h), int(P), int(heads_per_rank)
+        self._ws = None
+
+    def forward(self, T, S, inp, resid, Wqkv, Wo, W1, W2, gamma_attn, gamma_mlp, out, out_resid,
+                beta_attn=None, beta_mlp=None, stream=None):
+        import torch
+        nbytes = caat_block_workspace_bytes(self.attn.handle, self.mlp.handle, self.nh, T)
+        if nbytes == 0:
+            raise ValueError("these handles and head count do not form a block")
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=inp.device)
+        self.attn.workspace(T, inp.device)
+        self.mlp.workspace(T, inp.device)
+        return caat_block_forward(self.attn.handle, self.mlp.handle, self.nh, T, S, inp, resid,
+                                  Wqkv, Wo, W1, W2, gamma_attn, gamma_mlp, out, out_resid,
+                                  self._ws, beta_attn=beta_attn, beta_mlp=beta_mlp, stream=stream)

@@ -1,0 +1,226 @@
+// Attention core of the full block: causal softmax attention of every head of every
+// rank, bf16 in and out, fp32 scores and accumulation.
+//
+// "Tensor-Parallelism with Partially Synchronized Activations", App. A.1 Eq. 16 / 18 and
+// App. A.2 Eq. 24: rank m computes its heads' outputs H_m = Attention(X_m W^Q_m,
+// X_m W^K_m, X_m W^V_m) from its own input X_m; with partially synchronized
+// activations the inputs differ per rank, and all ranks run on this device (§3.2).
+//
+// One workgroup (4 waves) takes 128 queries of one head of one rank; each wave holds 32
+// queries' Q fragments in registers for the whole key loop.  Keys come in blocks of 64
+// through two LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys], both filled by
+// buffer loads that write LDS directly, 16-byte chunks XOR-swizzled by row).  Per block:
+//   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, keys as rows, queries as columns), so
+//                   each lane's accumulators hold one query's scores for 16 keys and the
+//                   row statistics of the online softmax need only the lane pair l, l^32;
+//   scale by log2(e)/sqrt(d), mask keys past the query or past the sequence, update the
+//   running max and sum, rescale the output accumulators;
+//   O^T += V^T P^T  with P^T taken straight from the S^T accumulators (bf16) as the
+//                   column operand: lane l's 8 values of a 16-key chunk are keys
+//                   4g..4g+3 and 8+4g..8+4g+3 (g = l / 32), and the V^T fragments are read
+//                   in the same key order (two 8-byte LDS reads), which sums the same
+//                   products in another order.
+// The last queries of a sequence and keys past it read as zero (buffer range checks)
+// and are masked; sequences never see each other.
+#include "caat_internal.h"
+
+#if defined(__HIP_DEVICE_COMPILE__)
+#define CAAT_UNROLL _Pragma("unroll")
+#else
+#define CAAT_UNROLL
+#endif
+
+namespace caat {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr uint32_t OOB = 0x80000000u;
+constexpr int RSRC_WORD3 = 0x00020000;
+constexpr int BQ = 128, BKV = 64;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             RSRC_WORD3);
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
+{
+    constexpr int CK = D / 8;                 // 16-byte chunks per K row
+    constexpr int KSLOTS = BKV * CK;          // K tile, 16-byte slots
+    constexpr int VSLOTS = D * (BKV / 8);     // V^T tile: d rows of 8 chunks
+    constexpr int KLOADS = KSLOTS / 256, VLOADS = VSLOTS / 256;
+    constexpr int NKK = D / 16;               // MFMA steps over d for the scores
+    constexpr int NDB = D / 32;               // 32-row blocks of O^T
+    static_assert(KSLOTS % 256 == 0 && VSLOTS % 256 == 0, "tiles must split over 256 lanes");
+    __shared__ __attribute__((aligned(16))) uint4 K0[KSLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 K1[KSLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 V0[VSLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 V1[VSLOTS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qb = nqb - 1 - (int)(blockIdx.x % nqb);     // longest key ranges first
+    const int sq = blockIdx.x / nqb;
+    const int hd = blockIdx.y, m = blockIdx.z;
+    const int T = a.T, S = a.S, nh = a.nh, Tp = a.Tp;
+    const int ld = 3 * nh * D;
+    const int seq0 = sq * S, ql0 = qb * BQ;
+
+    const __bf16 *QKV = reinterpret_cast<const __bf16 *>(a.qkv) + (size_t)m * T * ld;
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(QKV, (uint32_t)((size_t)T * ld * 2u));
+    const __bf16 *VT = reinterpret_cast<const __bf16 *>(a.vt) + ((size_t)m * nh + hd) * D * Tp;
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(VT, (uint32_t)((size_t)D * Tp * 2u));
+
+    // Q fragments (column operand of S^T): query ql, d values 16 kk + 8 (lane / 32) ...
+    const int ql = ql0 + wave * 32 + (lane & 31);
+    const int g = lane >> 5;
+    bf16x8 qf[NKK];
+    {
+        const uint32_t qoff = (uint32_t)(((size_t)(seq0 + ql) * ld + (size_t)hd * D + 8 * g) * 2u);
+        CAAT_UNROLL for (int kk = 0; kk < NKK; ++kk)
+            qf[kk] = load16(rQ, ql < S ? qoff + kk * 32u : OOB);
+    }
+
+    // Tile loads: load i of a wave writes the 64 slots from (i * 256 + 64 wave) on, lane
+    // by lane, so slot s = i * 256 + tid holds the global chunk (s % rowchunks) ^ f(row).
+    uint32_t koff[KLOADS];
+    int krow[KLOADS];
+    CAAT_UNROLL for (int i = 0; i < KLOADS; ++i) {
+        const int s = i * 256 + tid, r = s / CK, c = (s % CK) ^ (r & (CK - 1));
+        krow[i] = r;
+        koff[i] = (uint32_t)(((size_t)(seq0 + r) * ld + (size_t)(nh + hd) * D + c * 8) * 2u);
+    }
+    uint32_t voff[VLOADS];
+    int vkey[VLOADS];
+    CAAT_UNROLL for (int i = 0; i < VLOADS; ++i) {
+        const int s = i * 256 + tid, dr = s / 8, c = (s % 8) ^ (dr & 7);
+        vkey[i] = c * 8;
+        voff[i] = (uint32_t)(((size_t)dr * Tp + seq0 + c * 8) * 2u);
+    }
+    const __amdgpu_buffer_rsrc_t rK = rQ;
+#define CAAT_ISSUE(kv0, Kb, Vb)                                                            \
+    do {                                                                                   \
+        CAAT_UNROLL for (int i = 0; i < KLOADS; ++i)                                       \
+            load_lds16(rK, (Kb) + i * 256 + wave * 64,                                     \
+                       ((kv0) + krow[i] < S) ? koff[i] + (uint32_t)((kv0) * ld * 2) : OOB);\
+        CAAT_UNROLL for (int i = 0; i < VLOADS; ++i)                                       \
+            load_lds16(rV, (Vb) + i * 256 + wave * 64,                                     \
+                       ((kv0) + vkey[i] < S) ? voff[i] + (uint32_t)((kv0) * 2) : OOB);     \
+    } while (0)
+
+    f32x16 acc_o[NDB];
+    CAAT_UNROLL for (int b = 0; b < NDB; ++b)
+        CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sc = 1.44269504088896341f / sqrtf((float)D);
+
+    // One key block on the stage (Kb, Vb).
+#define CAAT_BLOCK(kv0, Kb, Vb)                                                            \
+    do {                                                                                   \
+        f32x16 acc_s[2];                                                                   \
+        CAAT_UNROLL for (int kb = 0; kb < 2; ++kb) {                                       \
+            CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_s[kb][v] = 0.f;                   \
+            const int r = kb * 32 + (lane & 31);                                           \
+            CAAT_UNROLL for (int kk = 0; kk < NKK; ++kk) {                                 \
+                const int c = (2 * kk + g) ^ (r & (CK - 1));                               \
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, (Kb)[r * CK + c]);            \
+                acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], \
+                                                                    0, 0, 0);              \
+            }                                                                              \
+        }                                                                                  \
+        float mb = -INFINITY;                                                              \
+        CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
+            CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
+                const int key = (kv0) + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);          \
+                const float sv = (key > ql || key >= S) ? -INFINITY : acc_s[kb][v] * sc;   \
+                acc_s[kb][v] = sv;                                                         \
+                mb = fmaxf(mb, sv);                                                        \
+            }                                                                              \
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));                                            \
+        const float m_new = fmaxf(m_run, mb);                                              \
+        const float alpha = exp2f(m_run - m_new);                                          \
+        float ls = 0.f;                                                                    \
+        bf16x8 pf[4];                                                                      \
+        CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
+            CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
+                const float p = exp2f(acc_s[kb][v] - m_new);                               \
+                ls += p;                                                                   \
+                pf[kb * 2 + (v >> 3)][v & 7] = static_cast<__bf16>(p);                     \
+            }                                                                              \
+        ls += __shfl_xor(ls, 32, 64);                                                      \
+        l_run = alpha * l_run + ls;                                                        \
+        m_run = m_new;                                                                     \
+        CAAT_UNROLL for (int b = 0; b < NDB; ++b)                                          \
+            CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;                 \
+        CAAT_UNROLL for (int b = 0; b < NDB; ++b) {                                        \
+            const int dr = b * 32 + (lane & 31);                                           \
+            const char *vrow = reinterpret_cast<const char *>((Vb) + dr * 8);              \
+            CAAT_UNROLL for (int kc = 0; kc < 4; ++kc) {                                   \
+                const uint2 lo = *reinterpret_cast<const uint2 *>(                         \
+                    vrow + ((2 * kc) ^ (dr & 7)) * 16 + 8 * g);                            \
+                const uint2 hi = *reinterpret_cast<const uint2 *>(                         \
+                    vrow + ((2 * kc + 1) ^ (dr & 7)) * 16 + 8 * g);                        \
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)); \
+                acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[b],   \
+                                                                   0, 0, 0);               \
+            }                                                                              \
+        }                                                                                  \
+    } while (0)
+
+    const int kv_end = min(S, ql0 + BQ);
+    const int nkv = (kv_end + BKV - 1) / BKV;
+    CAAT_ISSUE(0, K0, V0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    int j = 0;
+    for (; j + 2 <= nkv; j += 2) {
+        CAAT_ISSUE((j + 1) * BKV, K1, V1);
+        CAAT_BLOCK(j * BKV, K0, V0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 2 < nkv) CAAT_ISSUE((j + 2) * BKV, K0, V0);
+        CAAT_BLOCK((j + 1) * BKV, K1, V1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    if (j < nkv) CAAT_BLOCK(j * BKV, K0, V0);
+#undef CAAT_ISSUE
+#undef CAAT_BLOCK
+
+    if (ql >= S) return;
+    const float inv = 1.0f / l_run;
+    __bf16 *Hrow = reinterpret_cast<__bf16 *>(a.H) + ((size_t)m * T + seq0 + ql) * nh * D +
+                   (size_t)hd * D;
+    // Accumulator element v of block b in lane l is d = 32 b + 8 (v / 4) + 4 (l / 32) + v % 4.
+    CAAT_UNROLL for (int b = 0; b < NDB; ++b)
+        CAAT_UNROLL for (int q4 = 0; q4 < 4; ++q4) {
+            bf16x4 o;
+            CAAT_UNROLL for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(acc_o[b][4 * q4 + e] * inv);
+            *reinterpret_cast<bf16x4 *>(Hrow + b * 32 + 8 * q4 + 4 * g) = o;
+        }
+}
+
+}  // namespace
+
+hipError_t attention_bf16(const AttnArgs &a, hipStream_t s) {
+    const int nqb = (a.S + BQ - 1) / BQ;
+    const dim3 grid(nqb * (a.T / a.S), a.nh, a.P), block(256);
+    if (a.d == 128)
+        hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a, nqb);
+    else
+        hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a, nqb);
+    return hipGetLastError();
+}
+
+}  // namespace caat

@@ -276,12 +276,12 @@ __global__ __launch_bounds__(256) void k_colsum(const float *__restrict__ part, 
 // stores 8 consecutive elements of a destination row, gathered from 8 LDS rows.
 template <typename TIO>
 __global__ __launch_bounds__(256) void k_transpose(const TIO *__restrict__ src, TIO *__restrict__ dst,
-                                                   int R, int C, int Rp)
+                                                   int R, int C, int Rp, int pitch, size_t bstride)
 {
     __shared__ float tile[64][65];
     const int b = blockIdx.z;
     const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-    const TIO *S = src + (size_t)b * R * C;
+    const TIO *S = src + (size_t)b * bstride;
     TIO *D = dst + (size_t)b * C * Rp;
     // Load: 64 rows x 8 chunks of 8 elements; thread i takes chunk i % 8 of rows i / 8
     // and i / 8 + 32.
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void k_transpose(const TIO *__restrict__ src, 
         const int r = rr + 32 * i, gr = r0 + r, gc = c0 + ck * 8;
         float v[8];
         if (gr < R && gc < C) {
-            Vec8<TIO>::load(S + (size_t)gr * C + gc, v);
+            Vec8<TIO>::load(S + (size_t)gr * pitch + gc, v);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = 0.f;
@@ -420,15 +420,20 @@ hipError_t colsum_f32(const float *part, int rows, int h, float *out, hipStream_
 
 hipError_t transpose(const void *src, void *dst, int B, int R, int C, int Rp, int dtype,
                      hipStream_t s) {
+    return transpose_strided(src, dst, B, R, C, Rp, C, (size_t)R * C, dtype, s);
+}
+
+hipError_t transpose_strided(const void *src, void *dst, int B, int R, int C, int Rp, int pitch,
+                             size_t bstride, int dtype, hipStream_t s) {
     const dim3 grid((C + 63) / 64, (Rp + 63) / 64, B), block(256);
     if (dtype == CAAT_BF16)
         hipLaunchKernelGGL(k_transpose<__bf16>, grid, block, 0, s,
                            reinterpret_cast<const __bf16 *>(src), reinterpret_cast<__bf16 *>(dst),
-                           R, C, Rp);
+                           R, C, Rp, pitch, bstride);
     else
         hipLaunchKernelGGL(k_transpose<float>, grid, block, 0, s,
                            reinterpret_cast<const float *>(src), reinterpret_cast<float *>(dst),
-                           R, C, Rp);
+                           R, C, Rp, pitch, bstride);
     return hipGetLastError();
 }
 

@@ -541,6 +541,136 @@ CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
     return CAAT_OK;
 }
 
+// ---------------------------------------------------------------------------------
+// The full block with logical devices: QKV projection, attention core, the out-projection
+// sublayer and the MLP sublayer (App. A Eq. 16 / 18 / 24, Eq. 22; §3.2; §4 Eq. 9).
+
+namespace {
+
+bool attn_shape_ok(int P, int T, int S, int nh, int d) {
+    if (P < 1 || P > 16 || T < 1 || S < 1 || nh < 1 || (d != 64 && d != 128)) return false;
+    if (T % S != 0 || S % 8 != 0) return false;
+    // 32-bit byte offsets inside one rank's QKV rows and V^T rows.
+    return (uint64_t)T * 3 * nh * d * 2 < 0x80000000ull &&
+           (uint64_t)d * round8(T) * 2 < 0x80000000ull;
+}
+
+size_t attn_ws_bytes(int P, int T, int nh, int d) {
+    return align256((size_t)P * nh * d * round8(T) * 2);
+}
+
+int run_attention(int P, int T, int S, int nh, int d, const void *qkv, void *H, void *vt,
+                  hipStream_t s) {
+    const int hp = nh * d, Tp = (int)round8(T);
+    // V^T [P][nh d][Tp] from the V columns of qkv (rows 3 hp apart).
+    if (caat::transpose_strided(reinterpret_cast<const char *>(qkv) + (size_t)2 * hp * 2, vt, P, T,
+                                hp, Tp, 3 * hp, (size_t)T * 3 * hp, CAAT_BF16, s) != hipSuccess)
+        return CAAT_EDEVICE;
+    caat::AttnArgs a{};
+    a.P = P; a.T = T; a.S = S; a.nh = nh; a.d = d;
+    a.qkv = qkv; a.vt = vt; a.Tp = Tp; a.H = H;
+    return caat::attention_bf16(a, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
+}
+
+struct BlockLayout { size_t qkv, vt, H, a_out, a_res, total; };
+
+BlockLayout block_layout(const caat_ctx *attn, int nh, int T) {
+    BlockLayout L{};
+    const size_t P = attn->P, h = attn->h, hp = h / P, d = hp / nh;
+    size_t off = 0;
+    auto take = [&](size_t n) { const size_t o = off; off += align256(n); return o; };
+    L.qkv = take(P * T * 3 * hp * 2);
+    L.vt = take(attn_ws_bytes((int)P, T, nh, (int)d));
+    L.H = take(P * T * hp * 2);
+    L.a_out = take(P * T * h * 2);
+    L.a_res = take(P * T * h * 2);
+    L.total = off;
+    return L;
+}
+
+int block_check(const caat_ctx *attn, const caat_ctx *mlp, int nh) {
+    if (attn == nullptr || mlp == nullptr) return CAAT_EINVAL;
+    if (attn->act != CAAT_NONE || mlp->act == CAAT_NONE) return CAAT_EINVAL;
+    if (attn->h != mlp->h || attn->P != mlp->P || attn->norm != mlp->norm) return CAAT_EINVAL;
+    if (attn->dtype != CAAT_BF16 || mlp->dtype != CAAT_BF16) return CAAT_EUNSUPPORTED;
+    if (nh < 1 || attn->kin % nh != 0) return CAAT_EINVAL;
+    const int d = attn->kin / nh;
+    if (d != 64 && d != 128) return CAAT_EUNSUPPORTED;
+    return CAAT_OK;
+}
+
+}  // namespace
+
+CAAT_API size_t caat_attention_workspace_bytes(int P, int T, int nh, int d) {
+    if (P < 1 || T < 1 || nh < 1 || d < 1) return 0;
+    return attn_ws_bytes(P, T, nh, d);
+}
+
+CAAT_API int caat_attention(int P, int T, int S, int nh, int d, const void *qkv, void *H,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (!aligned16(qkv) || !aligned16(H)) return CAAT_EINVAL;
+    if (P < 1 || T < 1 || S < 1 || nh < 1) return CAAT_EINVAL;
+    if (T % S != 0 || S % 8 != 0) return CAAT_EINVAL;
+    if (!attn_shape_ok(P, T, S, nh, d)) return CAAT_EUNSUPPORTED;
+    if (!aligned16(workspace) || workspace_bytes < attn_ws_bytes(P, T, nh, d))
+        return CAAT_EWORKSPACE;
+    const int rc = device_check();
+    if (rc != CAAT_OK) return rc;
+    return run_attention(P, T, S, nh, d, qkv, H, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+CAAT_API size_t caat_block_workspace_bytes(caat_handle attn, caat_handle mlp, int nh, int T) {
+    if (T < 1 || block_check(attn, mlp, nh) != CAAT_OK) return 0;
+    return block_layout(attn, nh, T).total;
+}
+
+CAAT_API int caat_block_forward(caat_handle attn, caat_handle mlp, int nh, const caat_block_args *a) {
+    if (a == nullptr) return CAAT_EINVAL;
+    int rc = block_check(attn, mlp, nh);
+    if (rc != CAAT_OK) return rc;
+    const int T = a->T, S = a->S, P = attn->P, h = attn->h, hp = attn->kin, d = hp / nh;
+    if (T < 1 || S < 1 || T % S != 0 || S % 8 != 0) return CAAT_EINVAL;
+    if (!aligned16(a->in) || !aligned16(a->resid) || !aligned16(a->Wqkv) || !aligned16(a->Wo) ||
+        !aligned16(a->W1) || !aligned16(a->W2) || !aligned16(a->gamma_attn) ||
+        !aligned16(a->gamma_mlp) || !aligned16(a->out) || !aligned16(a->out_resid))
+        return CAAT_EINVAL;
+    if (!aligned16_or_null(a->beta_attn) || !aligned16_or_null(a->beta_mlp)) return CAAT_EINVAL;
+    if (!attn_shape_ok(P, T, S, nh, d) || !t_ok(attn, T) || !t_ok(mlp, T)) return CAAT_EUNSUPPORTED;
+    const BlockLayout L = block_layout(attn, nh, T);
+    if (!aligned16(a->workspace) || a->workspace_bytes < L.total) return CAAT_EWORKSPACE;
+    if (attn->ws == nullptr || attn->ws_bytes < caat_workspace_bytes(attn, T) ||
+        mlp->ws == nullptr || mlp->ws_bytes < caat_workspace_bytes(mlp, T))
+        return CAAT_EWORKSPACE;
+    rc = device_check();
+    if (rc != CAAT_OK) return rc;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(a->stream);
+    char *ws = reinterpret_cast<char *>(a->workspace);
+    // QKV projection per rank (column-parallel: the rank's heads), then attention.
+    caat::GemmArgs g{};
+    g.P = P; g.N = 3 * hp; g.T = T; g.K = h;
+    g.W = a->Wqkv; g.w_stride = (size_t)3 * hp * h;
+    g.X = a->in; g.x_stride = (size_t)T * h;
+    g.out = ws + L.qkv; g.o_stride = (size_t)T * 3 * hp; g.ldo = 3 * hp;
+    g.epi = caat::EPI_STORE; g.kseg = 1;
+    rc = run_gemm(attn, g, s);
+    if (rc != CAAT_OK) return rc;
+    rc = run_attention(P, T, S, nh, d, ws + L.qkv, ws + L.H, ws + L.vt, s);
+    if (rc != CAAT_OK) return rc;
+    // The two sublayers, through the handles' own workspaces.
+    caat_args sa{};
+    sa.T = T; sa.in = ws + L.H; sa.resid = a->resid; sa.W1 = nullptr; sa.W2 = a->Wo;
+    sa.gamma = a->gamma_attn; sa.beta = a->beta_attn; sa.out = ws + L.a_out;
+    sa.out_resid = ws + L.a_res; sa.stream = a->stream;
+    rc = caat_forward_ex(attn, &sa);
+    if (rc != CAAT_OK) return rc;
+    caat_args sm{};
+    sm.T = T; sm.in = ws + L.a_out; sm.resid = ws + L.a_res; sm.W1 = a->W1; sm.W2 = a->W2;
+    sm.gamma = a->gamma_mlp; sm.beta = a->beta_mlp; sm.out = a->out; sm.out_resid = a->out_resid;
+    sm.stream = a->stream;
+    return caat_forward_ex(mlp, &sm);
+}
+
 CAAT_API const char *caat_error_string(int code) {
     switch (code) {
     case CAAT_OK: return "success";

@@ -97,6 +97,10 @@ hipError_t colsum_f32(const float *part, int rows, int h, float *out, hipStream_
 // dst[b][c][r] = src[b][r][c] for r < R, 0 for R <= r < Rp (Rp % 8 == 0, Rp >= R).
 hipError_t transpose(const void *src, void *dst, int B, int R, int C, int Rp, int dtype,
                      hipStream_t s);
+// The same for source rows `pitch` elements apart and batches `bstride` elements apart
+// (pitch % 8 == 0): dst[b][c][r] = src[b * bstride + r * pitch + c].
+hipError_t transpose_strided(const void *src, void *dst, int B, int R, int C, int Rp, int pitch,
+                             size_t bstride, int dtype, hipStream_t s);
 // Activation backward over rows of the pre-activation A [rows][F1]:
 //   da = dY * sigma'(A) ([rows][F1]; SwiGLU: gate and up halves), Y = sigma(A)
 //   ([rows][fs]).
@@ -105,4 +109,17 @@ hipError_t act_backward(int act, int dtype, size_t rows, int fs, const void *A, 
 // dst[i] += src[i], n % 8 == 0.
 hipError_t add_inplace(void *dst, const void *src, size_t n, int dtype, hipStream_t s);
 
+}  // namespace caat
+
+// ---------------------------------------------------------------------------------
+// Attention core of the full block (bf16): causal softmax attention per head.
+namespace caat {
+struct AttnArgs {
+    int P, T, S, nh, d;     // ranks, tokens, sequence length (T % S == 0), heads per rank, width
+    const void *qkv;        // [P][T][3 nh d]: Q, K, V of the rank's heads
+    const void *vt;         // [P][nh][d][Tp]: V transposed, Tp = T rounded up to 8
+    int Tp;
+    void *H;                // [P][T][nh d]
+};
+hipError_t attention_bf16(const AttnArgs &a, hipStream_t s);
 }  // namespace caat

@@ -16,6 +16,8 @@ BASE_SEED = 20250624
 X, W1, W2, CTX, WO, X0, GAMMA, BETA, PARTIALS, RESID = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 # Upstream gradients for the backward: dL/d out and dL/d out_resid.
 DOUT, DRES = 11, 12
+# The full block: QKV projection weights, and QKV activations for the attention core alone.
+WQKV, QKV = 13, 14
 
 
 def _generator(seed: int, tensor_id: int) -> torch.Generator:
