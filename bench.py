@@ -12,6 +12,10 @@ entry point with an event between consecutive kernels on the stream the library
 launches on, which yields the step time and every kernel's average duration from the
 same timed steps.
 
+With --pass block a step is one full transformer block of a pair workload: the QKV
+projection, the causal attention core and both sublayers (caat_block_forward, which
+records the caller's events after each of its steps).
+
 With --pass backward a step is the backward of the whole path instead (the MLP
 sublayer's backward, then the out-projection sublayer's), through caat_backward; the
 library records the caller's events after each of its steps, so every kernel's
@@ -31,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tokens/sec per CAAT sublayer fwd (1 GPU, P emulated); % MFMA or HBM roofline"
 METRIC_BWD = "tokens/sec per CAAT sublayer bwd (1 GPU, P emulated); % MFMA or HBM roofline"
+METRIC_BLOCK = "tokens/sec per CAAT block fwd (1 GPU, P emulated); % MFMA or HBM roofline"
 PEAK = {"mfma": 2500.0, "hbm": 8000.0}   # MI355X: bf16 dense TFLOP/s, HBM3E GB/s
 DEFAULT_WORKLOAD = "7b-prefill-pair-bf16"
 
@@ -307,6 +312,107 @@ def bench_backward(args, w, T, p):
     print(json.dumps(line), flush=True)
 
 
+def kernel_work_block(w, T, step):
+    """Algorithmic FLOPs and HBM bytes of one step of the full block (BLOCK_STEPS)."""
+    P, h = w.P, w.h
+    hp = h // P
+    nh = w.heads // P
+    d = hp // nh
+    S = w.seq
+    b = 2
+    if step == "qkv":
+        return 2.0 * P * T * h * 3 * hp, b * (P * T * h + P * 3 * hp * h + P * T * 3 * hp)
+    if step == "vT":
+        return 0.0, b * 2 * P * T * hp
+    if step == "attn":
+        pairs = (T // S) * S * (S + 1) // 2          # causal (query, key) pairs per head
+        return 4.0 * P * nh * d * pairs, b * (P * T * 3 * hp + P * T * hp)
+    raise KeyError(step)
+
+
+def bench_block(args, w, T, p):
+    import torch
+    import partial_activation_sync_amd as caat
+    from partial_activation_sync_amd import synth
+
+    if not (w.heads and w.seq) or T % w.seq:
+        print(f"--pass block needs a pair workload with heads and a sequence length dividing T "
+              f"({w.name}: heads={w.heads}, seq={w.seq}, T={T})", flush=True)
+        sys.exit(2)
+    P, h, S = w.P, w.h, w.seq
+    nh, hp = w.heads // P, h // P
+    log(f"[bench] block {w.name} T={T} S={S} P={P} h={h} heads/rank={nh} ffn={w.ffn} p={p}")
+    bf = torch.bfloat16
+    F1 = 2 * w.f_s if w.act == "swiglu" else w.f_s
+    n = lambda shape, tid, **kw: synth.normal(shape, tid, dtype=bf, **kw).cuda()
+    x, r = n((P, T, h), synth.X), n((P, T, h), synth.X0)
+    Wqkv, Wo = n((P, 3 * hp, h), synth.WQKV, std=0.02), n((P, h, hp), synth.WO, std=0.02)
+    W1, W2 = n((P, F1, h), synth.W1, std=0.02), n((P, h, w.f_s), synth.W2, std=0.02)
+    g, beta = torch.ones(h, dtype=bf, device="cuda"), torch.zeros(h, dtype=bf, device="cuda")
+    out, out_r = torch.empty_like(x), torch.empty_like(x)
+    blk = caat.Block(h, w.ffn, P, p, nh, norm=w.norm, act=w.act, eps=w.eps)
+    steps = caat.BLOCK_STEPS
+    K = args.steps
+
+    def events(k):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in ev:
+            e.record()
+        return ev
+
+    start = events(K)
+    ev = [events(len(steps)) for _ in range(K)]
+    torch.cuda.synchronize()
+    step = lambda evs=None: blk.forward(T, S, x, r, Wqkv, Wo, W1, W2, g, g, out, out_r,
+                                        beta_attn=beta, beta_mlp=beta, events=evs)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(K):
+        start[s].record()
+        step([e.cuda_event for e in ev[s]])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    span_ms = start[0].elapsed_time(ev[K - 1][-1]) / K
+    ms = {name: sum((start[s] if i == 0 else ev[s][i - 1]).elapsed_time(ev[s][i])
+                    for s in range(K)) / K for i, name in enumerate(steps)}
+    log(f"[bench] {K} block steps: {span_ms:.4f} ms/step, wall {wall / K * 1e3:.3f} ms/step")
+    detail = {}
+    for name, t in ms.items():
+        d = {"ms": round(t, 4), "share": round(t / span_ms, 3)}
+        if name in ("qkv", "vT", "attn"):
+            flops, nbytes = kernel_work_block(w, T, name)
+            if flops:
+                d["TFLOP/s"] = round(flops / t / 1e9, 1)
+                d["mfma_frac"] = round(flops / t / 1e9 / PEAK["mfma"], 3)
+            d["GB/s"] = round(nbytes / t / 1e6, 1)
+            d["hbm_frac"] = round(nbytes / t / 1e6 / PEAK["hbm"], 3)
+        detail[name] = d
+        log(f"[bench]   {name:14s} {t:8.4f} ms  {d}")
+    # The sublayer steps hold several kernels each (their rooflines are the forward
+    # pass's); the roofline here is the dominant single-kernel step of the block.
+    dom = max(("qkv", "attn"), key=lambda k: ms[k])
+    flops, nbytes = kernel_work_block(w, T, dom)
+    achieved = flops / ms[dom] / 1e9
+    roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK["mfma"],
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma"], 4), "kernel": dom,
+            "algorithmic_per_launch": flops, "traffic": None}
+    line = {
+        "metric": METRIC_BLOCK, "value": round(T / (span_ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(span_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations, N(0,0.02^2) weights",
+        "config": {"workload": w.name, "pass": "block", "P": P, "h": h, "ffn": w.ffn, "T": T,
+                   "seq": S, "heads": w.heads, "p": p, "act": w.act, "norm": w.norm,
+                   "parallelism": f"tp{P} emulated on 1 GPU"},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "kernels": detail,
+    }
+    print(json.dumps(line), flush=True)
+
+
 COPY_BYTES = 512 << 20
 
 
@@ -339,7 +445,7 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as a captured HIP graph (one graph per weight "
                          "copy, replayed); value and ms_per_step then come from the replays")
-    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward", "block"), default="forward",
                     help="time the forward (default) or the backward of the path")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (HBM counter calibration)")
@@ -364,6 +470,8 @@ def main():
     torch.cuda.set_device(0)
     if args.pass_ == "backward":
         return bench_backward(args, w, T, p)
+    if args.pass_ == "block":
+        return bench_block(args, w, T, p)
     log(f"[bench] {w.name} T={T} p={p} P={w.P} h={w.h} ffn={w.ffn} act={w.act} norm={w.norm}")
     t0 = time.perf_counter()
     inputs = runner.make_inputs(w, T=T)

@@ -267,6 +267,10 @@ typedef struct {
     void *workspace;        /* caat_block_workspace_bytes of it */
     size_t workspace_bytes;
     void *stream;
+    void *const *events;    /* NULL, or n_events hipEvent_t recorded after each step:
+                               0 QKV GEMM, 1 V transpose, 2 attention, 3 out-projection
+                               sublayer, 4 MLP sublayer (for timing) */
+    int n_events;
 } caat_block_args;
 
 /* Bytes of block workspace (QKV, V^T, head outputs and the out-projection sublayer's

@@ -61,9 +61,11 @@ class caat_block_args(ctypes.Structure):
                 ("gamma_mlp", ctypes.c_void_p), ("beta_mlp", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("out_resid", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("events", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_events", ctypes.c_int)]
 
 
+BLOCK_STEPS = ("qkv", "vT", "attn", "attn_sublayer", "mlp_sublayer")
 BWD_STEPS = ("norm", "W2T", "dY", "a", "act", "W1T", "dx", "daT_xT", "dW1", "YT_dZtT", "dW2")
 
 
@@ -269,11 +271,16 @@ def caat_block_workspace_bytes(attn, mlp, nh, T) -> int:
 
 
 def caat_block_forward(attn, mlp, nh, T, S, inp, resid, Wqkv, Wo, W1, W2, gamma_attn, gamma_mlp,
-                       out, out_resid, workspace, beta_attn=None, beta_mlp=None, stream=None):
+                       out, out_resid, workspace, beta_attn=None, beta_mlp=None, stream=None,
+                       events=None):
+    """events: None, or raw hipEvent_t handles recorded after each of BLOCK_STEPS."""
+    ev = (ctypes.c_void_p * len(events))(*events) if events is not None else None
     a = caat_block_args(int(T), int(S), _ptr(inp), _ptr(resid), _ptr(Wqkv), _ptr(Wo), _ptr(W1),
                         _ptr(W2), _ptr(gamma_attn), _ptr(beta_attn), _ptr(gamma_mlp),
                         _ptr(beta_mlp), _ptr(out), _ptr(out_resid), _ptr(workspace),
-                        workspace.numel() * workspace.element_size(), _stream(stream))
+                        workspace.numel() * workspace.element_size(), _stream(stream),
+                        ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None,
+                        len(events) if events is not None else 0)
     return _check(lib().caat_block_forward(attn, mlp, int(nh), ctypes.byref(a)),
                   "caat_block_forward")
 
@@ -385,7 +392,7 @@ class Block:
         self._ws = None
 
     def forward(self, T, S, inp, resid, Wqkv, Wo, W1, W2, gamma_attn, gamma_mlp, out, out_resid,
-                beta_attn=None, beta_mlp=None, stream=None):
+                beta_attn=None, beta_mlp=None, stream=None, events=None):
         import torch
         nbytes = caat_block_workspace_bytes(self.attn.handle, self.mlp.handle, self.nh, T)
         if nbytes == 0:
@@ -396,4 +403,5 @@ class Block:
         self.mlp.workspace(T, inp.device)
         return caat_block_forward(self.attn.handle, self.mlp.handle, self.nh, T, S, inp, resid,
                                   Wqkv, Wo, W1, W2, gamma_attn, gamma_mlp, out, out_resid,
-                                  self._ws, beta_attn=beta_attn, beta_mlp=beta_mlp, stream=stream)
+                                  self._ws, beta_attn=beta_attn, beta_mlp=beta_mlp, stream=stream,
+                                  events=events)

@@ -8,8 +8,8 @@
 //
 // One workgroup (4 waves) takes 128 queries of one head of one rank; each wave holds 32
 // queries' Q fragments in registers for the whole key loop.  Keys come in blocks of 64
-// through two LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys], both filled by
-// buffer loads that write LDS directly, 16-byte chunks XOR-swizzled by row).  Per block:
+// through three LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys], both filled by
+// buffer loads that write LDS directly, rows padded by one 16-byte slot).  Per block:
 //   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, keys as rows, queries as columns), so
 //                   each lane's accumulators hold one query's scores for 16 keys and the
 //                   row statistics of the online softmax need only the lane pair l, l^32;
@@ -54,25 +54,38 @@ __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
+__global__ __launch_bounds__(256)
+void k_attn(AttnArgs a, int nqb)
 {
     constexpr int CK = D / 8;                 // 16-byte chunks per K row
-    constexpr int KSLOTS = BKV * CK;          // K tile, 16-byte slots
-    constexpr int VSLOTS = D * (BKV / 8);     // V^T tile: d rows of 8 chunks
-    constexpr int KLOADS = KSLOTS / 256, VLOADS = VSLOTS / 256;
+    constexpr int KROW = CK + 1;              // K row pitch in slots (one slot of padding)
+    constexpr int VROW = BKV / 8 + 1;         // V^T row pitch in slots (8 chunks + padding)
+    constexpr int KLOADS = (BKV * KROW + 255) / 256, VLOADS = (D * VROW + 255) / 256;
+    constexpr int KSLOTS = KLOADS * 256, VSLOTS = VLOADS * 256;
     constexpr int NKK = D / 16;               // MFMA steps over d for the scores
     constexpr int NDB = D / 32;               // 32-row blocks of O^T
-    static_assert(KSLOTS % 256 == 0 && VSLOTS % 256 == 0, "tiles must split over 256 lanes");
     __shared__ __attribute__((aligned(16))) uint4 K0[KSLOTS];
     __shared__ __attribute__((aligned(16))) uint4 K1[KSLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 K2[KSLOTS];
     __shared__ __attribute__((aligned(16))) uint4 V0[VSLOTS];
     __shared__ __attribute__((aligned(16))) uint4 V1[VSLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 V2[VSLOTS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qb = nqb - 1 - (int)(blockIdx.x % nqb);     // longest key ranges first
-    const int sq = blockIdx.x / nqb;
-    const int hd = blockIdx.y, m = blockIdx.z;
+    // Workgroups go round-robin to the 8 XCDs; consecutive tiles, which are the query
+    // blocks of one (rank, head, sequence) and read the same keys and values, are given
+    // to one XCD so that its L2 serves them.  Longest key ranges first.
+    int tile;
+    {
+        const int b = blockIdx.x, total = gridDim.x;
+        const int xcd = b & 7, idx = b >> 3, q = total >> 3, rem = total & 7;
+        tile = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+    }
+    const int nseq = a.T / a.S;
+    const int qb = nqb - 1 - tile % nqb;
+    const int sq = (tile / nqb) % nseq;
+    const int hd = (tile / (nqb * nseq)) % a.nh, m = tile / (nqb * nseq * a.nh);
     const int T = a.T, S = a.S, nh = a.nh, Tp = a.Tp;
     const int ld = 3 * nh * D;
     const int seq0 = sq * S, ql0 = qb * BQ;
@@ -93,20 +106,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
     }
 
     // Tile loads: load i of a wave writes the 64 slots from (i * 256 + 64 wave) on, lane
-    // by lane, so slot s = i * 256 + tid holds the global chunk (s % rowchunks) ^ f(row).
+    // by lane, so slot s = i * 256 + tid holds chunk s % pitch of row s / pitch.  Rows
+    // are padded by one slot (loaded out of range, as zero) so that the fragment reads
+    // of 16 consecutive rows fall in distinct banks while every read of a row is one base
+    // address plus an immediate offset.
     uint32_t koff[KLOADS];
     int krow[KLOADS];
     CAAT_UNROLL for (int i = 0; i < KLOADS; ++i) {
-        const int s = i * 256 + tid, r = s / CK, c = (s % CK) ^ (r & (CK - 1));
-        krow[i] = r;
-        koff[i] = (uint32_t)(((size_t)(seq0 + r) * ld + (size_t)(nh + hd) * D + c * 8) * 2u);
+        const int s = i * 256 + tid, r = s / KROW, c = s % KROW;
+        const bool in = r < BKV && c < CK;
+        krow[i] = in ? r : BKV + S;            // never inside the sequence: always out of range
+        koff[i] = (uint32_t)(((size_t)(seq0 + (in ? r : 0)) * ld + (size_t)(nh + hd) * D +
+                              (in ? c : 0) * 8) * 2u);
     }
     uint32_t voff[VLOADS];
     int vkey[VLOADS];
     CAAT_UNROLL for (int i = 0; i < VLOADS; ++i) {
-        const int s = i * 256 + tid, dr = s / 8, c = (s % 8) ^ (dr & 7);
-        vkey[i] = c * 8;
-        voff[i] = (uint32_t)(((size_t)dr * Tp + seq0 + c * 8) * 2u);
+        const int s = i * 256 + tid, dr = s / VROW, c = s % VROW;
+        const bool in = dr < D && c < BKV / 8;
+        vkey[i] = in ? c * 8 : S;              // padding: out of range
+        voff[i] = (uint32_t)(((size_t)(in ? dr : 0) * Tp + seq0 + (in ? c : 0) * 8) * 2u);
     }
     const __amdgpu_buffer_rsrc_t rK = rQ;
 #define CAAT_ISSUE(kv0, Kb, Vb)                                                            \
@@ -125,16 +144,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
     float m_run = -INFINITY, l_run = 0.f;
     const float sc = 1.44269504088896341f / sqrtf((float)D);
 
-    // One key block on the stage (Kb, Vb).
-#define CAAT_BLOCK(kv0, Kb, Vb)                                                            \
+    // One key block on the stage (Kb, Vb).  MASK: the block holds keys past a query of
+    // the workgroup or past the sequence (the last two blocks); interior blocks skip it.
+#define CAAT_BLOCK(kv0, Kb, Vb, MASK)                                                      \
     do {                                                                                   \
         f32x16 acc_s[2];                                                                   \
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb) {                                       \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_s[kb][v] = 0.f;                   \
-            const int r = kb * 32 + (lane & 31);                                           \
+            const uint4 *krow_ = (Kb) + (kb * 32 + (lane & 31)) * KROW + g;                \
             CAAT_UNROLL for (int kk = 0; kk < NKK; ++kk) {                                 \
-                const int c = (2 * kk + g) ^ (r & (CK - 1));                               \
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, (Kb)[r * CK + c]);            \
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, krow_[2 * kk]);               \
                 acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], \
                                                                     0, 0, 0);              \
             }                                                                              \
@@ -142,35 +161,40 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
         float mb = -INFINITY;                                                              \
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
-                const int key = (kv0) + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);          \
-                const float sv = (key > ql || key >= S) ? -INFINITY : acc_s[kb][v] * sc;   \
+                float sv = acc_s[kb][v] * sc;                                              \
+                if (MASK) {                                                                \
+                    const int key = (kv0) + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);      \
+                    sv = (key > ql || key >= S) ? -INFINITY : sv;                          \
+                }                                                                          \
                 acc_s[kb][v] = sv;                                                         \
                 mb = fmaxf(mb, sv);                                                        \
             }                                                                              \
         mb = fmaxf(mb, __shfl_xor(mb, 32, 64));                                            \
         const float m_new = fmaxf(m_run, mb);                                              \
-        const float alpha = exp2f(m_run - m_new);                                          \
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);                         \
+        /* the output is rescaled only when some query's running max moved */             \
+        const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;               \
         float ls = 0.f;                                                                    \
         bf16x8 pf[4];                                                                      \
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
-                const float p = exp2f(acc_s[kb][v] - m_new);                               \
+                const float p = __builtin_amdgcn_exp2f(acc_s[kb][v] - m_new);              \
                 ls += p;                                                                   \
                 pf[kb * 2 + (v >> 3)][v & 7] = static_cast<__bf16>(p);                     \
             }                                                                              \
         ls += __shfl_xor(ls, 32, 64);                                                      \
         l_run = alpha * l_run + ls;                                                        \
         m_run = m_new;                                                                     \
-        CAAT_UNROLL for (int b = 0; b < NDB; ++b)                                          \
-            CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;                 \
+        if (moved) {                                                                       \
+            CAAT_UNROLL for (int b = 0; b < NDB; ++b)                                      \
+                CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;             \
+        }                                                                                  \
         CAAT_UNROLL for (int b = 0; b < NDB; ++b) {                                        \
-            const int dr = b * 32 + (lane & 31);                                           \
-            const char *vrow = reinterpret_cast<const char *>((Vb) + dr * 8);              \
+            const char *vrow = reinterpret_cast<const char *>(                             \
+                (Vb) + (b * 32 + (lane & 31)) * VROW) + 8 * g;                             \
             CAAT_UNROLL for (int kc = 0; kc < 4; ++kc) {                                   \
-                const uint2 lo = *reinterpret_cast<const uint2 *>(                         \
-                    vrow + ((2 * kc) ^ (dr & 7)) * 16 + 8 * g);                            \
-                const uint2 hi = *reinterpret_cast<const uint2 *>(                         \
-                    vrow + ((2 * kc + 1) ^ (dr & 7)) * 16 + 8 * g);                        \
+                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (2 * kc) * 16);   \
+                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (2 * kc + 1) * 16); \
                 const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)); \
                 acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[b],   \
                                                                    0, 0, 0);               \
@@ -180,21 +204,35 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
 
     const int kv_end = min(S, ql0 + BQ);
     const int nkv = (kv_end + BKV - 1) / BKV;
+    // Blocks whose keys all precede the workgroup's first query need no mask.
+#define CAAT_ANY_BLOCK(kv0, Kb, Vb)                                                        \
+    do {                                                                                   \
+        if ((kv0) + BKV <= ql0) CAAT_BLOCK(kv0, Kb, Vb, false);                            \
+        else CAAT_BLOCK(kv0, Kb, Vb, true);                                                \
+    } while (0)
+    // Three stages: block j's loads are issued at the start of block j - 2.  The loop
+    // runs whole groups of three blocks; loads of a block past the keys fall out of range
+    // (zero) without a branch, and such blocks are fully masked, so they add nothing.
+    // At the end of a block the wait leaves the newest block's loads in flight.
+#define CAAT_STEP3(j, Kc, Vc, Kn, Vn)                                                      \
+    do {                                                                                   \
+        CAAT_ISSUE(((j) + 2) * BKV, Kn, Vn);                                               \
+        CAAT_ANY_BLOCK((j) * BKV, Kc, Vc);                                                 \
+        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KLOADS + VLOADS) : "memory");            \
+        __syncthreads();                                                                   \
+    } while (0)
     CAAT_ISSUE(0, K0, V0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    CAAT_ISSUE(BKV, K1, V1);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KLOADS + VLOADS) : "memory");
     __syncthreads();
-    int j = 0;
-    for (; j + 2 <= nkv; j += 2) {
-        CAAT_ISSUE((j + 1) * BKV, K1, V1);
-        CAAT_BLOCK(j * BKV, K0, V0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (j + 2 < nkv) CAAT_ISSUE((j + 2) * BKV, K0, V0);
-        CAAT_BLOCK((j + 1) * BKV, K1, V1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+    for (int j = 0; j < nkv; j += 3) {
+        CAAT_STEP3(j, K0, V0, K2, V2);
+        CAAT_STEP3(j + 1, K1, V1, K0, V0);
+        CAAT_STEP3(j + 2, K2, V2, K1, V1);
     }
-    if (j < nkv) CAAT_BLOCK(j * BKV, K0, V0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef CAAT_STEP3
+#undef CAAT_ANY_BLOCK
 #undef CAAT_ISSUE
 #undef CAAT_BLOCK
 
@@ -215,7 +253,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nqb)
 
 hipError_t attention_bf16(const AttnArgs &a, hipStream_t s) {
     const int nqb = (a.S + BQ - 1) / BQ;
-    const dim3 grid(nqb * (a.T / a.S), a.nh, a.P), block(256);
+    const dim3 grid(nqb * (a.T / a.S) * a.nh * a.P), block(256);
     if (a.d == 128)
         hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a, nqb);
     else

@@ -560,11 +560,14 @@ size_t attn_ws_bytes(int P, int T, int nh, int d) {
 }
 
 int run_attention(int P, int T, int S, int nh, int d, const void *qkv, void *H, void *vt,
-                  hipStream_t s) {
+                  hipStream_t s, void *mid_event = nullptr) {
     const int hp = nh * d, Tp = (int)round8(T);
     // V^T [P][nh d][Tp] from the V columns of qkv (rows 3 hp apart).
     if (caat::transpose_strided(reinterpret_cast<const char *>(qkv) + (size_t)2 * hp * 2, vt, P, T,
                                 hp, Tp, 3 * hp, (size_t)T * 3 * hp, CAAT_BF16, s) != hipSuccess)
+        return CAAT_EDEVICE;
+    if (mid_event != nullptr &&
+        hipEventRecord(reinterpret_cast<hipEvent_t>(mid_event), s) != hipSuccess)
         return CAAT_EDEVICE;
     caat::AttnArgs a{};
     a.P = P; a.T = T; a.S = S; a.nh = nh; a.d = d;
@@ -653,9 +656,19 @@ CAAT_API int caat_block_forward(caat_handle attn, caat_handle mlp, int nh, const
     g.X = a->in; g.x_stride = (size_t)T * h;
     g.out = ws + L.qkv; g.o_stride = (size_t)T * 3 * hp; g.ldo = 3 * hp;
     g.epi = caat::EPI_STORE; g.kseg = 1;
+    auto ev = [&](int k) -> void * {
+        return (a->events != nullptr && k < a->n_events) ? a->events[k] : nullptr;
+    };
+    auto mark = [&](int k) -> int {
+        return (ev(k) == nullptr ||
+                hipEventRecord(reinterpret_cast<hipEvent_t>(ev(k)), s) == hipSuccess)
+                   ? CAAT_OK : CAAT_EDEVICE;
+    };
     rc = run_gemm(attn, g, s);
+    if (rc == CAAT_OK) rc = mark(0);
     if (rc != CAAT_OK) return rc;
-    rc = run_attention(P, T, S, nh, d, ws + L.qkv, ws + L.H, ws + L.vt, s);
+    rc = run_attention(P, T, S, nh, d, ws + L.qkv, ws + L.H, ws + L.vt, s, ev(1));
+    if (rc == CAAT_OK) rc = mark(2);
     if (rc != CAAT_OK) return rc;
     // The two sublayers, through the handles' own workspaces.
     caat_args sa{};
@@ -663,12 +676,15 @@ CAAT_API int caat_block_forward(caat_handle attn, caat_handle mlp, int nh, const
     sa.gamma = a->gamma_attn; sa.beta = a->beta_attn; sa.out = ws + L.a_out;
     sa.out_resid = ws + L.a_res; sa.stream = a->stream;
     rc = caat_forward_ex(attn, &sa);
+    if (rc == CAAT_OK) rc = mark(3);
     if (rc != CAAT_OK) return rc;
     caat_args sm{};
     sm.T = T; sm.in = ws + L.a_out; sm.resid = ws + L.a_res; sm.W1 = a->W1; sm.W2 = a->W2;
     sm.gamma = a->gamma_mlp; sm.beta = a->beta_mlp; sm.out = a->out; sm.out_resid = a->out_resid;
     sm.stream = a->stream;
-    return caat_forward_ex(mlp, &sm);
+    rc = caat_forward_ex(mlp, &sm);
+    if (rc == CAAT_OK) rc = mark(4);
+    return rc;
 }
 
 CAAT_API const char *caat_error_string(int code) {

@@ -26,7 +26,8 @@ class Workload:
     sublayers: Tuple[str, ...]      # (MLP,) or (ATTN_OUT, MLP)
     eps: float = 1e-5
     replicated_x: bool = False      # the MLP input is one draw copied to every rank
-    heads: int = 0                  # informational: the out-projection does not use it
+    heads: int = 0                  # attention heads (all ranks); the full block splits them
+    seq: int = 0                    # sequence length: T = (T / seq) sequences (full block)
     note: str = ""
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
@@ -42,7 +43,7 @@ TINY_MLP_F32 = Workload(
 
 PAIR_130M_BF16 = Workload(
     "130m-pair-bf16", "bf16", P=4, h=768, ffn=3072, T=4096, p=0.5, act="gelu",
-    norm="layernorm", sublayers=(ATTN_OUT, MLP), heads=12,
+    norm="layernorm", sublayers=(ATTN_OUT, MLP), heads=12, seq=2048,
     note="h=768, ffn=3072, P=4, T=4096 (2 x 2048); out-projection then MLP")
 
 MLP_1P1B_BF16 = Workload(
@@ -52,7 +53,7 @@ MLP_1P1B_BF16 = Workload(
 
 PREFILL_7B_BF16 = Workload(
     "7b-prefill-pair-bf16", "bf16", P=8, h=4096, ffn=11008, T=8192, p=0.5, act="swiglu",
-    norm="rmsnorm", sublayers=(ATTN_OUT, MLP), heads=32,
+    norm="rmsnorm", sublayers=(ATTN_OUT, MLP), heads=32, seq=4096,
     note="h=4096, SwiGLU ffn=11008 (1376 per shard), P=8, T=8192 (2 x 4096)")
 
 DECODE_7B_BF16 = Workload(
