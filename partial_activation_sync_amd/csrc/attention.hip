@@ -6,22 +6,27 @@
 // X_m W^K_m, X_m W^V_m) from its own input X_m; with partially synchronized
 // activations the inputs differ per rank, and all ranks run on this device (§3.2).
 //
-// One workgroup (4 waves) takes 128 queries of one head of one rank; each wave holds 32
-// queries' Q fragments in registers for the whole key loop.  Keys come in blocks of 64
-// through three LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys], both filled by
-// buffer loads that write LDS directly, rows padded by one 16-byte slot).  Per block:
+// One workgroup (8 waves, two per SIMD) takes 256 queries of one head of one rank; each
+// wave holds 32 queries' Q fragments in registers for the whole key loop.  Keys come in
+// blocks of 64 through three LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys],
+// both filled by buffer loads that write LDS directly, rows padded by one 16-byte slot).
+// Per block and wave:
 //   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, keys as rows, queries as columns), so
 //                   each lane's accumulators hold one query's scores for 16 keys and the
 //                   row statistics of the online softmax need only the lane pair l, l^32;
-//   scale by log2(e)/sqrt(d), mask keys past the query or past the sequence, update the
-//   running max and sum, rescale the output accumulators;
+//   mask keys past the query or past the sequence (only on the wave's diagonal block),
+//   update the running max in log2 units (scale log2(e)/sqrt(d) folded into the exp2
+//   argument), and rescale the output only when some query's max grew by more than 8
+//   (a stale max leaves every probability at most 2^8, which fp32 sums and bf16 holds);
 //   O^T += V^T P^T  with P^T taken straight from the S^T accumulators (bf16) as the
 //                   column operand: lane l's 8 values of a 16-key chunk are keys
 //                   4g..4g+3 and 8+4g..8+4g+3 (g = l / 32), and the V^T fragments are read
 //                   in the same key order (two 8-byte LDS reads), which sums the same
 //                   products in another order.
-// The last queries of a sequence and keys past it read as zero (buffer range checks)
-// and are masked; sequences never see each other.
+// A wave skips key blocks that lie wholly past its last query; the workgroup's loads and
+// barriers run for all of them.  While one wave of a SIMD works through its softmax, the
+// other's matrix products run.  Queries past the sequence and keys past it read as zero
+// (buffer range checks) and are masked; sequences never see each other.
 #include "caat_internal.h"
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -39,7 +44,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int RSRC_WORD3 = 0x00020000;
-constexpr int BQ = 128, BKV = 64;
+constexpr int NWAVE = 8, NT = 64 * NWAVE, BQ = 32 * NWAVE, BKV = 64;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
@@ -54,14 +59,14 @@ __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 template <int D>
-__global__ __launch_bounds__(256)
-void k_attn(AttnArgs a, int nqb)
+__global__ __launch_bounds__(NT)
+void k_attn(AttnArgs a, int nqb, int ngrp)
 {
     constexpr int CK = D / 8;                 // 16-byte chunks per K row
     constexpr int KROW = CK + 1;              // K row pitch in slots (one slot of padding)
     constexpr int VROW = BKV / 8 + 1;         // V^T row pitch in slots (8 chunks + padding)
-    constexpr int KLOADS = (BKV * KROW + 255) / 256, VLOADS = (D * VROW + 255) / 256;
-    constexpr int KSLOTS = KLOADS * 256, VSLOTS = VLOADS * 256;
+    constexpr int KLOADS = (BKV * KROW + NT - 1) / NT, VLOADS = (D * VROW + NT - 1) / NT;
+    constexpr int KSLOTS = KLOADS * NT, VSLOTS = VLOADS * NT;
     constexpr int NKK = D / 16;               // MFMA steps over d for the scores
     constexpr int NDB = D / 32;               // 32-row blocks of O^T
     __shared__ __attribute__((aligned(16))) uint4 K0[KSLOTS];
@@ -73,19 +78,13 @@ void k_attn(AttnArgs a, int nqb)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // Workgroups go round-robin to the 8 XCDs; consecutive tiles, which are the query
-    // blocks of one (rank, head, sequence) and read the same keys and values, are given
-    // to one XCD so that its L2 serves them.  Longest key ranges first.
-    int tile;
-    {
-        const int b = blockIdx.x, total = gridDim.x;
-        const int xcd = b & 7, idx = b >> 3, q = total >> 3, rem = total & 7;
-        tile = xcd < rem ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
-    }
+    // Dispatch order: every (rank, head, sequence) group's longest query block first, then
+    // the next longest.  Consecutive workgroups go to the 8 XCDs in turn, so with a
+    // multiple of 8 groups each XCD keeps to the same groups and its L2 serves their keys.
+    const int grp = blockIdx.x % ngrp;
+    const int qb = nqb - 1 - (int)(blockIdx.x / ngrp);
     const int nseq = a.T / a.S;
-    const int qb = nqb - 1 - tile % nqb;
-    const int sq = (tile / nqb) % nseq;
-    const int hd = (tile / (nqb * nseq)) % a.nh, m = tile / (nqb * nseq * a.nh);
+    const int sq = grp % nseq, hd = (grp / nseq) % a.nh, m = grp / (nseq * a.nh);
     const int T = a.T, S = a.S, nh = a.nh, Tp = a.Tp;
     const int ld = 3 * nh * D;
     const int seq0 = sq * S, ql0 = qb * BQ;
@@ -96,7 +95,8 @@ void k_attn(AttnArgs a, int nqb)
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(VT, (uint32_t)((size_t)D * Tp * 2u));
 
     // Q fragments (column operand of S^T): query ql, d values 16 kk + 8 (lane / 32) ...
-    const int ql = ql0 + wave * 32 + (lane & 31);
+    const int wq0 = ql0 + wave * 32;          // the wave's first query
+    const int ql = wq0 + (lane & 31);
     const int g = lane >> 5;
     bf16x8 qf[NKK];
     {
@@ -104,16 +104,18 @@ void k_attn(AttnArgs a, int nqb)
         CAAT_UNROLL for (int kk = 0; kk < NKK; ++kk)
             qf[kk] = load16(rQ, ql < S ? qoff + kk * 32u : OOB);
     }
+    // Last key the wave needs (-1: every query of the wave lies past the sequence).
+    const int wlast = wq0 < S ? min(wq0 + 31, S - 1) : -1;
 
-    // Tile loads: load i of a wave writes the 64 slots from (i * 256 + 64 wave) on, lane
-    // by lane, so slot s = i * 256 + tid holds chunk s % pitch of row s / pitch.  Rows
+    // Tile loads: load i of a wave writes the 64 slots from (i * NT + 64 wave) on, lane
+    // by lane, so slot s = i * NT + tid holds chunk s % pitch of row s / pitch.  Rows
     // are padded by one slot (loaded out of range, as zero) so that the fragment reads
     // of 16 consecutive rows fall in distinct banks while every read of a row is one base
     // address plus an immediate offset.
     uint32_t koff[KLOADS];
     int krow[KLOADS];
     CAAT_UNROLL for (int i = 0; i < KLOADS; ++i) {
-        const int s = i * 256 + tid, r = s / KROW, c = s % KROW;
+        const int s = i * NT + tid, r = s / KROW, c = s % KROW;
         const bool in = r < BKV && c < CK;
         krow[i] = in ? r : BKV + S;            // never inside the sequence: always out of range
         koff[i] = (uint32_t)(((size_t)(seq0 + (in ? r : 0)) * ld + (size_t)(nh + hd) * D +
@@ -122,7 +124,7 @@ void k_attn(AttnArgs a, int nqb)
     uint32_t voff[VLOADS];
     int vkey[VLOADS];
     CAAT_UNROLL for (int i = 0; i < VLOADS; ++i) {
-        const int s = i * 256 + tid, dr = s / VROW, c = s % VROW;
+        const int s = i * NT + tid, dr = s / VROW, c = s % VROW;
         const bool in = dr < D && c < BKV / 8;
         vkey[i] = in ? c * 8 : S;              // padding: out of range
         voff[i] = (uint32_t)(((size_t)(in ? dr : 0) * Tp + seq0 + (in ? c : 0) * 8) * 2u);
@@ -131,21 +133,23 @@ void k_attn(AttnArgs a, int nqb)
 #define CAAT_ISSUE(kv0, Kb, Vb)                                                            \
     do {                                                                                   \
         CAAT_UNROLL for (int i = 0; i < KLOADS; ++i)                                       \
-            load_lds16(rK, (Kb) + i * 256 + wave * 64,                                     \
+            load_lds16(rK, (Kb) + i * NT + wave * 64,                                      \
                        ((kv0) + krow[i] < S) ? koff[i] + (uint32_t)((kv0) * ld * 2) : OOB);\
         CAAT_UNROLL for (int i = 0; i < VLOADS; ++i)                                       \
-            load_lds16(rV, (Vb) + i * 256 + wave * 64,                                     \
+            load_lds16(rV, (Vb) + i * NT + wave * 64,                                      \
                        ((kv0) + vkey[i] < S) ? voff[i] + (uint32_t)((kv0) * 2) : OOB);     \
     } while (0)
 
     f32x16 acc_o[NDB];
     CAAT_UNROLL for (int b = 0; b < NDB; ++b)
         CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] = 0.f;
+    // Running max in log2 units (score * sc) and running sum of 2^(score * sc - m_run).
     float m_run = -INFINITY, l_run = 0.f;
     const float sc = 1.44269504088896341f / sqrtf((float)D);
+    constexpr float RESCALE_MARGIN = 8.f;
 
-    // One key block on the stage (Kb, Vb).  MASK: the block holds keys past a query of
-    // the workgroup or past the sequence (the last two blocks); interior blocks skip it.
+    // One key block on the stage (Kb, Vb).  MASK: the block holds keys past one of the
+    // wave's queries or past the sequence (the wave's diagonal block).
 #define CAAT_BLOCK(kv0, Kb, Vb, MASK)                                                      \
     do {                                                                                   \
         f32x16 acc_s[2];                                                                   \
@@ -161,31 +165,28 @@ void k_attn(AttnArgs a, int nqb)
         float mb = -INFINITY;                                                              \
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
-                float sv = acc_s[kb][v] * sc;                                              \
                 if (MASK) {                                                                \
                     const int key = (kv0) + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);      \
-                    sv = (key > ql || key >= S) ? -INFINITY : sv;                          \
+                    if (key > ql || key >= S) acc_s[kb][v] = -INFINITY;                    \
                 }                                                                          \
-                acc_s[kb][v] = sv;                                                         \
-                mb = fmaxf(mb, sv);                                                        \
+                mb = fmaxf(mb, acc_s[kb][v]);                                              \
             }                                                                              \
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));                                            \
-        const float m_new = fmaxf(m_run, mb);                                              \
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64)) * sc;                                       \
+        const bool grow = mb > m_run + RESCALE_MARGIN;                                     \
+        const float m_new = grow ? mb : m_run;                                             \
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);                         \
-        /* the output is rescaled only when some query's running max moved */             \
-        const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;               \
         float ls = 0.f;                                                                    \
         bf16x8 pf[4];                                                                      \
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
-                const float p = __builtin_amdgcn_exp2f(acc_s[kb][v] - m_new);              \
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kb][v], sc, -m_new)); \
                 ls += p;                                                                   \
                 pf[kb * 2 + (v >> 3)][v & 7] = static_cast<__bf16>(p);                     \
             }                                                                              \
         ls += __shfl_xor(ls, 32, 64);                                                      \
         l_run = alpha * l_run + ls;                                                        \
         m_run = m_new;                                                                     \
-        if (moved) {                                                                       \
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {                                      \
             CAAT_UNROLL for (int b = 0; b < NDB; ++b)                                      \
                 CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;             \
         }                                                                                  \
@@ -204,16 +205,17 @@ void k_attn(AttnArgs a, int nqb)
 
     const int kv_end = min(S, ql0 + BQ);
     const int nkv = (kv_end + BKV - 1) / BKV;
-    // Blocks whose keys all precede the workgroup's first query need no mask.
+    // Per wave: blocks wholly before its first query need no mask, blocks wholly past its
+    // last query are skipped.
 #define CAAT_ANY_BLOCK(kv0, Kb, Vb)                                                        \
     do {                                                                                   \
-        if ((kv0) + BKV <= ql0) CAAT_BLOCK(kv0, Kb, Vb, false);                            \
-        else CAAT_BLOCK(kv0, Kb, Vb, true);                                                \
+        if ((kv0) + BKV <= wq0 && (kv0) + BKV <= S) CAAT_BLOCK(kv0, Kb, Vb, false);        \
+        else if ((kv0) <= wlast) CAAT_BLOCK(kv0, Kb, Vb, true);                            \
     } while (0)
     // Three stages: block j's loads are issued at the start of block j - 2.  The loop
     // runs whole groups of three blocks; loads of a block past the keys fall out of range
-    // (zero) without a branch, and such blocks are fully masked, so they add nothing.
-    // At the end of a block the wait leaves the newest block's loads in flight.
+    // (zero) without a branch, and every wave skips such blocks.  At the end of a block
+    // the wait leaves the newest block's loads in flight.
 #define CAAT_STEP3(j, Kc, Vc, Kn, Vn)                                                      \
     do {                                                                                   \
         CAAT_ISSUE(((j) + 2) * BKV, Kn, Vn);                                               \
@@ -253,11 +255,12 @@ void k_attn(AttnArgs a, int nqb)
 
 hipError_t attention_bf16(const AttnArgs &a, hipStream_t s) {
     const int nqb = (a.S + BQ - 1) / BQ;
-    const dim3 grid(nqb * (a.T / a.S) * a.nh * a.P), block(256);
+    const int ngrp = (a.T / a.S) * a.nh * a.P;
+    const dim3 grid(nqb * ngrp), block(NT);
     if (a.d == 128)
-        hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a, nqb);
+        hipLaunchKernelGGL(k_attn<128>, grid, block, 0, s, a, nqb, ngrp);
     else
-        hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a, nqb);
+        hipLaunchKernelGGL(k_attn<64>, grid, block, 0, s, a, nqb, ngrp);
     return hipGetLastError();
 }
 
