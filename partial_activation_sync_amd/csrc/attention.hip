@@ -6,10 +6,11 @@
 // X_m W^K_m, X_m W^V_m) from its own input X_m; with partially synchronized
 // activations the inputs differ per rank, and all ranks run on this device (§3.2).
 //
-// One workgroup (8 waves, two per SIMD) takes 256 queries of one head of one rank; each
-// wave holds 32 queries' Q fragments in registers for the whole key loop.  Keys come in
-// blocks of 64 through three LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys],
-// both filled by buffer loads that write LDS directly, rows padded by one 16-byte slot).
+// One workgroup (4 waves) takes 128 queries of one head of one rank, and two workgroups
+// share a CU (two waves per SIMD, 80 KB of LDS each); each wave holds 32 queries' Q
+// fragments in registers for the whole key loop.  Keys come in blocks of 64 through two
+// LDS stages (K tile [64 keys][d] and V^T tile [d][64 keys], both filled by buffer loads
+// that write LDS directly, rows padded by one 16-byte slot).
 // Per block and wave:
 //   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, keys as rows, queries as columns), so
 //                   each lane's accumulators hold one query's scores for 16 keys and the
@@ -24,8 +25,9 @@
 //                   in the same key order (two 8-byte LDS reads), which sums the same
 //                   products in another order.
 // A wave skips key blocks that lie wholly past its last query; the workgroup's loads and
-// barriers run for all of them.  While one wave of a SIMD works through its softmax, the
-// other's matrix products run.  Queries past the sequence and keys past it read as zero
+// barriers run for all of them.  The two workgroups of a CU synchronize independently, so
+// one's softmax arithmetic overlaps the other's matrix products.  Queries past the
+// sequence and keys past it read as zero
 // (buffer range checks) and are masked; sequences never see each other.
 #include "caat_internal.h"
 
@@ -44,22 +46,23 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr uint32_t OOB = 0x80000000u;
 constexpr int RSRC_WORD3 = 0x00020000;
-constexpr int NWAVE = 8, NT = 64 * NWAVE, BQ = 32 * NWAVE, BKV = 64;
+constexpr int NW = 4, NT = 64 * NW, BQ = 32 * NW, BKV = 64;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              RSRC_WORD3);
 }
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff) {
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff,
+                                           uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, 0);
+        r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 template <int D>
-__global__ __launch_bounds__(NT)
+__global__ __launch_bounds__(NT, 2)
 void k_attn(AttnArgs a, int nqb, int ngrp)
 {
     constexpr int CK = D / 8;                 // 16-byte chunks per K row
@@ -71,10 +74,8 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
     constexpr int NDB = D / 32;               // 32-row blocks of O^T
     __shared__ __attribute__((aligned(16))) uint4 K0[KSLOTS];
     __shared__ __attribute__((aligned(16))) uint4 K1[KSLOTS];
-    __shared__ __attribute__((aligned(16))) uint4 K2[KSLOTS];
     __shared__ __attribute__((aligned(16))) uint4 V0[VSLOTS];
     __shared__ __attribute__((aligned(16))) uint4 V1[VSLOTS];
-    __shared__ __attribute__((aligned(16))) uint4 V2[VSLOTS];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,33 +112,33 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
     // by lane, so slot s = i * NT + tid holds chunk s % pitch of row s / pitch.  Rows
     // are padded by one slot (loaded out of range, as zero) so that the fragment reads
     // of 16 consecutive rows fall in distinct banks while every read of a row is one base
-    // address plus an immediate offset.
+    // address plus an immediate offset.  The K descriptor of a block starts at its first
+    // key and ends with the sequence, so rows past the sequence read as zero with no
+    // per-lane test; V^T rows are tested per 8-key chunk against the keys left.
     uint32_t koff[KLOADS];
-    int krow[KLOADS];
     CAAT_UNROLL for (int i = 0; i < KLOADS; ++i) {
         const int s = i * NT + tid, r = s / KROW, c = s % KROW;
-        const bool in = r < BKV && c < CK;
-        krow[i] = in ? r : BKV + S;            // never inside the sequence: always out of range
-        koff[i] = (uint32_t)(((size_t)(seq0 + (in ? r : 0)) * ld + (size_t)(nh + hd) * D +
-                              (in ? c : 0) * 8) * 2u);
+        koff[i] = (r < BKV && c < CK) ? (uint32_t)((r * ld + c * 8) * 2) : OOB;
     }
     uint32_t voff[VLOADS];
     int vkey[VLOADS];
     CAAT_UNROLL for (int i = 0; i < VLOADS; ++i) {
         const int s = i * NT + tid, dr = s / VROW, c = s % VROW;
         const bool in = dr < D && c < BKV / 8;
-        vkey[i] = in ? c * 8 : S;              // padding: out of range
-        voff[i] = (uint32_t)(((size_t)(in ? dr : 0) * Tp + seq0 + (in ? c : 0) * 8) * 2u);
+        vkey[i] = in ? c * 8 : BKV;            // padding: never below the keys left
+        voff[i] = in ? (uint32_t)((dr * Tp + c * 8) * 2) : OOB;
     }
-    const __amdgpu_buffer_rsrc_t rK = rQ;
+    const __bf16 *Kseq = QKV + (size_t)seq0 * ld + (size_t)(nh + hd) * D;
 #define CAAT_ISSUE(kv0, Kb, Vb)                                                            \
     do {                                                                                   \
+        const int left_ = S - (kv0);                                                       \
+        const __amdgpu_buffer_rsrc_t rK_ = make_rsrc(                                      \
+            Kseq + (size_t)(kv0) * ld, left_ > 0 ? (uint32_t)left_ * (uint32_t)ld * 2u : 0u); \
         CAAT_UNROLL for (int i = 0; i < KLOADS; ++i)                                       \
-            load_lds16(rK, (Kb) + i * NT + wave * 64,                                      \
-                       ((kv0) + krow[i] < S) ? koff[i] + (uint32_t)((kv0) * ld * 2) : OOB);\
+            load_lds16(rK_, (Kb) + i * NT + wave * 64, koff[i], 0);                        \
         CAAT_UNROLL for (int i = 0; i < VLOADS; ++i)                                       \
-            load_lds16(rV, (Vb) + i * NT + wave * 64,                                      \
-                       ((kv0) + vkey[i] < S) ? voff[i] + (uint32_t)((kv0) * 2) : OOB);     \
+            load_lds16(rV, (Vb) + i * NT + wave * 64, vkey[i] < left_ ? voff[i] : OOB,     \
+                       (uint32_t)(seq0 + (kv0)) * 2u);                                     \
     } while (0)
 
     f32x16 acc_o[NDB];
@@ -205,36 +206,38 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
 
     const int kv_end = min(S, ql0 + BQ);
     const int nkv = (kv_end + BKV - 1) / BKV;
-    // Per wave: blocks wholly before its first query need no mask, blocks wholly past its
-    // last query are skipped.
-#define CAAT_ANY_BLOCK(kv0, Kb, Vb)                                                        \
+    // Blocks wholly before the workgroup's first query (and inside the sequence) need no
+    // mask for any wave; they run in a loop without branches, so the output accumulators
+    // stay in place.  The last blocks (at most two, plus one for a ragged sequence) run
+    // masked, and a wave skips those that lie wholly past its last query.
+    const int nfull = min(ql0, S) / BKV;
+    // Two stages: block j + 1's loads are issued at the start of block j, and the
+    // barrier after the wait both publishes them and frees the stage block j read.
+#define CAAT_NEXT()                                                                        \
     do {                                                                                   \
-        if ((kv0) + BKV <= wq0 && (kv0) + BKV <= S) CAAT_BLOCK(kv0, Kb, Vb, false);        \
-        else if ((kv0) <= wlast) CAAT_BLOCK(kv0, Kb, Vb, true);                            \
-    } while (0)
-    // Three stages: block j's loads are issued at the start of block j - 2.  The loop
-    // runs whole groups of three blocks; loads of a block past the keys fall out of range
-    // (zero) without a branch, and every wave skips such blocks.  At the end of a block
-    // the wait leaves the newest block's loads in flight.
-#define CAAT_STEP3(j, Kc, Vc, Kn, Vn)                                                      \
-    do {                                                                                   \
-        CAAT_ISSUE(((j) + 2) * BKV, Kn, Vn);                                               \
-        CAAT_ANY_BLOCK((j) * BKV, Kc, Vc);                                                 \
-        asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KLOADS + VLOADS) : "memory");            \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");                                   \
         __syncthreads();                                                                   \
     } while (0)
     CAAT_ISSUE(0, K0, V0);
-    CAAT_ISSUE(BKV, K1, V1);
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(KLOADS + VLOADS) : "memory");
-    __syncthreads();
-    for (int j = 0; j < nkv; j += 3) {
-        CAAT_STEP3(j, K0, V0, K2, V2);
-        CAAT_STEP3(j + 1, K1, V1, K0, V0);
-        CAAT_STEP3(j + 2, K2, V2, K1, V1);
+    CAAT_NEXT();
+    int j = 0;
+    for (; j + 2 <= nfull; j += 2) {
+        CAAT_ISSUE((j + 1) * BKV, K1, V1);
+        CAAT_BLOCK(j * BKV, K0, V0, false);
+        CAAT_NEXT();
+        CAAT_ISSUE((j + 2) * BKV, K0, V0);
+        CAAT_BLOCK((j + 1) * BKV, K1, V1, false);
+        CAAT_NEXT();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#undef CAAT_STEP3
-#undef CAAT_ANY_BLOCK
+    for (; j < nkv; j += 2) {
+        CAAT_ISSUE((j + 1) * BKV, K1, V1);
+        if (j * BKV <= wlast) CAAT_BLOCK(j * BKV, K0, V0, true);
+        CAAT_NEXT();
+        CAAT_ISSUE((j + 2) * BKV, K0, V0);
+        if ((j + 1) * BKV <= wlast) CAAT_BLOCK((j + 1) * BKV, K1, V1, true);
+        CAAT_NEXT();
+    }
+#undef CAAT_NEXT
 #undef CAAT_ISSUE
 #undef CAAT_BLOCK
 
