@@ -21,7 +21,9 @@
 //   * the fragment reads for sub-step kk+1 are interleaved with the MFMAs of sub-step
 //     kk, and the next step's first fragments with the last MFMAs of the step;
 //   * LDS rows are 128 B (64 bf16) split in eight 16-byte chunks stored at
-//     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts.
+//     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts;
+//   * the output tile is assembled in the idle LDS stages and stored in whole rows,
+//     16 bytes per lane.
 // Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
 // range of tiles, which share operand rows.
 //
@@ -274,41 +276,64 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
 #undef CAAT_STEP_LAST
 #undef CAAT_ISSUE
 
-    // Epilogue.  Accumulator element v of block (i, j) in lane l is channel row
-    // 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.
-    __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
-    CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-        const int t = t0 + wt * WT + j * 32 + r32;
-        if (t >= T) continue;
-        __bf16 *orow = O + (size_t)t * a.ldo;
-        if (EPI == EPI_SWIGLU) {
-            CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
-                const int yb = n0 + ((wn * IB + i) >> 1) * 32;
-                CAAT_UNROLL for (int g = 0; g < 4; ++g) {
-                    const int y = yb + 8 * g + 4 * kh;
-                    if (y >= N) continue;
-                    bf16x4 o;
-                    CAAT_UNROLL for (int q = 0; q < 4; ++q)
-                        o[q] = static_cast<__bf16>(silu(acc[i][j][4 * g + q]) * acc[i + 1][j][4 * g + q]);
-                    *reinterpret_cast<bf16x4 *>(orow + y) = o;
-                }
-            }
-        } else {
-            CAAT_UNROLL for (int i = 0; i < IB; ++i) {
-                CAAT_UNROLL for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * kh;
-                    if (n >= N) continue;
-                    bf16x4 o;
-                    CAAT_UNROLL for (int q = 0; q < 4; ++q) {
-                        float v = acc[i][j][4 * g + q];
-                        if (EPI == EPI_GELU) v = gelu_erf(v);
-                        if (EPI == EPI_GELU_TANH) v = gelu_tanh(v);
-                        o[q] = static_cast<__bf16>(v);
+    // Epilogue through LDS.  Accumulator element v of block (i, j) in lane l is channel
+    // row 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.  Each
+    // wave writes its outputs (bf16, after the activation) into a [token][column] image
+    // of the tile in the idle LDS stages (the tokens of wave row 0 in L0, of row 1 in
+    // L1): 16-byte chunk C of image row r sits at C ^ (r & SWM), its 8-byte halves
+    // swapped when bit 4 of r is set, which keeps both the 8-byte writes and the 16-byte
+    // reads free of bank conflicts.  Then every thread stores whole 16-byte chunks, and a
+    // wave's store covers whole token rows, instead of 8 bytes in each of 32 rows.
+    constexpr int CPR = NCOL / 8;                    // 16-byte chunks per token row
+    constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;
+    static_assert(WGT == 2 && (BT / 2) * CPR <= SLOTS, "the output image must fit two stages");
+    static_assert((BT * CPR) % NTH == 0, "output chunks must split evenly");
+    // The last step may have refilled a stage nothing reads; let it land first.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+        uint2 *img = reinterpret_cast<uint2 *>(wt == 0 ? L0 : L1);
+        CAAT_UNROLL for (int j = 0; j < JB; ++j) {
+            const int r = j * 32 + r32;                          // image row of the token
+            const int sw = r & SWM, hs = (r >> 4) & 1;
+            if (EPI == EPI_SWIGLU) {
+                CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
+                    const int cb = ((wn * IB + i) >> 1) * 4;      // first chunk of the 32 columns
+                    CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                        bf16x4 o;
+                        CAAT_UNROLL for (int q = 0; q < 4; ++q)
+                            o[q] = static_cast<__bf16>(silu(acc[i][j][4 * g + q]) * acc[i + 1][j][4 * g + q]);
+                        img[(r * CPR + ((cb + g) ^ sw)) * 2 + (kh ^ hs)] = __builtin_bit_cast(uint2, o);
                     }
-                    *reinterpret_cast<bf16x4 *>(orow + n) = o;
+                }
+            } else {
+                CAAT_UNROLL for (int i = 0; i < IB; ++i) {
+                    const int cb = (wn * WN + i * 32) / 8;
+                    CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                        bf16x4 o;
+                        CAAT_UNROLL for (int q = 0; q < 4; ++q) {
+                            float v = acc[i][j][4 * g + q];
+                            if (EPI == EPI_GELU) v = gelu_erf(v);
+                            if (EPI == EPI_GELU_TANH) v = gelu_tanh(v);
+                            o[q] = static_cast<__bf16>(v);
+                        }
+                        img[(r * CPR + ((cb + g) ^ sw)) * 2 + (kh ^ hs)] = __builtin_bit_cast(uint2, o);
+                    }
                 }
             }
         }
+    }
+    __syncthreads();
+    __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
+    CAAT_UNROLL for (int it = 0; it < BT * CPR / NTH; ++it) {
+        const int q = it * NTH + tid;
+        const int row = q / CPR, c = q % CPR;
+        const int r = row % (BT / 2);
+        uint4 v = (row < BT / 2 ? L0 : L1)[r * CPR + (c ^ (r & SWM))];
+        if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        const int t = t0 + row, n = n0 + c * 8;
+        if (t < T && n < N)
+            *reinterpret_cast<uint4 *>(O + (size_t)t * a.ldo + n) = v;
     }
 }
 
