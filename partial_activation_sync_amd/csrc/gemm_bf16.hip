@@ -371,16 +371,16 @@ bool gemm_bf16_supported(const GemmArgs &a) {
            a.ldo % 8 == 0 && (a.kseg == 1 || a.epi == EPI_STORE);
 }
 
-// Tile choice: 256 x 256 (4 waves, 128 x 128 each) when there are at least two full
-// waves of such tiles on the 256 CUs, or one full wave with a long contraction; else
-// 128 x 128 so that smaller problems still spread over every CU.  (An 8-wave 256 x 256
-// variant measured no faster for short contractions once the fragment reads were
-// pipelined, so there is none.)
+// Tile choice: 256 x 256 with 8 waves (4 x 2, 64 x 128 each, two waves per SIMD so that
+// one's fragment reads and waits are covered by the other's MFMAs) when there are at
+// least two full waves of such tiles on the 256 CUs, or one full wave with a long
+// contraction; else 128 x 128 with 4 waves so that smaller problems still spread over
+// every CU.
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int ncol256 = (a.epi == EPI_SWIGLU) ? 128 : 256;
     const long tiles256 = (long)a.P * ((a.N + ncol256 - 1) / ncol256) * ((a.T + 255) / 256);
     const long ktot = (long)a.K * a.kseg;
-    if (tiles256 >= 512 || (tiles256 >= 256 && ktot >= 4096)) return launch<256, 256, 2, 2>(a, s);
+    if (tiles256 >= 512 || (tiles256 >= 256 && ktot >= 4096)) return launch<256, 256, 4, 2>(a, s);
     return launch<128, 128, 2, 2>(a, s);
 }
 
