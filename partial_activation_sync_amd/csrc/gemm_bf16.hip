@@ -279,22 +279,23 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     // Epilogue through LDS.  Accumulator element v of block (i, j) in lane l is channel
     // row 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.  Each
     // wave writes its outputs (bf16, after the activation) into a [token][column] image
-    // of the tile in the idle LDS stages (the tokens of wave row 0 in L0, of row 1 in
-    // L1): 16-byte chunk C of image row r sits at C ^ (r & SWM), its 8-byte halves
+    // of the tile in the idle LDS stages (the first half of the tokens in L0, the second
+    // in L1): 16-byte chunk C of image row r sits at C ^ (r & SWM), its 8-byte halves
     // swapped when bit 4 of r is set, which keeps both the 8-byte writes and the 16-byte
     // reads free of bank conflicts.  Then every thread stores whole 16-byte chunks, and a
     // wave's store covers whole token rows, instead of 8 bytes in each of 32 rows.
     constexpr int CPR = NCOL / 8;                    // 16-byte chunks per token row
     constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;
-    static_assert(WGT == 2 && (BT / 2) * CPR <= SLOTS, "the output image must fit two stages");
+    static_assert((BT / 2) * CPR <= SLOTS && WT % 32 == 0, "the output image must fit two stages");
     static_assert((BT * CPR) % NTH == 0, "output chunks must split evenly");
     // The last step may have refilled a stage nothing reads; let it land first.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     {
-        uint2 *img = reinterpret_cast<uint2 *>(wt == 0 ? L0 : L1);
         CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-            const int r = j * 32 + r32;                          // image row of the token
+            const int tb = wt * WT + j * 32;                     // the 32 tokens' first row
+            uint2 *img = reinterpret_cast<uint2 *>(tb < BT / 2 ? L0 : L1);
+            const int r = tb % (BT / 2) + r32;                   // image row of the token
             const int sw = r & SWM, hs = (r >> 4) & 1;
             if (EPI == EPI_SWIGLU) {
                 CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
