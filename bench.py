@@ -223,7 +223,8 @@ def bench_backward(args, w, T, p):
         f"norm={w.norm}")
     inputs = runner.make_inputs(w, T=T)
     run = runner.Run(w, inputs, p=p, store_resid=True, weight_copies=1)
-    br = runner.BackwardRun(run)
+    stored = args.preact == "stored"
+    br = runner.BackwardRun(run, store_preact=stored)
     torch.cuda.synchronize()
     subs = ["mlp"] + (["attn"] if run.attn is not None else [])
     steps = caat.BWD_STEPS
@@ -265,6 +266,8 @@ def bench_backward(args, w, T, p):
         flops, nbytes = kernel_work_bwd(w, T, sub, name)
         if sub == "attn" and name in ("a", "act", "W1T", "dx", "daT_xT", "dW1"):
             continue          # no first GEMM in the out-projection
+        if name == "a" and stored:
+            continue          # the pre-activation comes from the training forward
         d = {"ms": round(ms, 4), "share": round(ms / span_ms, 3)}
         if flops:
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
@@ -292,6 +295,22 @@ def bench_backward(args, w, T, p):
                        "backward.hip" if not flops else
                        ("gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"))
     roof["traffic"] = traffic_for(src, traffic_key(w.name + ":bwd", T, dom))
+    # What the stored pre-activation costs the forward: a training forward (K1's epilogue
+    # also writes x W1^T) against the plain one, same inputs, same stream.
+    fwd_ms = {}
+    for name, pre in (("plain", None), ("train", br.preact)):
+        if name == "train" and pre is None:
+            continue
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(2):
+            run.step(preact=pre)
+        e0.record()
+        for _ in range(5):
+            run.step(preact=pre)
+        e1.record()
+        torch.cuda.synchronize()
+        fwd_ms[name] = round(e0.elapsed_time(e1) / 5, 4)
+    log(f"[bench] forward per step: {fwd_ms} (train: also stores the pre-activation)")
     base = None
     if args.cpu_budget > 0:
         log("[bench] timing the oracle backward on host cores ...")
@@ -304,10 +323,12 @@ def bench_backward(args, w, T, p):
         "data": "synthetic: seeded N(0,1) activations and upstream gradients, N(0,0.02^2) weights",
         "config": {"workload": w.name, "pass": "backward", "P": w.P, "h": w.h, "ffn": w.ffn,
                    "T": T, "p": p, "n_s": run.mlp.n_s, "act": w.act, "norm": w.norm,
-                   "sublayers": list(w.sublayers), "parallelism": f"tp{w.P} emulated on 1 GPU"},
+                   "sublayers": list(w.sublayers), "parallelism": f"tp{w.P} emulated on 1 GPU",
+                   "preact": args.preact},
         "roofline": roof,
         "cpu_baseline": base,
         "kernels": detail,
+        "forward_ms": fwd_ms,
     }
     print(json.dumps(line), flush=True)
 
@@ -445,6 +466,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as a captured HIP graph (one graph per weight "
                          "copy, replayed); value and ms_per_step then come from the replays")
+    ap.add_argument("--preact", choices=("stored", "recompute"), default="stored",
+                    help="backward: read the pre-activation a training forward stored, or "
+                         "recompute it with a GEMM")
     ap.add_argument("--pass", dest="pass_", choices=("forward", "backward", "block"), default="forward",
                     help="time the forward (default) or the backward of the path")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -126,6 +126,13 @@ typedef struct {
  * out-projection (CAAT_NONE) must come through here, since its input is not [P][T][h]. */
 int caat_forward_ex(caat_handle handle, const caat_args *args);
 
+/* caat_forward_ex for training (MLP only): the same outputs, and preact [P][T][F1]
+ * (caller-owned, 16-byte aligned) receives the raw pre-activation x W1^T (SwiGLU: the
+ * gate columns [0, f_s), then the up columns), the operand of sigma' in the backward of
+ * Eq. 22.  Passed to caat_backward (caat_bwd_args.preact), it replaces the backward's
+ * recompute GEMM with bitwise-identical values.  Returns CAAT_EINVAL for CAAT_NONE. */
+int caat_forward_train(caat_handle handle, const caat_args *args, void *preact);
+
 /* Step a1 alone (MLP only): Y = act(x W1^T) per rank, x [P][T][h] -> Y [P][T][f_s].
  * First sum of Eq. 22 and the nonlinearity. */
 int caat_column_gemm_act(caat_handle handle, int T, const void *x, const void *W1, void *Y,
@@ -206,13 +213,16 @@ typedef struct {
     void *const *events;    /* NULL, or n_events hipEvent_t: event k is recorded on the
                                stream after step k (see CAAT_BWD_STEPS), for timing */
     int n_events;
+    const void *preact;     /* NULL: recompute x W1^T; else the pre-activation
+                               caat_forward_train stored [P][T][F1] (MLP only) */
 } caat_bwd_args;
 
 /* The steps of caat_backward, in launch order (for caat_bwd_args.events).  Steps that
  * do not apply (CAAT_NONE has no first GEMM) launch nothing; their events are still
  * recorded.
  *   0 norm derivative + reduce over ranks + dgamma/dbeta    1 transpose of W2
- *   2 GEMM dY = dZt W2                                       3 GEMM a = x W1^T (recompute)
+ *   2 GEMM dY = dZt W2                                       3 GEMM a = x W1^T (recompute;
+ *                                                              nothing when preact is given)
  *   4 activation backward (da, Y)                            5 transpose of W1
  *   6 GEMM dx = da W1 (+ residual gradient when resid = in)  7 transposes of da and x
  *   8 GEMM dW1 = da^T x                                      9 transposes of Y (or H), dZt

@@ -50,7 +50,8 @@ class caat_bwd_args(ctypes.Structure):
                 ("dW1", ctypes.c_void_p), ("dW2", ctypes.c_void_p), ("dgamma", ctypes.c_void_p),
                 ("dbeta", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p),
-                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int)]
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int),
+                ("preact", ctypes.c_void_p)]
 
 
 class caat_block_args(ctypes.Structure):
@@ -89,6 +90,7 @@ def lib():
         L.caat_set_workspace.argtypes = [vp, vp, sz]
         L.caat_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp]
         L.caat_forward_ex.argtypes = [vp, ctypes.POINTER(caat_args)]
+        L.caat_forward_train.argtypes = [vp, ctypes.POINTER(caat_args), vp]
         L.caat_column_gemm_act.argtypes = [vp, i, vp, vp, vp, vp]
         L.caat_row_gemm.argtypes = [vp, i, vp, vp, vp, vp]
         L.caat_partial_sync_norm.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp]
@@ -108,7 +110,8 @@ def lib():
         L.caat_error_string.restype = ctypes.c_char_p
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
-                     "caat_forward_ex", "caat_column_gemm_act", "caat_row_gemm",
+                     "caat_forward_ex", "caat_forward_train", "caat_column_gemm_act",
+                     "caat_row_gemm",
                      "caat_partial_sync_norm", "caat_row_gemm_reduce", "caat_sync_norm",
                      "caat_backward", "caat_partial_sync_norm_backward", "caat_attention",
                      "caat_block_forward"):
@@ -197,6 +200,15 @@ def caat_forward_ex(handle, T, inp, W1, W2, gamma, out, resid=None, beta=None, o
     return _check(lib().caat_forward_ex(handle, ctypes.byref(a)), "caat_forward_ex")
 
 
+def caat_forward_train(handle, T, inp, W1, W2, gamma, out, preact, resid=None, beta=None,
+                       out_resid=None, stream=None):
+    """caat_forward_ex that also stores the pre-activation [P][T][F1] in preact."""
+    a = caat_args(int(T), _ptr(inp), _ptr(resid), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(beta),
+                  _ptr(out), _ptr(out_resid), _stream(stream))
+    return _check(lib().caat_forward_train(handle, ctypes.byref(a), _ptr(preact)),
+                  "caat_forward_train")
+
+
 def caat_column_gemm_act(handle, T, x, W1, Y, stream=None):
     return _check(lib().caat_column_gemm_act(handle, int(T), _ptr(x), _ptr(W1), _ptr(Y),
                                              _stream(stream)), "caat_column_gemm_act")
@@ -232,9 +244,10 @@ def caat_backward_workspace_bytes(handle, T) -> int:
 
 def caat_backward(handle, T, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgamma,
                   workspace, dW1=None, dres=None, dresid=None, dbeta=None, stream=None,
-                  events=None):
+                  events=None, preact=None):
     """events: None, or CAAT_BWD_STEPS raw hipEvent_t handles (ints) recorded after
-    each step (see BWD_STEPS)."""
+    each step (see BWD_STEPS).  preact: the pre-activation caat_forward_train stored
+    (None: the backward recomputes it)."""
     ev = None
     if events is not None:
         ev = (ctypes.c_void_p * len(events))(*events)
@@ -243,7 +256,7 @@ def caat_backward(handle, T, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgam
                       _ptr(dgamma), _ptr(dbeta), _ptr(workspace),
                       workspace.numel() * workspace.element_size(), _stream(stream),
                       ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)) if ev is not None else None,
-                      len(events) if events is not None else 0)
+                      len(events) if events is not None else 0, _ptr(preact))
     return _check(lib().caat_backward(handle, ctypes.byref(a)), "caat_backward")
 
 
@@ -331,7 +344,10 @@ class Sublayer:
         if t.dtype != self.torch_dtype:
             raise ValueError(f"{name}: dtype {t.dtype}, expected {self.torch_dtype}")
 
-    def forward(self, inp, W1, W2, gamma, out, resid=None, beta=None, out_resid=None, stream=None):
+    def forward(self, inp, W1, W2, gamma, out, resid=None, beta=None, out_resid=None, stream=None,
+                preact=None):
+        """preact (MLP only): a [P][T][F1] tensor that also receives the raw pre-activation
+        (caat_forward_train), for a backward that then skips its recompute GEMM."""
         P, h = self.P, self.h
         T = inp.shape[1]
         self._expect(inp, (P, T, self.kin), "in")
@@ -345,11 +361,17 @@ class Sublayer:
         self._expect(out, (P, T, h), "out")
         self._expect(out_resid, (P, T, h), "out_resid")
         self.workspace(T, inp.device)
+        if preact is not None:
+            if self.act == NONE:
+                raise ValueError("preact: the out-projection has no pre-activation")
+            self._expect(preact, (P, T, F1), "preact")
+            return caat_forward_train(self.handle, T, inp, W1, W2, gamma, out, preact,
+                                      resid=resid, beta=beta, out_resid=out_resid, stream=stream)
         return caat_forward_ex(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
                                out, resid=resid, beta=beta, out_resid=out_resid, stream=stream)
 
     def backward(self, inp, W1, W2, gamma, out_resid, dout, din, dW2, dgamma, dW1=None,
-                 dres=None, dresid=None, dbeta=None, stream=None, events=None):
+                 dres=None, dresid=None, dbeta=None, stream=None, events=None, preact=None):
         """Gradients of one sublayer (shape and dtype checks, then caat_backward)."""
         import torch
         P, h = self.P, self.h
@@ -363,6 +385,7 @@ class Sublayer:
             F1 = 2 * self.f_s if self.act == SWIGLU else self.f_s
             self._expect(W1, (P, F1, h), "W1")
             self._expect(dW1, (P, F1, h), "dW1")
+            self._expect(preact, (P, T, F1), "preact")
         for name, t in (("out_resid", out_resid), ("dout", dout), ("dres", dres),
                         ("dresid", dresid)):
             self._expect(t, (P, T, h), name)
@@ -375,7 +398,8 @@ class Sublayer:
             self._bws = torch.empty(nbytes, dtype=torch.uint8, device=inp.device)
         return caat_backward(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
                              out_resid, dout, din, dW2, dgamma, self._bws, dW1=dW1, dres=dres,
-                             dresid=dresid, dbeta=dbeta, stream=stream, events=events)
+                             dresid=dresid, dbeta=dbeta, stream=stream, events=events,
+                             preact=preact)
 
 
 class Block:

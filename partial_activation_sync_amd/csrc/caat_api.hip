@@ -81,6 +81,19 @@ caat::GemmArgs col_args(const caat_ctx *c, int T, const void *x, const void *W1,
     return g;
 }
 
+// The raw pre-activation as one plain GEMM: a[m][t][n] = sum_j x[m][t][j] W1[m][n][j],
+// n < F1 (SwiGLU: gate rows, then up rows), row stride F1.
+caat::GemmArgs preact_args(const caat_ctx *c, int T, const void *W1, const void *x, void *a) {
+    caat::GemmArgs g{};
+    g.P = c->P; g.N = c->F1; g.T = T; g.K = c->h;
+    g.W = W1; g.w_stride = (size_t)c->F1 * c->h;
+    g.X = x;  g.x_stride = (size_t)T * c->h;
+    g.out = a; g.o_stride = (size_t)T * c->F1; g.ldo = c->F1;
+    g.epi = caat::EPI_STORE;
+    g.kseg = 1;
+    return g;
+}
+
 caat::GemmArgs row_args(const caat_ctx *c, int T, const void *in, const void *W2, void *Z) {
     caat::GemmArgs g{};
     g.P = c->P; g.N = c->h; g.T = T; g.K = c->k2;
@@ -232,7 +245,11 @@ CAAT_API int caat_set_workspace(caat_handle handle, void *dev_ptr, size_t bytes)
     return CAAT_OK;
 }
 
-CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
+namespace {
+
+// The forward of one sublayer; preact (nullable, MLP only) also receives the raw
+// pre-activation x W1^T, [P][T][F1].
+int forward_impl(caat_handle c, const caat_args *a, void *preact) {
     if (c == nullptr || a == nullptr) return CAAT_EINVAL;
     const int T = a->T;
     if (T < 1) return CAAT_EINVAL;
@@ -260,7 +277,18 @@ CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
     void *S = ws + y_bytes(c, T) + partial_bytes(c, T);
     const void *gemm_in = a->in;
     if (c->act != CAAT_NONE) {
-        rc = run_gemm(c, col_args(c, T, a->in, a->W1, Y), s);
+        caat::GemmArgs g = col_args(c, T, a->in, a->W1, Y);
+        if (preact != nullptr) {
+            if (c->dtype == CAAT_BF16 && !caat::gemm_decode_applies(g)) {
+                // The MFMA kernel's epilogue stores the pre-activation beside Y.
+                g.pre = preact; g.pre_stride = (size_t)T * c->F1; g.ld_pre = c->F1;
+            } else {
+                // Other kernels: the same contraction as the backward's recompute.
+                rc = run_gemm(c, preact_args(c, T, a->W1, a->in, preact), s);
+                if (rc != CAAT_OK) return rc;
+            }
+        }
+        rc = run_gemm(c, g, s);
         if (rc != CAAT_OK) return rc;
         gemm_in = Y;
     }
@@ -272,6 +300,17 @@ CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
     rc = run_gemm(c, row_args(c, T, gemm_in, a->W2, Z), s);
     if (rc != CAAT_OK) return rc;
     return run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s);
+}
+
+}  // namespace
+
+CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
+    return forward_impl(c, a, nullptr);
+}
+
+CAAT_API int caat_forward_train(caat_handle c, const caat_args *a, void *preact) {
+    if (c == nullptr || c->act == CAAT_NONE || !aligned16(preact)) return CAAT_EINVAL;
+    return forward_impl(c, a, preact);
 }
 
 CAAT_API int caat_forward(caat_handle c, int T, const void *x, const void *W1, const void *W2,
@@ -470,6 +509,7 @@ CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
         !aligned16(a->dW2) || !aligned16(a->dgamma))
         return CAAT_EINVAL;
     if (mlp && (!aligned16(a->W1) || !aligned16(a->dW1))) return CAAT_EINVAL;
+    if (!aligned16_or_null(a->preact) || (!mlp && a->preact != nullptr)) return CAAT_EINVAL;
     if (!aligned16_or_null(a->dres) || !aligned16_or_null(a->dresid) ||
         !aligned16_or_null(a->dbeta))
         return CAAT_EINVAL;
@@ -507,10 +547,15 @@ CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
     CAAT_TRY(mark());
     const void *y_in = a->in;              // the second GEMM's input (H for the out-projection)
     if (mlp) {
-        // 3, 4: recompute the pre-activation, then da = dY * sigma'(a) and Y = sigma(a).
-        CAAT_TRY(run_gemm(c, plain_args(c, T, F1, h, a->W1, a->in, ws + L.A), s));
+        // 3, 4: the pre-activation (stored by caat_forward_train, or recomputed), then
+        // da = dY * sigma'(a) and Y = sigma(a).
+        const void *pre = a->preact;
+        if (pre == nullptr) {
+            CAAT_TRY(run_gemm(c, preact_args(c, T, a->W1, a->in, ws + L.A), s));
+            pre = ws + L.A;
+        }
         CAAT_TRY(mark());
-        CAAT_HIP(caat::act_backward(c->act, c->dtype, (size_t)P * T, fs, ws + L.A, dY, ws + L.da,
+        CAAT_HIP(caat::act_backward(c->act, c->dtype, (size_t)P * T, fs, pre, dY, ws + L.da,
                                     ws + L.Y, s));
         CAAT_TRY(mark());
         y_in = ws + L.Y;

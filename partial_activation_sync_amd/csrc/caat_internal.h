@@ -46,6 +46,11 @@ struct GemmArgs {
     int epi;
     int kseg;                          // K segments (>= 1)
     size_t w_kseg, x_kseg;             // elements between K segments
+    // Optional second output of an activation epilogue (nullptr: none): the raw
+    // pre-activation, [t][F1] per batch with row stride ld_pre (SwiGLU: gate columns
+    // [0, N), up columns [up_off, up_off + N)).  Only the bf16 MFMA kernel writes it.
+    void *pre;      size_t pre_stride;
+    int ld_pre;
 };
 
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s);

@@ -23,7 +23,8 @@
 //   * LDS rows are 128 B (64 bf16) split in eight 16-byte chunks stored at
 //     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts;
 //   * the output tile is assembled in the idle LDS stages and stored in whole rows,
-//     16 bytes per lane.
+//     16 bytes per lane (an activation epilogue can store the raw pre-activation too,
+//     for a backward pass that then need not recompute it).
 // Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
 // range of tiles, which share operand rows.
 //
@@ -291,6 +292,43 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     // The last step may have refilled a stage nothing reads; let it land first.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (EPI != EPI_STORE && a.pre != nullptr) {
+        // The raw pre-activation first, through the same image (all BN weight rows of the
+        // tile; SwiGLU: the gate columns in image chunks [0, CPR), the up columns after).
+        constexpr int CPP = BN / 8;
+        constexpr int SWP = (CPP < 16 ? CPP : 16) - 1;
+        static_assert((BT / 2) * CPP <= SLOTS && (BT * CPP) % NTH == 0, "pre-activation image");
+        CAAT_UNROLL for (int j = 0; j < JB; ++j) {
+            const int tb = wt * WT + j * 32;
+            uint2 *img = reinterpret_cast<uint2 *>(tb < BT / 2 ? L0 : L1);
+            const int r = tb % (BT / 2) + r32;
+            const int sw = r & SWP, hs = (r >> 4) & 1;
+            CAAT_UNROLL for (int i = 0; i < IB; ++i) {
+                const int b32 = (wn * WN + i * 32) / 32;          // 32-row weight block
+                const int cb = (EPI == EPI_SWIGLU) ? (b32 & 1) * CPR + (b32 >> 1) * 4 : b32 * 4;
+                CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                    bf16x4 o;
+                    CAAT_UNROLL for (int q = 0; q < 4; ++q) o[q] = static_cast<__bf16>(acc[i][j][4 * g + q]);
+                    img[(r * CPP + ((cb + g) ^ sw)) * 2 + (kh ^ hs)] = __builtin_bit_cast(uint2, o);
+                }
+            }
+        }
+        __syncthreads();
+        __bf16 *Pm = reinterpret_cast<__bf16 *>(a.pre) + (size_t)m * a.pre_stride;
+        CAAT_UNROLL for (int it = 0; it < BT * CPP / NTH; ++it) {
+            const int q = it * NTH + tid;
+            const int row = q / CPP, c = q % CPP;
+            const int r = row % (BT / 2);
+            uint4 v = (row < BT / 2 ? L0 : L1)[r * CPP + (c ^ (r & SWP))];
+            if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+            const int up = (EPI == EPI_SWIGLU) && c >= CPR;
+            const int y = n0 + (c - up * CPR) * 8;
+            const int t = t0 + row;
+            if (t < T && y < N)
+                *reinterpret_cast<uint4 *>(Pm + (size_t)t * a.ld_pre + (up ? a.up_off : 0) + y) = v;
+        }
+        __syncthreads();
+    }
     {
         CAAT_UNROLL for (int j = 0; j < JB; ++j) {
             const int tb = wt * WT + j * 32;                     // the 32 tokens' first row

@@ -83,8 +83,9 @@ class Run:
         self.out = torch.empty((P, T, h), dtype=dt, device=device)
         self.out_resid = torch.empty((P, T, h), dtype=dt, device=device) if store_resid else None
 
-    def step(self, stream=None):
-        """One forward of the whole path (out-projection sublayer, then the MLP)."""
+    def step(self, stream=None, preact=None):
+        """One forward of the whole path (out-projection sublayer, then the MLP).  preact:
+        a [P][T][F1] tensor that receives the MLP's pre-activation (a training forward)."""
         d = self.dev
         if self.attn is not None:
             self.attn.forward(d["ctx"], None, d["Wo"], d["gamma"], self.attn_out, resid=d["x0"],
@@ -93,7 +94,7 @@ class Run:
         else:
             mlp_in, mlp_resid = d["x"], d["x"]
         self.mlp.forward(mlp_in, d["W1"], d["W2"], d["gamma"], self.out, resid=mlp_resid,
-                         beta=d["beta"], out_resid=self.out_resid, stream=stream)
+                         beta=d["beta"], out_resid=self.out_resid, stream=stream, preact=preact)
 
     def outputs(self):
         o = {"out": self.out}
@@ -159,7 +160,9 @@ class BackwardRun:
     out-projection sublayer's backward fed with the gradients of the MLP's input and
     residual (the chain rule through the pair).  A step only enqueues library calls."""
 
-    def __init__(self, run: Run, seed=synth.BASE_SEED):
+    def __init__(self, run: Run, seed=synth.BASE_SEED, store_preact=True):
+        """store_preact: the forward is a training forward that stores the MLP's
+        pre-activation, which the backward then reads instead of recomputing."""
         self.run = run
         w = run.w
         P, T, h = w.P, run.T, w.h
@@ -167,7 +170,9 @@ class BackwardRun:
         dev = run.out.device
         if run.out_resid is None:
             raise ValueError("the backward needs the forward's out_resid")
-        run.step()
+        F1 = 2 * w.f_s if w.act == "swiglu" else w.f_s
+        self.preact = torch.empty((P, T, F1), dtype=dt, device=dev) if store_preact else None
+        run.step(preact=self.preact)
         self.dout = synth.normal((P, T, h), synth.DOUT, dtype=dt, seed=seed).to(dev)
         self.dres = synth.normal((P, T, h), synth.DRES, dtype=dt, seed=seed).to(dev)
         e = lambda shape, dtype=dt: torch.empty(shape, dtype=dtype, device=dev)
@@ -187,7 +192,7 @@ class BackwardRun:
         mlp_in = run.attn_out if run.attn is not None else d["x"]
         run.mlp.backward(mlp_in, d["W1"], d["W2"], d["gamma"], run.out_resid, self.dout, g["din"],
                          g["dW2"], g["dgamma"], dW1=g["dW1"], dres=self.dres, dresid=g["dresid"],
-                         dbeta=g["dbeta"], events=events_mlp)
+                         dbeta=g["dbeta"], events=events_mlp, preact=self.preact)
         if run.attn is not None:
             a = self.attn_g
             run.attn.backward(d["ctx"], None, d["Wo"], d["gamma"], run.attn_out_resid, g["din"],

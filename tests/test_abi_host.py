@@ -123,6 +123,8 @@ def test_forward_checks_before_any_launch():
     assert L.caat_column_gemm_act(att, 4, fake, fake, fake, st) == caat.EINVAL
     a = caat.caat_args(4, fake, None, None, fake, fake, None, fake, None, None)
     assert L.caat_forward_ex(att, ctypes.byref(a)) == caat.EINVAL                     # resid needed
+    a = caat.caat_args(4, fake, fake, None, fake, fake, None, fake, None, None)
+    assert L.caat_forward_train(att, ctypes.byref(a), fake) == caat.EINVAL          # MLP only
     caat.caat_destroy(att)
 
 
@@ -168,7 +170,8 @@ def test_backward_workspace_and_checks_before_any_launch():
         ("T", T), ("in_", fake), ("W1", fake), ("W2", fake), ("gamma", fake),
         ("out_resid", fake), ("dout", fake), ("dres", None), ("din", fake), ("dresid", None),
         ("dW1", fake), ("dW2", fake), ("dgamma", fake), ("dbeta", None), ("workspace", fake),
-        ("workspace_bytes", need), ("stream", None), ("events", None), ("n_events", 0))])
+        ("workspace_bytes", need), ("stream", None), ("events", None), ("n_events", 0),
+        ("preact", None))])
     assert L.caat_backward(None, ctypes.byref(args())) == caat.EINVAL
     assert L.caat_backward(hd, None) == caat.EINVAL
     assert L.caat_backward(hd, ctypes.byref(args(T=0))) == caat.EINVAL
@@ -178,6 +181,7 @@ def test_backward_workspace_and_checks_before_any_launch():
     assert L.caat_backward(hd, ctypes.byref(args(dgamma=fake + 4))) == caat.EINVAL
     assert L.caat_backward(hd, ctypes.byref(args(workspace_bytes=need - 1))) == caat.EWORKSPACE
     assert L.caat_backward(hd, ctypes.byref(args(workspace=None))) == caat.EWORKSPACE
+    assert L.caat_backward(hd, ctypes.byref(args(preact=fake + 8))) == caat.EINVAL   # misaligned
     small = 2 * a256(NB * h * 4)
     assert L.caat_partial_sync_norm_backward(hd, T, fake, fake, None, fake, fake, None, fake,
                                              None, fake, small - 1, None) == caat.EWORKSPACE
@@ -192,6 +196,9 @@ def test_backward_workspace_and_checks_before_any_launch():
                                         P * k2 * Tp * 2])
     # the out-projection's residual is not its input: dresid is required
     assert L.caat_backward(att, ctypes.byref(args(W1=None, dW1=None, workspace_bytes=need))) == caat.EINVAL
+    # a stored pre-activation belongs to an MLP
+    assert L.caat_backward(att, ctypes.byref(args(W1=None, dW1=None, dresid=fake, preact=fake,
+                                                  workspace_bytes=need))) == caat.EINVAL
     caat.caat_destroy(att)
 
 

@@ -193,3 +193,51 @@ def test_backward_pair_chain_matches_oracle():
     _say("   errors:", {k: f"{e:.2e}" for k, e in errs.items()})
     for k, e in errs.items():
         assert e <= TOL["bf16"], (k, e)
+
+
+@pytest.mark.parametrize("act,dtype,T", [("swiglu", "bf16", 192), ("gelu", "bf16", 130),
+                                         ("swiglu", "bf16", 24), ("gelu_tanh", "f32", 40)])
+def test_stored_preactivation(act, dtype, T):
+    """caat_forward_train: the same out / out_resid as caat_forward_ex bit for bit, the
+    pre-activation x W1^T against the oracle's linear layer, and a backward fed with it
+    bit-identical to the backward that recomputes it (T = 24: the weight-streaming
+    kernels, which fill the pre-activation with a separate GEMM)."""
+    P, h, ffn = 4, 256, 768
+    _say(f"[case] stored pre-activation act={act} {dtype} T={T}")
+    d = _inputs(P, T, h, ffn, act, dtype, resid_given=True, dres_given=True)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+    sub = caat.Sublayer(h, ffn, P, 0.5, norm="rmsnorm", act=act, dtype=dtype, eps=1e-5)
+    dt = sub.torch_dtype
+    F1 = dev["W1"].shape[1]
+    outs = {}
+    for train in (False, True):
+        out = torch.empty((P, T, h), dtype=dt, device="cuda")
+        out_resid = torch.empty_like(out)
+        pre = torch.full((P, T, F1), float("nan"), dtype=dt, device="cuda") if train else None
+        sub.forward(dev["x"], dev["W1"], dev["W2"], dev["gamma"], out, resid=dev["resid"],
+                    beta=dev["beta"], out_resid=out_resid, preact=pre)
+        outs[train] = (out, out_resid, pre)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[True][0], outs[False][0])
+    assert torch.equal(outs[True][1], outs[False][1])
+    pre = outs[True][2]
+    ref = oracle.linear(d["x"].float(), d["W1"].float())
+    err = rel_err(pre, ref)
+    _say(f"   pre-activation error {err:.2e}")
+    assert err <= TOL[dtype]
+    grads = {}
+    for stored in (False, True):
+        g = {
+            "dx": torch.empty_like(dev["x"]),
+            "dresid": torch.empty((P, T, h), dtype=dt, device="cuda"),
+            "dW1": torch.empty_like(dev["W1"]),
+            "dW2": torch.empty_like(dev["W2"]),
+            "dgamma": torch.empty((h,), dtype=torch.float32, device="cuda"),
+        }
+        sub.backward(dev["x"], dev["W1"], dev["W2"], dev["gamma"], outs[False][1], dev["dout"],
+                     g["dx"], g["dW2"], g["dgamma"], dW1=g["dW1"], dres=dev["dres"],
+                     dresid=g["dresid"], preact=pre if stored else None)
+        grads[stored] = g
+    torch.cuda.synchronize()
+    for k in grads[False]:
+        assert torch.equal(grads[True][k], grads[False][k]), k
