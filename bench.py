@@ -224,6 +224,10 @@ def bench_backward(args, w, T, p):
     inputs = runner.make_inputs(w, T=T)
     run = runner.Run(w, inputs, p=p, store_resid=True, weight_copies=1)
     stored = args.preact == "stored"
+    F1 = 2 * w.f_s if w.act == "swiglu" else w.f_s
+    # bf16 weight-gradient GEMMs contract over tokens from the token-major operands
+    # (no transposes) when every width is a multiple of 8, as the library decides.
+    tn = w.dtype == "bf16" and all(n % 8 == 0 for n in (w.h, w.f_s, F1, w.h // w.P))
     br = runner.BackwardRun(run, store_preact=stored)
     torch.cuda.synchronize()
     subs = ["mlp"] + (["attn"] if run.attn is not None else [])
@@ -268,6 +272,8 @@ def bench_backward(args, w, T, p):
             continue          # no first GEMM in the out-projection
         if name == "a" and stored:
             continue          # the pre-activation comes from the training forward
+        if name in ("daT_xT", "YT_dZtT") and tn:
+            continue          # bf16 weight gradients read the token-major operands
         d = {"ms": round(ms, 4), "share": round(ms / span_ms, 3)}
         if flops:
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
@@ -293,7 +299,8 @@ def bench_backward(args, w, T, p):
     roof["algorithmic_per_launch"] = flops if flops else nbytes
     src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
                        "backward.hip" if not flops else
-                       ("gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"))
+                       ("gemm_tn.hip" if tn and name in ("dW1", "dW2") else
+                        "gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"))
     roof["traffic"] = traffic_for(src, traffic_key(w.name + ":bwd", T, dom))
     # What the stored pre-activation costs the forward: a training forward (K1's epilogue
     # also writes x W1^T) against the plain one, same inputs, same stream.

@@ -226,7 +226,9 @@ typedef struct {
  *   4 activation backward (da, Y)                            5 transpose of W1
  *   6 GEMM dx = da W1 (+ residual gradient when resid = in)  7 transposes of da and x
  *   8 GEMM dW1 = da^T x                                      9 transposes of Y (or H), dZt
- *  10 GEMM dW2 = dZt^T Y */
+ *  10 GEMM dW2 = dZt^T Y
+ * With bf16 (and h, k2, F1 multiples of 8) the weight-gradient GEMMs contract over tokens
+ * straight from the token-major operands: steps 7 and 9 launch nothing. */
 #define CAAT_BWD_STEPS 11
 
 /* The whole backward of one sublayer for every rank.  Returns CAAT_EWORKSPACE for a

@@ -30,6 +30,7 @@
 // sequence and keys past it read as zero
 // (buffer range checks) and are masked; sequences never see each other.
 #include "caat_internal.h"
+#include "bufload.h"
 
 #if defined(__HIP_DEVICE_COMPILE__)
 #define CAAT_UNROLL _Pragma("unroll")
@@ -40,26 +41,9 @@
 namespace caat {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr uint32_t OOB = 0x80000000u;
-constexpr int RSRC_WORD3 = 0x00020000;
 constexpr int NW = 4, NT = 64 * NW, BQ = 32 * NW, BKV = 64;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             RSRC_WORD3);
-}
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff,
-                                           uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
-}
-__device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 template <int D>
 __global__ __launch_bounds__(NT, 2)

@@ -401,10 +401,17 @@ struct BwdLayout {
     size_t dzt, dres, gpart, bpart, W2T, dY, dztT, YT, A, da, Y, W1T, xT, daT, total;
 };
 
+// bf16 weight gradients contract over tokens straight from the token-major operands
+// (gemm_tn); otherwise (fp32, or widths not a multiple of 8) through transposed copies.
+bool tn_weight_grads(const caat_ctx *c) {
+    return c->dtype == CAAT_BF16 && c->h % 8 == 0 && c->k2 % 8 == 0 && c->F1 % 8 == 0;
+}
+
 BwdLayout bwd_layout(const caat_ctx *c, int T) {
     BwdLayout L{};
     const size_t E = esize(c), P = c->P, h = c->h, k2 = c->k2, F1 = c->F1, fs = c->fs;
     const size_t Tp = round8(T), NB = caat::psync_bwd_blocks(T);
+    const bool tr = !tn_weight_grads(c);
     size_t off = 0;
     auto take = [&](size_t n) { const size_t o = off; off += align256(n); return o; };
     L.dzt = take(P * T * h * E);
@@ -413,18 +420,35 @@ BwdLayout bwd_layout(const caat_ctx *c, int T) {
     L.bpart = take(NB * h * 4);
     L.W2T = take(P * k2 * h * E);
     L.dY = take(P * T * k2 * E);
-    L.dztT = take(P * h * Tp * E);
-    L.YT = take(P * k2 * Tp * E);
+    if (tr) {
+        L.dztT = take(P * h * Tp * E);
+        L.YT = take(P * k2 * Tp * E);
+    }
     if (c->act != CAAT_NONE) {
         L.A = take(P * T * F1 * E);
         L.da = take(P * T * F1 * E);
         L.Y = take(P * T * fs * E);
         L.W1T = take(P * h * F1 * E);
-        L.xT = take(P * h * Tp * E);
-        L.daT = take(P * F1 * Tp * E);
+        if (tr) {
+            L.xT = take(P * h * Tp * E);
+            L.daT = take(P * F1 * Tp * E);
+        }
     }
     L.total = off;
     return L;
+}
+
+// Weight gradient out[m][n] = sum_t A[t][m] B[t][n] per rank, from token-major A [T][M]
+// and B [T][N] (gemm_tn).
+int run_tn(const caat_ctx *c, int T, int M, int N, const void *A, const void *B, void *out,
+           hipStream_t s) {
+    caat::TnArgs t{};
+    t.P = c->P; t.M = M; t.N = N; t.K = T;
+    t.A = A; t.a_stride = (size_t)T * M; t.lda = M;
+    t.B = B; t.b_stride = (size_t)T * N; t.ldb = N;
+    t.out = out; t.o_stride = (size_t)M * N; t.ldo = N;
+    if (!caat::gemm_tn_supported(t)) return CAAT_EUNSUPPORTED;
+    return caat::gemm_tn_bf16(t, s) == hipSuccess ? CAAT_OK : CAAT_EDEVICE;
 }
 
 // B3's share of the workspace (the per-workgroup norm-parameter partials).
@@ -523,6 +547,7 @@ CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
     hipStream_t s = reinterpret_cast<hipStream_t>(a->stream);
     char *ws = reinterpret_cast<char *>(a->workspace);
     const int P = c->P, h = c->h, k2 = c->k2, F1 = c->F1, fs = c->fs, Tp = (int)round8(T);
+    const bool tn = tn_weight_grads(c);
     void *dzt = ws + L.dzt;
     void *dresid = a->dresid ? a->dresid : ws + L.dres;
 #define CAAT_TRY(call) do { const int rc_ = (call); if (rc_ != CAAT_OK) return rc_; } while (0)
@@ -566,20 +591,31 @@ CAAT_API int caat_backward(caat_handle c, const caat_bwd_args *a) {
         if (a->dresid == nullptr)
             CAAT_HIP(caat::add_inplace(a->din, dresid, (size_t)P * T * h, c->dtype, s));
         CAAT_TRY(mark());
-        // 7, 8: dW1 = da^T x: contraction over tokens, both operands transposed.
-        CAAT_HIP(caat::transpose(ws + L.da, ws + L.daT, P, T, F1, Tp, c->dtype, s));
-        CAAT_HIP(caat::transpose(a->in, ws + L.xT, P, T, h, Tp, c->dtype, s));
-        CAAT_TRY(mark());
-        CAAT_TRY(run_gemm(c, plain_args(c, F1, h, Tp, ws + L.xT, ws + L.daT, a->dW1), s));
+        // 7, 8: dW1 = da^T x: contraction over tokens (bf16: from the token-major
+        // operands; else through transposed copies).
+        if (tn) {
+            CAAT_TRY(mark());
+            CAAT_TRY(run_tn(c, T, F1, h, ws + L.da, a->in, a->dW1, s));
+        } else {
+            CAAT_HIP(caat::transpose(ws + L.da, ws + L.daT, P, T, F1, Tp, c->dtype, s));
+            CAAT_HIP(caat::transpose(a->in, ws + L.xT, P, T, h, Tp, c->dtype, s));
+            CAAT_TRY(mark());
+            CAAT_TRY(run_gemm(c, plain_args(c, F1, h, Tp, ws + L.xT, ws + L.daT, a->dW1), s));
+        }
         CAAT_TRY(mark());
     } else {
         for (int k = 3; k <= 8; ++k) CAAT_TRY(mark());
     }
     // 9, 10: dW2 = dZt^T Y (or dZt^T H): contraction over tokens.
-    CAAT_HIP(caat::transpose(y_in, ws + L.YT, P, T, k2, Tp, c->dtype, s));
-    CAAT_HIP(caat::transpose(dzt, ws + L.dztT, P, T, h, Tp, c->dtype, s));
-    CAAT_TRY(mark());
-    CAAT_TRY(run_gemm(c, plain_args(c, h, k2, Tp, ws + L.YT, ws + L.dztT, a->dW2), s));
+    if (tn) {
+        CAAT_TRY(mark());
+        CAAT_TRY(run_tn(c, T, h, k2, dzt, y_in, a->dW2, s));
+    } else {
+        CAAT_HIP(caat::transpose(y_in, ws + L.YT, P, T, k2, Tp, c->dtype, s));
+        CAAT_HIP(caat::transpose(dzt, ws + L.dztT, P, T, h, Tp, c->dtype, s));
+        CAAT_TRY(mark());
+        CAAT_TRY(run_gemm(c, plain_args(c, h, k2, Tp, ws + L.YT, ws + L.dztT, a->dW2), s));
+    }
     CAAT_TRY(mark());
 #undef CAAT_TRY
 #undef CAAT_HIP

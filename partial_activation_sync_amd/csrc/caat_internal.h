@@ -54,6 +54,18 @@ struct GemmArgs {
 };
 
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s);
+
+// out[b][m][n] = sum_k A[b][k][m] B[b][k][n], bf16 in and out, fp32 accumulation: the
+// contraction runs across rows of two token-major operands (row strides lda, ldb,
+// elements; batch strides in elements).  M, N, lda, ldb, ldo multiples of 8.
+struct TnArgs {
+    int P, M, N, K;
+    const void *A;  size_t a_stride;  int lda;
+    const void *B;  size_t b_stride;  int ldb;
+    void *out;      size_t o_stride;  int ldo;
+};
+bool gemm_tn_supported(const TnArgs &a);
+hipError_t gemm_tn_bf16(const TnArgs &a, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs &a, hipStream_t s);
 bool gemm_bf16_supported(const GemmArgs &a);
 // Weight-streaming variant for decode batches (T <= 64), bf16.

@@ -32,6 +32,7 @@
 // columns ([g0..31, u0..31, g32..63, u32..63, ...]), so every wave holds matching
 // gate/up accumulators in the same lanes and applies silu(g) * u in registers.
 #include "caat_internal.h"
+#include "bufload.h"
 
 // Scheduling directives and unroll pragmas exist only in the device pass; the host
 // pass only needs the kernel's signature.
@@ -48,26 +49,10 @@
 namespace caat {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 64;
-constexpr uint32_t OOB = 0x80000000u;   // byte offset past every buffer's range
-constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 buffer descriptor: 32-bit dword format
 constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             RSRC_WORD3);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l writes lds + 16 l.
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff,
-                                           uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
-}
 
 __device__ __forceinline__ float gelu_erf(float v) {
     return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));

@@ -158,11 +158,19 @@ def test_backward_workspace_and_checks_before_any_launch():
     hd = caat.caat_create(h, ffn, P, 0.5, caat.LAYERNORM, caat.SWIGLU, caat.BF16)
     fs, F1, Tp, NB = ffn // P, 2 * ffn // P, 40, T
     a256 = lambda n: (n + 255) // 256 * 256
+    # bf16: the weight gradients contract over tokens from the token-major operands, so
+    # no transposed activations; fp32 keeps the transposed copies (token count Tp).
     parts = [P * T * h * 2, P * T * h * 2, NB * h * 4, NB * h * 4, P * fs * h * 2,
-             P * T * fs * 2, P * h * Tp * 2, P * fs * Tp * 2,
-             P * T * F1 * 2, P * T * F1 * 2, P * T * fs * 2, P * h * F1 * 2, P * h * Tp * 2,
-             P * F1 * Tp * 2]
+             P * T * fs * 2,
+             P * T * F1 * 2, P * T * F1 * 2, P * T * fs * 2, P * h * F1 * 2]
     assert caat.caat_backward_workspace_bytes(hd, T) == sum(a256(n) for n in parts)
+    h32 = caat.caat_create(h, ffn, P, 0.5, caat.LAYERNORM, caat.SWIGLU, caat.F32)
+    parts32 = [P * T * h * 4, P * T * h * 4, NB * h * 4, NB * h * 4, P * fs * h * 4,
+               P * T * fs * 4, P * h * Tp * 4, P * fs * Tp * 4,
+               P * T * F1 * 4, P * T * F1 * 4, P * T * fs * 4, P * h * F1 * 4, P * h * Tp * 4,
+               P * F1 * Tp * 4]
+    assert caat.caat_backward_workspace_bytes(h32, T) == sum(a256(n) for n in parts32)
+    caat.caat_destroy(h32)
     assert caat.caat_backward_workspace_bytes(hd, 0) == 0
     assert caat.caat_backward_workspace_bytes(None, T) == 0
     need = caat.caat_backward_workspace_bytes(hd, T)
@@ -192,8 +200,7 @@ def test_backward_workspace_and_checks_before_any_launch():
     need = caat.caat_backward_workspace_bytes(att, T)
     k2 = h // P
     assert need == sum(a256(n) for n in [P * T * h * 2, P * T * h * 2, NB * h * 4, NB * h * 4,
-                                        P * k2 * h * 2, P * T * k2 * 2, P * h * Tp * 2,
-                                        P * k2 * Tp * 2])
+                                        P * k2 * h * 2, P * T * k2 * 2])
     # the out-projection's residual is not its input: dresid is required
     assert L.caat_backward(att, ctypes.byref(args(W1=None, dW1=None, workspace_bytes=need))) == caat.EINVAL
     # a stored pre-activation belongs to an MLP

@@ -97,6 +97,13 @@ def test_7b_prefill_full_size_sampled():
     _run_and_compare(w, rows=synth.sample_rows(w.T, 64))
 
 
+def test_7b_prefill_ragged_large_tiles():
+    """T = 7992: the 256 x 256 tiles (8 waves, epilogue through LDS) with a last token
+    tile of 56 rows; the sampled rows include the last token."""
+    T = 7992
+    _run_and_compare(W.PREFILL_7B_BF16, T=T, norm_params="random", rows=synth.sample_rows(T, 64))
+
+
 # ---------------------------------------------------------------------------
 # Steps on their own
 # ---------------------------------------------------------------------------
