@@ -60,34 +60,48 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
         for (int e = 0; e < 8; ++e) gacc[j][e] = bacc[j][e] = 0.f;
     }
 
-    for (int t = blockIdx.x; t < T; t += gridDim.x) {
+    // The (token, rank group) pairs of this workgroup in order; where the registers allow,
+    // software-pipelined: the loads of the next pair are in flight while the current one
+    // is reduced and stored.
+    const int ngroups = (P + GB - 1) / GB;
+    const int ntok = (int)blockIdx.x < T ? (T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    const int niter = ntok * ngroups;
+    float sg[NCH][8];
+    // Every load of a pair at once, kept in the storage format (zero past the end).
+    auto issue = [&](int it, Raw<TIO> (&rr)[GB][NCH], Raw<TIO> (&dd)[GB][NCH],
+                     Raw<TIO> (&ee)[GB][NCH]) {
+        const bool live = it < niter;
+        const int t = blockIdx.x + (it / ngroups) * gridDim.x, g0 = (it % ngroups) * GB;
         const size_t row = (size_t)t * h;
-        float sg[NCH][8];
 #pragma unroll
-        for (int j = 0; j < NCH; ++j)
+        for (int q = 0; q < GB; ++q) {
+            const int m = g0 + q;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sg[j][e] = 0.f;
-
-        for (int g0 = 0; g0 < P; g0 += GB) {
-            // Every load of the group at once, kept in the storage format.
-            Raw<TIO> rr[GB][NCH], dd[GB][NCH], ee[GB][NCH];
-#pragma unroll
-            for (int q = 0; q < GB; ++q) {
-                const int m = g0 + q;
-#pragma unroll
-                for (int j = 0; j < NCH; ++j) {
-                    if (m < P && ok[j]) {
-                        const size_t off = m * rs + row + c[j] * 8;
-                        rr[q][j].load(Rv + off);
-                        dd[q][j].load(Dv + off);
-                        if (DRv) ee[q][j].load(DRv + off); else ee[q][j].zero();
-                    } else {
-                        rr[q][j].zero();
-                        dd[q][j].zero();
-                        ee[q][j].zero();
-                    }
+            for (int j = 0; j < NCH; ++j) {
+                if (live && m < P && ok[j]) {
+                    const size_t off = m * rs + row + c[j] * 8;
+                    rr[q][j].load(Rv + off);
+                    dd[q][j].load(Dv + off);
+                    if (DRv) ee[q][j].load(DRv + off); else ee[q][j].zero();
+                } else {
+                    rr[q][j].zero();
+                    dd[q][j].zero();
+                    ee[q][j].zero();
                 }
             }
+        }
+    };
+    auto process = [&](int it, Raw<TIO> (&rr)[GB][NCH], Raw<TIO> (&dd)[GB][NCH],
+                       Raw<TIO> (&ee)[GB][NCH]) {
+        const int t = blockIdx.x + (it / ngroups) * gridDim.x, g0 = (it % ngroups) * GB;
+        const size_t row = (size_t)t * h;
+        if (g0 == 0) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sg[j][e] = 0.f;
+        }
+        {
             // Row statistics of r (fp32), as the forward normalization computes them.
             float mean[GB], inv[GB];
             {
@@ -199,25 +213,44 @@ __global__ __launch_bounds__(512) void k_psync_norm_bwd(PsyncBwdArgs a)
                     }
                 }
             }
-            // red[0] is written again by the next group's first block sum.
+            // red[0] is written again by the next pair's first block sum.
             __syncthreads();
         }
-        // Shared channels: every rank's partial receives the sum over ranks.
+        if (g0 + GB >= P) {
+            // Shared channels: every rank's partial receives the sum over ranks.
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            if (!ok[j]) continue;
-            const int l0 = c[j] * 8;
-            if (l0 >= n_s) continue;
-            for (int m = 0; m < P; ++m) {
-                const size_t off = m * rs + row + l0;
-                if (l0 + 8 <= n_s) {
-                    Vec8<TIO>::store(DZ + off, sg[j]);
-                } else {
+            for (int j = 0; j < NCH; ++j) {
+                if (!ok[j]) continue;
+                const int l0 = c[j] * 8;
+                if (l0 >= n_s) continue;
+                for (int m = 0; m < P; ++m) {
+                    const size_t off = m * rs + row + l0;
+                    if (l0 + 8 <= n_s) {
+                        Vec8<TIO>::store(DZ + off, sg[j]);
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (l0 + e < n_s) DZ[off + e] = static_cast<TIO>(sg[j][e]);
+                        for (int e = 0; e < 8; ++e)
+                            if (l0 + e < n_s) DZ[off + e] = static_cast<TIO>(sg[j][e]);
+                    }
                 }
             }
+        }
+    };
+    Raw<TIO> rA[GB][NCH], dA[GB][NCH], eA[GB][NCH];
+    if constexpr (NCH == 1 && sizeof(TIO) == 2) {
+        // Two register sets in turn (the wider shapes and fp32 have no room for them).
+        Raw<TIO> rB[GB][NCH], dB[GB][NCH], eB[GB][NCH];
+        issue(0, rA, dA, eA);
+        for (int it = 0; it < niter; it += 2) {
+            issue(it + 1, rB, dB, eB);
+            process(it, rA, dA, eA);
+            issue(it + 2, rA, dA, eA);
+            if (it + 1 < niter) process(it + 1, rB, dB, eB);
+        }
+    } else {
+        for (int it = 0; it < niter; ++it) {
+            issue(it, rA, dA, eA);
+            process(it, rA, dA, eA);
         }
     }
 
