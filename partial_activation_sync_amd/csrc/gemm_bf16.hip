@@ -15,11 +15,12 @@
 //     no ds_write); rows outside the matrices and the K tail read as zero from the
 //     buffer descriptor's range check;
 //   * two LDS stages held in two separate arrays, so the compiler can tell the stage
-//     being filled from the stage being read; one barrier per K step, half way through
-//     its last sub-step; the next step's loads are issued at the start of a step and
-//     fly while its MFMAs run;
+//     being filled from the stage being read; one barrier per K step, after its last
+//     MFMAs; the next step's loads are issued at the start of a step and fly while its
+//     MFMAs run;
 //   * the fragment reads for sub-step kk+1 are interleaved with the MFMAs of sub-step
-//     kk, and the next step's first fragments with the last MFMAs of the step;
+//     kk; the next step's first fragments are read after the barrier, while the SIMD's
+//     other wave runs its MFMAs;
 //   * LDS rows are 128 B (64 bf16) split in eight 16-byte chunks stored at
 //     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts;
 //   * the output tile is assembled in the idle LDS stages and stored in whole rows,
@@ -214,22 +215,24 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
     // One K step on stage Lb whose sub-step 0 fragments are in set 0; Ln (the other
-    // stage) receives step ks + 1.  The wait and the barrier sit half way through the
-    // last sub-step: by then step ks + 1 has had most of a step to land, and the second
-    // half of the MFMAs covers the reads of its first fragments.  At the barrier every
-    // wave's reads of Lb are complete, so the next step may refill Lb.
+    // stage) receives step ks + 1.  The wait and the barrier follow the step's last
+    // MFMAs, which gives step ks + 1 the whole step to land; the reads of its first
+    // fragments follow the barrier (the SIMD's other wave covers them; placing the
+    // barrier half way through the last sub-step, to hide them under this wave's own
+    // MFMAs, measured 1-3 % slower with two waves per SIMD).  At the barrier every wave's
+    // reads of Lb are complete, so the next step may refill Lb.
 #define CAAT_STEP_MORE(ks, Lb, Ln)                                                         \
     do {                                                                                   \
         CAAT_ISSUE(min((ks) + 1, nsteps - 1), Ln);                                         \
         CAAT_READ(1, Lb, 1); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
         CAAT_READ(0, Lb, 2); CAAT_MMA(1, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
         CAAT_READ(1, Lb, 3); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
-        CAAT_MMA(1, 0, IB / 2);                                                            \
+        CAAT_MMA(1, 0, IB);                                                                \
         CAAT_SCHED_FENCE();                                                                \
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                        \
         __builtin_amdgcn_s_barrier();                                                      \
         CAAT_SCHED_FENCE();                                                                \
-        CAAT_READ(0, Ln, 0); CAAT_MMA(1, IB / 2, IB); CAAT_INTERLEAVE(NMFMA / 2);          \
+        CAAT_READ(0, Ln, 0);                                                               \
     } while (0)
     // The last K step: no next step to load or read.
 #define CAAT_STEP_LAST(Lb)                                                                 \

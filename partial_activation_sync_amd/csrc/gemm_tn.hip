@@ -160,12 +160,12 @@ __global__ __launch_bounds__(NTH) void k_gemm_tn(TnArgs a, int tilesN, int tiles
         CAAT_READ(1, Lb, 1); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
         CAAT_READ(0, Lb, 2); CAAT_MMA(1, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
         CAAT_READ(1, Lb, 3); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
-        CAAT_MMA(1, 0, IB / 2);                                                            \
+        CAAT_MMA(1, 0, IB);                                                                \
         CAAT_SCHED_FENCE();                                                                \
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");                        \
         __builtin_amdgcn_s_barrier();                                                      \
         CAAT_SCHED_FENCE();                                                                \
-        CAAT_READ(0, Ln, 0); CAAT_MMA(1, IB / 2, IB); CAAT_INTERLEAVE(NMFMA / 2);          \
+        CAAT_READ(0, Ln, 0);                                                               \
     } while (0)
 #define CAAT_STEP_LAST(Lb)                                                                 \
     do {                                                                                   \
