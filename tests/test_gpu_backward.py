@@ -241,3 +241,44 @@ def test_stored_preactivation(act, dtype, T):
     torch.cuda.synchronize()
     for k in grads[False]:
         assert torch.equal(grads[True][k], grads[False][k]), k
+
+
+def test_stored_preactivation_large_tiles():
+    """7B dims, T = 1024: K1 runs on the 256 x 256 tiles (8 waves), whose epilogue writes
+    the gate and up pre-activations through the LDS image.  The training forward's outputs
+    equal the plain forward's bit for bit, the pre-activation matches an fp32 matmul of the
+    same bf16 inputs, and the backward fed with it equals the recomputing one bit for bit."""
+    P, T, h, ffn = 8, 1024, 4096, 11008
+    _say(f"[case] stored pre-activation, large tiles P={P} T={T} h={h} ffn={ffn}")
+    d = _inputs(P, T, h, ffn, "swiglu", "bf16", resid_given=True, dres_given=True)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in d.items()}
+    sub = caat.Sublayer(h, ffn, P, 0.5, norm="rmsnorm", act="swiglu", dtype="bf16", eps=1e-5)
+    F1 = dev["W1"].shape[1]
+    res = {}
+    for train in (False, True):
+        out = torch.empty((P, T, h), dtype=torch.bfloat16, device="cuda")
+        out_resid = torch.empty_like(out)
+        pre = torch.empty((P, T, F1), dtype=torch.bfloat16, device="cuda") if train else None
+        sub.forward(dev["x"], dev["W1"], dev["W2"], dev["gamma"], out, resid=dev["resid"],
+                    out_resid=out_resid, preact=pre)
+        res[train] = (out, out_resid, pre)
+    torch.cuda.synchronize()
+    assert torch.equal(res[True][0], res[False][0])
+    assert torch.equal(res[True][1], res[False][1])
+    pre = res[True][2]
+    ref = torch.matmul(dev["x"].float(), dev["W1"].float().transpose(1, 2).contiguous())
+    err = float((pre.float() - ref).abs().max() / ref.abs().max())
+    _say(f"   pre-activation error vs fp32 matmul {err:.2e}")
+    assert err <= TOL["bf16"]
+    grads = {}
+    for stored in (False, True):
+        g = {"dx": torch.empty_like(dev["x"]), "dresid": torch.empty((P, T, h), dtype=torch.bfloat16, device="cuda"),
+             "dW1": torch.empty_like(dev["W1"]), "dW2": torch.empty_like(dev["W2"]),
+             "dgamma": torch.empty((h,), dtype=torch.float32, device="cuda")}
+        sub.backward(dev["x"], dev["W1"], dev["W2"], dev["gamma"], res[False][1], dev["dout"],
+                     g["dx"], g["dW2"], g["dgamma"], dW1=g["dW1"], dres=dev["dres"],
+                     dresid=g["dresid"], preact=pre if stored else None)
+        grads[stored] = g
+    torch.cuda.synchronize()
+    for k in grads[False]:
+        assert torch.equal(grads[True][k], grads[False][k]), k
