@@ -15,15 +15,17 @@
 //   S^T = K Q^T     (v_mfma_f32_32x32x16_bf16, keys as rows, queries as columns), so
 //                   each lane's accumulators hold one query's scores for 16 keys and the
 //                   row statistics of the online softmax need only the lane pair l, l^32;
+//                   MFMA row rho computes key rho with bits 2 and 3 exchanged, so that
+//                   accumulator element v of lane l holds key 16 (v / 8) + 8 g + v % 8
+//                   (g = l / 32) of its 32-key block;
 //   mask keys past the query or past the sequence (only on the wave's diagonal block),
 //   update the running max in log2 units (scale log2(e)/sqrt(d) folded into the exp2
 //   argument), and rescale the output only when some query's max grew by more than 8
 //   (a stale max leaves every probability at most 2^8, which fp32 sums and bf16 holds);
 //   O^T += V^T P^T  with P^T taken straight from the S^T accumulators (bf16) as the
-//                   column operand: lane l's 8 values of a 16-key chunk are keys
-//                   4g..4g+3 and 8+4g..8+4g+3 (g = l / 32), and the V^T fragments are read
-//                   in the same key order (two 8-byte LDS reads), which sums the same
-//                   products in another order.
+//                   column operand: lane l's 8 values of a 16-key chunk are its keys
+//                   8g..8g+7, so each V^T fragment is one 16-byte LDS read of 8
+//                   consecutive keys.
 // A wave skips key blocks that lie wholly past its last query; the workgroup's loads and
 // barriers run for all of them.  The two workgroups of a CU synchronize independently, so
 // one's softmax arithmetic overlaps the other's matrix products.  Queries past the
@@ -131,6 +133,8 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
     // Running max in log2 units (score * sc) and running sum of 2^(score * sc - m_run).
     float m_run = -INFINITY, l_run = 0.f;
     const float sc = 1.44269504088896341f / sqrtf((float)D);
+    // K tile row of the lane's S^T MFMA row: bits 2 and 3 of the row exchanged.
+    const int krho = ((lane & 31) & ~12) | ((lane & 4) << 1) | ((lane & 8) >> 1);
     constexpr float RESCALE_MARGIN = 8.f;
 
     // One key block on the stage (Kb, Vb).  MASK: the block holds keys past one of the
@@ -140,7 +144,7 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
         f32x16 acc_s[2];                                                                   \
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb) {                                       \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_s[kb][v] = 0.f;                   \
-            const uint4 *krow_ = (Kb) + (kb * 32 + (lane & 31)) * KROW + g;                \
+            const uint4 *krow_ = (Kb) + (kb * 32 + krho) * KROW + g;                       \
             CAAT_UNROLL for (int kk = 0; kk < NKK; ++kk) {                                 \
                 const bf16x8 kf = __builtin_bit_cast(bf16x8, krow_[2 * kk]);               \
                 acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc_s[kb], \
@@ -151,7 +155,7 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
         CAAT_UNROLL for (int kb = 0; kb < 2; ++kb)                                         \
             CAAT_UNROLL for (int v = 0; v < 16; ++v) {                                     \
                 if (MASK) {                                                                \
-                    const int key = (kv0) + kb * 32 + 8 * (v >> 2) + 4 * g + (v & 3);      \
+                    const int key = (kv0) + kb * 32 + 16 * (v >> 3) + 8 * g + (v & 7);     \
                     if (key > ql || key >= S) acc_s[kb][v] = -INFINITY;                    \
                 }                                                                          \
                 mb = fmaxf(mb, acc_s[kb][v]);                                              \
@@ -176,12 +180,9 @@ void k_attn(AttnArgs a, int nqb, int ngrp)
                 CAAT_UNROLL for (int v = 0; v < 16; ++v) acc_o[b][v] *= alpha;             \
         }                                                                                  \
         CAAT_UNROLL for (int b = 0; b < NDB; ++b) {                                        \
-            const char *vrow = reinterpret_cast<const char *>(                             \
-                (Vb) + (b * 32 + (lane & 31)) * VROW) + 8 * g;                             \
+            const uint4 *vrow = (Vb) + (b * 32 + (lane & 31)) * VROW + g;                  \
             CAAT_UNROLL for (int kc = 0; kc < 4; ++kc) {                                   \
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (2 * kc) * 16);   \
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (2 * kc + 1) * 16); \
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)); \
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, vrow[2 * kc]);                \
                 acc_o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kc], acc_o[b],   \
                                                                    0, 0, 0);               \
             }                                                                              \
