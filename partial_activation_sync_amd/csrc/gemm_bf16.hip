@@ -10,7 +10,7 @@
 // (output channels n), the column operand the activations (tokens t), so each lane's
 // accumulator holds 4 consecutive output channels of one token and stores 8 bytes.
 //
-// Pipeline (one workgroup per BN x BT tile, K stepped by 64):
+// Pipeline (BN x BT tiles, K stepped by 64; a workgroup runs a sequence of tiles):
 //   * global -> LDS with buffer loads that write LDS directly (no staging registers,
 //     no ds_write); rows outside the matrices and the K tail read as zero from the
 //     buffer descriptor's range check;
@@ -23,9 +23,12 @@
 //     other wave runs its MFMAs;
 //   * LDS rows are 128 B (64 bf16) split in eight 16-byte chunks stored at
 //     chunk ^ f(row), which keeps the 16-byte fragment reads free of bank conflicts;
-//   * the output tile is assembled in the idle LDS stages and stored in whole rows,
-//     16 bytes per lane (an activation epilogue can store the raw pre-activation too,
-//     for a backward pass that then need not recompute it).
+//   * the output tile is assembled in LDS stage L1 and stored in whole rows, 16 bytes
+//     per lane (an activation epilogue can store the raw pre-activation too, for a
+//     backward pass that then need not recompute it), while the workgroup's next tile's
+//     first K step already loads into L0: the grid is at most one workgroup per
+//     resident slot, so a tile's prologue latency, the drain of its stores and the
+//     workgroup launch gap hide under the previous tile's epilogue.
 // Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
 // range of tiles, which share operand rows.
 //
@@ -68,14 +71,6 @@ __device__ __forceinline__ float silu(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-// Block index -> tile index.  Workgroups go round-robin to the 8 XCDs; give each XCD
-// one contiguous range of tiles.
-__device__ __forceinline__ int xcd_tile(int b, int total) {
-    const int xcd = b & 7, idx = b >> 3;
-    const int q = total >> 3, r = total & 7;
-    return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
 template <int BN, int BT, int WGN, int WGT, int EPI>
 __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int tilesN, int tilesT)
 {
@@ -97,55 +92,67 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wn = wave % WGN, wt = wave / WGN;
-    const int per = tilesN * tilesT;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int m = tile / per, rem = tile - m * per;
-    const int tn = rem % tilesN, tt = rem / tilesN;
-    const int n0 = tn * NCOL, t0 = tt * BT;
+    const int per = tilesN * tilesT, total = a.P * per;
     const int N = a.N, T = a.T, K = a.K;
 
-    const __bf16 *Wm = reinterpret_cast<const __bf16 *>(a.W) + (size_t)m * a.w_stride;
-    const __bf16 *Xm = reinterpret_cast<const __bf16 *>(a.X) + (size_t)m * a.x_stride;
+    // Tiles of this workgroup.  XCD x (= block index mod 8; workgroups go round-robin to
+    // the 8 XCDs, each with its own L2) owns the contiguous tile range [xs, xs + xc),
+    // which shares operand rows; its nx workgroups take every nx-th tile of the range.
+    // The grid never exceeds the tile count, so every workgroup has a first tile.
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int xc = (total >> 3) + (xcd < (total & 7));
+    const int xs = xcd * (total >> 3) + min(xcd, total & 7);
+    const int nx = ((int)gridDim.x >> 3) + (xcd < ((int)gridDim.x & 7));
+    if (idx >= xc) return;
+
     const int wrows = (EPI == EPI_SWIGLU) ? a.up_off + N : N;
     // One descriptor spans every K segment; a segment's offset goes in the scalar
     // offset of the load, so the per-lane offsets below stay the same for all of them.
     const int kseg = a.kseg;
-    const __amdgpu_buffer_rsrc_t rW =
-        make_rsrc(Wm, (uint32_t)(((size_t)(kseg - 1) * a.w_kseg + (size_t)wrows * K) * 2u));
-    const __amdgpu_buffer_rsrc_t rX =
-        make_rsrc(Xm, (uint32_t)(((size_t)(kseg - 1) * a.x_kseg + (size_t)T * K) * 2u));
+    const uint32_t wbytes = (uint32_t)(((size_t)(kseg - 1) * a.w_kseg + (size_t)wrows * K) * 2u);
+    const uint32_t xbytes = (uint32_t)(((size_t)(kseg - 1) * a.x_kseg + (size_t)T * K) * 2u);
 
     // Load i of a lane fills LDS slot (i*NW + wave)*64 + lane: a 64-slot block is 8
     // rows, row = 8 * block + lane / 8, and the slot holds chunk c = (lane & 7) ^ f(row)
     // with f(row) = (row & 7) ^ ((row >> 3) & 1) = (lane >> 3) ^ (block & 1).
     const int cl = (lane & 7) ^ ((lane >> 3) & 7);
-    uint32_t off[LOADS];
-    CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {
-        const int blk = i * NW + wave;
-        const int c = cl ^ (blk & 1);
-        const int row = blk * 8 + (lane >> 3);
-        uint32_t grow;
-        bool ok;
-        if (i < WLOADS) {
-            if (EPI == EPI_SWIGLU) {
-                const int b32 = row >> 5, y = n0 + (b32 >> 1) * 32 + (row & 31);
-                ok = y < N;
-                grow = (b32 & 1) ? a.up_off + y : y;
-            } else {
-                grow = n0 + row;
-                ok = (int)grow < N;
-            }
-        } else {
-            grow = t0 + row - BN;
-            ok = (int)grow < T;
-        }
-        off[i] = ok ? (grow * (uint32_t)K + c * 8) * 2u : OOB;
-    }
-
-    f32x16 acc[IB][JB];
-    CAAT_UNROLL for (int i = 0; i < IB; ++i)
-        CAAT_UNROLL for (int j = 0; j < JB; ++j)
-            CAAT_UNROLL for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    // Rank, first output column, first token, operand descriptors and per-lane load
+    // offsets of tile TI.  The lane index passes through an empty asm so that the
+    // tile-independent parts of the offsets are recomputed per tile rather than held in
+    // registers across the tile loop.
+#define CAAT_TILE_SETUP(TI, M, N0, T0, RW, RX, OFF)                                        \
+    do {                                                                                   \
+        int ln_ = lane;                                                                    \
+        asm volatile("" : "+v"(ln_));                                                      \
+        const int cl_ = (ln_ & 7) ^ ((ln_ >> 3) & 7);                                      \
+        M = (TI) / per;                                                                    \
+        const int rem_ = (TI) - M * per;                                                   \
+        N0 = (rem_ % tilesN) * NCOL;                                                       \
+        T0 = (rem_ / tilesN) * BT;                                                         \
+        RW = make_rsrc(reinterpret_cast<const __bf16 *>(a.W) + (size_t)M * a.w_stride, wbytes); \
+        RX = make_rsrc(reinterpret_cast<const __bf16 *>(a.X) + (size_t)M * a.x_stride, xbytes); \
+        CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {                                      \
+            const int blk = i * NW + wave;                                                 \
+            const int c = cl_ ^ (blk & 1);                                                 \
+            const int row = blk * 8 + (ln_ >> 3);                                          \
+            uint32_t grow;                                                                 \
+            bool ok;                                                                       \
+            if (i < WLOADS) {                                                              \
+                if (EPI == EPI_SWIGLU) {                                                   \
+                    const int b32 = row >> 5, y = (N0) + (b32 >> 1) * 32 + (row & 31);     \
+                    ok = y < N;                                                            \
+                    grow = (b32 & 1) ? a.up_off + y : y;                                   \
+                } else {                                                                   \
+                    grow = (N0) + row;                                                     \
+                    ok = (int)grow < N;                                                    \
+                }                                                                          \
+            } else {                                                                       \
+                grow = (T0) + row - BN;                                                    \
+                ok = (int)grow < T;                                                        \
+            }                                                                              \
+            OFF[i] = ok ? (grow * (uint32_t)K + c * 8) * 2u : OOB;                         \
+        }                                                                                  \
+    } while (0)
 
     // Fragment slots: a wave block's rows start at a multiple of 32, so f(row) = f(r32).
     const int r32 = lane & 31, kh = lane >> 5;
@@ -160,9 +167,10 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     const int nsteps = kseg * nk;              // K steps over all segments
     const bool ktail = (K % BK) != 0;
 
-    // Enqueue the loads of combined K step ks (segment ks / nk) into LDS stage Lb.  Only
-    // a ragged last step of a segment masks chunks past K (they read as zero).
-#define CAAT_ISSUE(ks, Lb)                                                                 \
+    // Enqueue the loads of combined K step ks (segment ks / nk) of the tile with
+    // descriptors RW, RX and offsets OFF into LDS stage Lb.  Only a ragged last step of a
+    // segment masks chunks past K (they read as zero).
+#define CAAT_ISSUE_T(ks, Lb, RW, RX, OFF)                                                  \
     do {                                                                                   \
         const int g_ = (ks) / nk;                                                          \
         const int k0_ = ((ks) - g_ * nk) * BK;                                             \
@@ -172,17 +180,19 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
             CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {                                  \
                 const int base = (i * NW + wave) * 64;                                     \
                 const int c = cl ^ ((i * NW + wave) & 1);                                  \
-                const uint32_t o = (k0_ + c * 8 < K) ? off[i] : OOB;                       \
-                load_lds16(i < WLOADS ? rW : rX, (Lb) + base, o, i < WLOADS ? sw_ : sx_);  \
+                const uint32_t o = (k0_ + c * 8 < K) ? OFF[i] : OOB;                       \
+                load_lds16(i < WLOADS ? RW : RX, (Lb) + base, o, i < WLOADS ? sw_ : sx_);  \
             }                                                                              \
         } else {                                                                           \
             CAAT_UNROLL for (int i = 0; i < LOADS; ++i)                                    \
-                load_lds16(i < WLOADS ? rW : rX, (Lb) + (i * NW + wave) * 64, off[i],      \
+                load_lds16(i < WLOADS ? RW : RX, (Lb) + (i * NW + wave) * 64, OFF[i],      \
                            i < WLOADS ? sw_ : sx_);                                        \
         }                                                                                  \
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
+#define CAAT_ISSUE(ks, Lb) CAAT_ISSUE_T(ks, Lb, rW, rX, off)
 
+    f32x16 acc[IB][JB];
     // Fragment registers: two sets, sub-steps alternate between them, carried across K
     // steps (the end of a step reads the first fragments of the next).  The reads for
     // sub-step kk+1 are interleaved with the MFMAs of sub-step kk; each sub-step is a
@@ -243,125 +253,202 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         CAAT_MMA(1, 0, IB);                                                                \
     } while (0)
 
+    // Epilogue through LDS stage L1.  Accumulator element v of block (i, j) in lane l is
+    // channel row 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.
+    // Each wave writes its outputs (bf16, after the activation) into a [token][column]
+    // image of the tile: 16-byte chunk C of image row r sits at C ^ (r & SWM), its 8-byte
+    // halves swapped when bit 4 of r is set, which keeps both the 8-byte writes and the
+    // 16-byte reads free of bank conflicts.  Then every thread stores whole 16-byte
+    // chunks, and a wave's store covers whole token rows, instead of 8 bytes in each of
+    // 32 rows.  An image larger than one stage goes through it in two passes of half the
+    // tokens each.  Meanwhile L0 receives the next tile's first K step.
+    constexpr int CPR = NCOL / 8;                    // 16-byte chunks per token row
+    constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;
+    constexpr int NPASS = (BT * CPR + SLOTS - 1) / SLOTS;
+    constexpr int PROWS = BT / NPASS;                // token rows per pass
+    static_assert(NPASS <= 2 && PROWS * CPR <= SLOTS && PROWS % WT == 0 && WT % 32 == 0,
+                  "the output image must fit one stage in at most two passes of whole waves");
+    static_assert((PROWS * CPR) % NTH == 0, "output chunks must split evenly");
+    constexpr int CPP = BN / 8;                      // pre-activation chunks per token row
+    constexpr int SWP = (CPP < 16 ? CPP : 16) - 1;
+    static_assert((BT / 2) * CPP <= SLOTS && (BT * CPP) % NTH == 0, "pre-activation image");
+
+    int tile = xs + idx;
+    int m, n0, t0;
+    __amdgpu_buffer_rsrc_t rW, rX;
+    uint32_t off[LOADS];
+    CAAT_TILE_SETUP(tile, m, n0, t0, rW, rX, off);
     CAAT_ISSUE(0, L0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    CAAT_READ(0, L0, 0);
-    // Whole pairs of steps in the loop; an odd last step follows it.  With an even
-    // count, the last step of the loop loads its own step again into the idle stage
-    // (the load index is clamped), which nothing reads: one code path reaches the
-    // epilogue from the loop and one from the last step, as few as the accumulators
-    // can take without spilling.
-    int kt = 0;
-    for (; kt + 2 <= nsteps; kt += 2) {
-        CAAT_STEP_MORE(kt, L0, L1);
-        CAAT_STEP_MORE(kt + 1, L1, L0);
+    for (;;) {
+        // The tile's first step has landed in L0; every wave has finished reading L1.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        CAAT_UNROLL for (int i = 0; i < IB; ++i)
+            CAAT_UNROLL for (int j = 0; j < JB; ++j)
+                CAAT_UNROLL for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+        CAAT_READ(0, L0, 0);
+        // Whole pairs of steps in the loop; an odd last step follows it.  With an even
+        // count, the last step of the loop loads its own step again into the idle stage
+        // (the load index is clamped), which nothing reads: one code path reaches the
+        // epilogue from the loop and one from the last step, as few as the accumulators
+        // can take without spilling.
+        int kt = 0;
+        for (; kt + 2 <= nsteps; kt += 2) {
+            CAAT_STEP_MORE(kt, L0, L1);
+            CAAT_STEP_MORE(kt + 1, L1, L0);
+        }
+        if (kt < nsteps) CAAT_STEP_LAST(L0);
+
+        // The last step may have refilled a stage nothing reads; let it land and let
+        // every wave finish its fragment reads.  Then the next tile's first step goes
+        // to L0 while this tile's outputs pass through L1.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        // Lane-derived epilogue indices from an opaque copy of the thread index, so that
+        // the compiler computes them here instead of holding them through the K loop.
+        int te = tid;
+        asm volatile("" : "+v"(te));
+        const int r32e = te & 31, khe = (te >> 5) & 1;
+        if (EPI != EPI_STORE && a.pre != nullptr) {
+            // The raw pre-activation first, through an image over both stages (the first
+            // half of the tokens in L0, the second in L1; all BN weight rows of the tile;
+            // SwiGLU: the gate columns in image chunks [0, CPR), the up columns after).
+            __bf16 *Pm = reinterpret_cast<__bf16 *>(a.pre) + (size_t)m * a.pre_stride;
+            CAAT_UNROLL for (int j = 0; j < JB; ++j) {
+                const int tb = wt * WT + j * 32;
+                uint2 *img = reinterpret_cast<uint2 *>(tb < BT / 2 ? L0 : L1);
+                const int r = tb % (BT / 2) + r32e;
+                const int sw = r & SWP, hs = (r >> 4) & 1;
+                CAAT_UNROLL for (int i = 0; i < IB; ++i) {
+                    const int b32 = (wn * WN + i * 32) / 32;          // 32-row weight block
+                    const int cb = (EPI == EPI_SWIGLU) ? (b32 & 1) * CPR + (b32 >> 1) * 4 : b32 * 4;
+                    CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                        bf16x4 o;
+                        CAAT_UNROLL for (int q = 0; q < 4; ++q) o[q] = static_cast<__bf16>(acc[i][j][4 * g + q]);
+                        img[(r * CPP + ((cb + g) ^ sw)) * 2 + (khe ^ hs)] = __builtin_bit_cast(uint2, o);
+                    }
+                }
+            }
+            __syncthreads();
+            CAAT_UNROLL for (int it = 0; it < BT * CPP / NTH; ++it) {
+                const int q = it * NTH + te;
+                const int row = q / CPP, c = q % CPP;
+                const int r = row % (BT / 2);
+                uint4 v = (row < BT / 2 ? L0 : L1)[r * CPP + (c ^ (r & SWP))];
+                if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+                const int up = (EPI == EPI_SWIGLU) && c >= CPR;
+                const int y = n0 + (c - up * CPR) * 8;
+                const int t = t0 + row;
+                if (t < T && y < N)
+                    *reinterpret_cast<uint4 *>(Pm + (size_t)t * a.ld_pre + (up ? a.up_off : 0) + y) = v;
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+
+        // The next tile's first step into L0, under this tile's output image in L1.
+        const int next = tile + nx;
+        const bool more = next < xs + xc;
+        int m2 = 0, n02 = 0, t02 = 0;
+        __amdgpu_buffer_rsrc_t rW2 = rW, rX2 = rX;
+        uint32_t off2[LOADS];
+        if (more) {
+            CAAT_TILE_SETUP(next, m2, n02, t02, rW2, rX2, off2);
+            CAAT_ISSUE_T(0, L0, rW2, rX2, off2);
+        }
+        __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
+        CAAT_UNROLL for (int ps = 0; ps < NPASS; ++ps) {
+            CAAT_UNROLL for (int j = 0; j < JB; ++j) {
+                const int tb = wt * WT + j * 32;                     // the 32 tokens' first row
+                if (tb / PROWS != ps) continue;
+                uint2 *img = reinterpret_cast<uint2 *>(L1);
+                const int r = tb % PROWS + r32e;                      // image row of the token
+                const int sw = r & SWM, hs = (r >> 4) & 1;
+                if (EPI == EPI_SWIGLU) {
+                    CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
+                        const int cb = ((wn * IB + i) >> 1) * 4;      // first chunk of the 32 columns
+                        CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                            bf16x4 o;
+                            CAAT_UNROLL for (int q = 0; q < 4; ++q)
+                                o[q] = static_cast<__bf16>(silu(acc[i][j][4 * g + q]) * acc[i + 1][j][4 * g + q]);
+                            img[(r * CPR + ((cb + g) ^ sw)) * 2 + (khe ^ hs)] = __builtin_bit_cast(uint2, o);
+                        }
+                    }
+                } else {
+                    CAAT_UNROLL for (int i = 0; i < IB; ++i) {
+                        const int cb = (wn * WN + i * 32) / 8;
+                        CAAT_UNROLL for (int g = 0; g < 4; ++g) {
+                            bf16x4 o;
+                            CAAT_UNROLL for (int q = 0; q < 4; ++q) {
+                                float v = acc[i][j][4 * g + q];
+                                if (EPI == EPI_GELU) v = gelu_erf(v);
+                                if (EPI == EPI_GELU_TANH) v = gelu_tanh(v);
+                                o[q] = static_cast<__bf16>(v);
+                            }
+                            img[(r * CPR + ((cb + g) ^ sw)) * 2 + (khe ^ hs)] = __builtin_bit_cast(uint2, o);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            CAAT_UNROLL for (int it = 0; it < PROWS * CPR / NTH; ++it) {
+                const int q = it * NTH + te;
+                const int r = q / CPR, c = q % CPR;
+                uint4 v = L1[r * CPR + (c ^ (r & SWM))];
+                if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+                const int t = t0 + ps * PROWS + r, n = n0 + c * 8;
+                if (t < T && n < N)
+                    *reinterpret_cast<uint4 *>(O + (size_t)t * a.ldo + n) = v;
+            }
+            if (ps + 1 < NPASS) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __syncthreads();
+            }
+        }
+        if (!more) break;
+        tile = next; m = m2; n0 = n02; t0 = t02; rW = rW2; rX = rX2;
+        CAAT_UNROLL for (int i = 0; i < LOADS; ++i) off[i] = off2[i];
     }
-    if (kt < nsteps) CAAT_STEP_LAST(L0);
 #undef CAAT_READ
 #undef CAAT_MMA
 #undef CAAT_INTERLEAVE
 #undef CAAT_STEP_MORE
 #undef CAAT_STEP_LAST
 #undef CAAT_ISSUE
+#undef CAAT_ISSUE_T
+#undef CAAT_TILE_SETUP
+}
 
-    // Epilogue through LDS.  Accumulator element v of block (i, j) in lane l is channel
-    // row 8 (v / 4) + 4 (l / 32) + v % 4 and token column l % 32 of that block.  Each
-    // wave writes its outputs (bf16, after the activation) into a [token][column] image
-    // of the tile in the idle LDS stages (the first half of the tokens in L0, the second
-    // in L1): 16-byte chunk C of image row r sits at C ^ (r & SWM), its 8-byte halves
-    // swapped when bit 4 of r is set, which keeps both the 8-byte writes and the 16-byte
-    // reads free of bank conflicts.  Then every thread stores whole 16-byte chunks, and a
-    // wave's store covers whole token rows, instead of 8 bytes in each of 32 rows.
-    constexpr int CPR = NCOL / 8;                    // 16-byte chunks per token row
-    constexpr int SWM = (CPR < 16 ? CPR : 16) - 1;
-    static_assert((BT / 2) * CPR <= SLOTS && WT % 32 == 0, "the output image must fit two stages");
-    static_assert((BT * CPR) % NTH == 0, "output chunks must split evenly");
-    // The last step may have refilled a stage nothing reads; let it land first.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (EPI != EPI_STORE && a.pre != nullptr) {
-        // The raw pre-activation first, through the same image (all BN weight rows of the
-        // tile; SwiGLU: the gate columns in image chunks [0, CPR), the up columns after).
-        constexpr int CPP = BN / 8;
-        constexpr int SWP = (CPP < 16 ? CPP : 16) - 1;
-        static_assert((BT / 2) * CPP <= SLOTS && (BT * CPP) % NTH == 0, "pre-activation image");
-        CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-            const int tb = wt * WT + j * 32;
-            uint2 *img = reinterpret_cast<uint2 *>(tb < BT / 2 ? L0 : L1);
-            const int r = tb % (BT / 2) + r32;
-            const int sw = r & SWP, hs = (r >> 4) & 1;
-            CAAT_UNROLL for (int i = 0; i < IB; ++i) {
-                const int b32 = (wn * WN + i * 32) / 32;          // 32-row weight block
-                const int cb = (EPI == EPI_SWIGLU) ? (b32 & 1) * CPR + (b32 >> 1) * 4 : b32 * 4;
-                CAAT_UNROLL for (int g = 0; g < 4; ++g) {
-                    bf16x4 o;
-                    CAAT_UNROLL for (int q = 0; q < 4; ++q) o[q] = static_cast<__bf16>(acc[i][j][4 * g + q]);
-                    img[(r * CPP + ((cb + g) ^ sw)) * 2 + (kh ^ hs)] = __builtin_bit_cast(uint2, o);
-                }
-            }
-        }
-        __syncthreads();
-        __bf16 *Pm = reinterpret_cast<__bf16 *>(a.pre) + (size_t)m * a.pre_stride;
-        CAAT_UNROLL for (int it = 0; it < BT * CPP / NTH; ++it) {
-            const int q = it * NTH + tid;
-            const int row = q / CPP, c = q % CPP;
-            const int r = row % (BT / 2);
-            uint4 v = (row < BT / 2 ? L0 : L1)[r * CPP + (c ^ (r & SWP))];
-            if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-            const int up = (EPI == EPI_SWIGLU) && c >= CPR;
-            const int y = n0 + (c - up * CPR) * 8;
-            const int t = t0 + row;
-            if (t < T && y < N)
-                *reinterpret_cast<uint4 *>(Pm + (size_t)t * a.ld_pre + (up ? a.up_off : 0) + y) = v;
-        }
-        __syncthreads();
-    }
-    {
-        CAAT_UNROLL for (int j = 0; j < JB; ++j) {
-            const int tb = wt * WT + j * 32;                     // the 32 tokens' first row
-            uint2 *img = reinterpret_cast<uint2 *>(tb < BT / 2 ? L0 : L1);
-            const int r = tb % (BT / 2) + r32;                   // image row of the token
-            const int sw = r & SWM, hs = (r >> 4) & 1;
-            if (EPI == EPI_SWIGLU) {
-                CAAT_UNROLL for (int i = 0; i < IB; i += 2) {
-                    const int cb = ((wn * IB + i) >> 1) * 4;      // first chunk of the 32 columns
-                    CAAT_UNROLL for (int g = 0; g < 4; ++g) {
-                        bf16x4 o;
-                        CAAT_UNROLL for (int q = 0; q < 4; ++q)
-                            o[q] = static_cast<__bf16>(silu(acc[i][j][4 * g + q]) * acc[i + 1][j][4 * g + q]);
-                        img[(r * CPR + ((cb + g) ^ sw)) * 2 + (kh ^ hs)] = __builtin_bit_cast(uint2, o);
-                    }
-                }
-            } else {
-                CAAT_UNROLL for (int i = 0; i < IB; ++i) {
-                    const int cb = (wn * WN + i * 32) / 8;
-                    CAAT_UNROLL for (int g = 0; g < 4; ++g) {
-                        bf16x4 o;
-                        CAAT_UNROLL for (int q = 0; q < 4; ++q) {
-                            float v = acc[i][j][4 * g + q];
-                            if (EPI == EPI_GELU) v = gelu_erf(v);
-                            if (EPI == EPI_GELU_TANH) v = gelu_tanh(v);
-                            o[q] = static_cast<__bf16>(v);
-                        }
-                        img[(r * CPR + ((cb + g) ^ sw)) * 2 + (kh ^ hs)] = __builtin_bit_cast(uint2, o);
-                    }
-                }
-            }
-        }
-    }
-    __syncthreads();
-    __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
-    CAAT_UNROLL for (int it = 0; it < BT * CPR / NTH; ++it) {
-        const int q = it * NTH + tid;
-        const int row = q / CPR, c = q % CPR;
-        const int r = row % (BT / 2);
-        uint4 v = (row < BT / 2 ? L0 : L1)[r * CPR + (c ^ (r & SWM))];
-        if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-        const int t = t0 + row, n = n0 + c * 8;
-        if (t < T && n < N)
-            *reinterpret_cast<uint4 *>(O + (size_t)t * a.ldo + n) = v;
-    }
+// Compute units of the current device (queried once).
+int cu_count() {
+    static const int n = [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        return cus > 0 ? cus : 256;
+    }();
+    return n;
+}
+
+// One launch of a kernel instance: at most as many workgroups as fit on the device at
+// once (each then runs a sequence of tiles), and never more than the tiles.
+template <int BN, int BT, int WGN, int WGT, int EPI>
+hipError_t launch_epi(const GemmArgs &a, int tilesN, int tilesT, hipStream_t s) {
+    constexpr int NTH = 64 * WGN * WGT;
+    static const int resident = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void *>(&k_gemm_bf16<BN, BT, WGN, WGT, EPI>), NTH,
+                0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    const long total = (long)a.P * tilesN * tilesT;
+    const long slots = (long)resident * cu_count();
+    const dim3 grid((unsigned)(total < slots ? total : slots)), block(NTH);
+    hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI>), grid, block, 0, s, a, tilesN, tilesT);
+    return hipGetLastError();
 }
 
 template <int BN, int BT, int WGN, int WGT>
@@ -369,22 +456,12 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
     const int ncol = (a.epi == EPI_SWIGLU) ? BN / 2 : BN;
     const int tilesN = (a.N + ncol - 1) / ncol;
     const int tilesT = (a.T + BT - 1) / BT;
-    const dim3 grid(a.P * tilesN * tilesT), block(64 * WGN * WGT);
     switch (a.epi) {
-    case EPI_GELU:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_GELU>), grid, block, 0, s, a, tilesN, tilesT);
-        break;
-    case EPI_GELU_TANH:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_GELU_TANH>), grid, block, 0, s, a, tilesN, tilesT);
-        break;
-    case EPI_SWIGLU:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_SWIGLU>), grid, block, 0, s, a, tilesN, tilesT);
-        break;
-    default:
-        hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI_STORE>), grid, block, 0, s, a, tilesN, tilesT);
-        break;
+    case EPI_GELU: return launch_epi<BN, BT, WGN, WGT, EPI_GELU>(a, tilesN, tilesT, s);
+    case EPI_GELU_TANH: return launch_epi<BN, BT, WGN, WGT, EPI_GELU_TANH>(a, tilesN, tilesT, s);
+    case EPI_SWIGLU: return launch_epi<BN, BT, WGN, WGT, EPI_SWIGLU>(a, tilesN, tilesT, s);
+    default: return launch_epi<BN, BT, WGN, WGT, EPI_STORE>(a, tilesN, tilesT, s);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
