@@ -324,7 +324,12 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
 // spreads over P x T workgroups instead of T.  Each workgroup reads the shared columns
 // of every rank (or S) and only its own rank's private columns and residual; the
 // shared columns are thereby read P times, which is a few MB at these sizes.
-template <int NCH, int NORM, typename TIO>
+// PM > 0 (a bound on P): every input of the thread is loaded before any is summed, so
+// the P partial loads are in flight together instead of one after another (at T = 1 the
+// kernel is a chain of memory latencies); the sum still runs over ranks in order.
+// PM = 0: the ranks' partials are loaded and summed one at a time (for the wider rows
+// whose loads would not fit in registers).
+template <int PM, int NCH, int NORM, typename TIO>
 __global__ __launch_bounds__(512) void k_psync_norm_rank(
     int P, int T, int h, int n_s, float s_priv, float eps,
     const TIO *__restrict__ partials, const TIO *__restrict__ resid,
@@ -342,6 +347,27 @@ __global__ __launch_bounds__(512) void k_psync_norm_rank(
 
     float r[NCH][8];
     float acc[1] = {0.f};
+    constexpr int PQ = PM > 0 ? PM : 1;
+    Raw<TIO> zq[PQ][NCH], zo[NCH], rs[NCH], gr[NCH], br[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int c = threadIdx.x + j * blockDim.x;
+        const int ch0 = c * 8;
+        zo[j].zero();
+        rs[j].zero();
+        gr[j].zero();
+        br[j].zero();
+        if (c >= nchunk) continue;
+        if (PM > 0 && ch0 < n_s && Sg == nullptr) {
+#pragma unroll
+            for (int q = 0; q < PQ; ++q)
+                if (q < P) zq[q][j].load(partials + q * rank_stride + row + ch0);
+        }
+        if (ch0 + 8 > n_s) zo[j].load(partials + own + ch0);
+        rs[j].load(resid + own + ch0);
+        gr[j].load(gamma + ch0);
+        if (NORM == CAAT_LAYERNORM && beta != nullptr) br[j].load(beta + ch0);
+    }
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
         const int c = threadIdx.x + j * blockDim.x;
@@ -350,19 +376,29 @@ __global__ __launch_bounds__(512) void k_psync_norm_rank(
         for (int e = 0; e < 8; ++e) r[j][e] = 0.f;
         if (c >= nchunk) continue;
         float S[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, z[8], res[8];
+        zo[j].unpack(z);
+        rs[j].unpack(res);
         if (ch0 < n_s) {
             if (Sg != nullptr) {
                 Vec8<TIO>::load(Sg + (size_t)t * s_ld + ch0, S);
+            } else if (PM > 0) {
+#pragma unroll
+                for (int q = 0; q < PQ; ++q) {
+                    if (q >= P) break;
+                    float zz[8];
+                    zq[q][j].unpack(zz);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) S[e] += zz[e];
+                }
             } else {
                 for (int q = 0; q < P; ++q) {
-                    Vec8<TIO>::load(partials + q * rank_stride + row + ch0, z);
+                    float zz[8];
+                    Vec8<TIO>::load(partials + q * rank_stride + row + ch0, zz);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) S[e] += z[e];
+                    for (int e = 0; e < 8; ++e) S[e] += zz[e];
                 }
             }
         }
-        if (ch0 + 8 > n_s) Vec8<TIO>::load(partials + own + ch0, z);
-        Vec8<TIO>::load(resid + own + ch0, res);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             r[j][e] = res[e] + ((ch0 + e < n_s) ? S[e] : s_priv * z[e]);
@@ -392,13 +428,8 @@ __global__ __launch_bounds__(512) void k_psync_norm_rank(
         if (c >= nchunk) continue;
         const int ch0 = c * 8;
         float gm[8], bt[8], o[8];
-        Vec8<TIO>::load(gamma + ch0, gm);
-        if (NORM == CAAT_LAYERNORM && beta != nullptr) {
-            Vec8<TIO>::load(beta + ch0, bt);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bt[e] = 0.f;
-        }
+        gr[j].unpack(gm);
+        br[j].unpack(bt);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = (r[j][e] - mean) * inv * gm[e] + bt[e];
         Vec8<TIO>::store(out + own + ch0, o);
@@ -428,14 +459,17 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
             int th = (nchunk + nchr - 1) / nchr;
             th = (th + 63) / 64 * 64;
             const dim3 grid_r(a.T, a.P), block_r(th);
-#define CAAT_K3R(N)                                                                          \
-    hipLaunchKernelGGL((k_psync_norm_rank<N, NORM, TIO>), grid_r, block_r, 0, s, a.P, a.T, a.h, \
+#define CAAT_K3R(PQ, N)                                                                          \
+    hipLaunchKernelGGL((k_psync_norm_rank<PQ, N, NORM, TIO>), grid_r, block_r, 0, s, a.P, a.T, a.h, \
                        a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
-            switch (nchr) {
-            case 1: CAAT_K3R(1); break;
-            case 2: CAAT_K3R(2); break;
-            default: CAAT_K3R(4); break;
-            }
+            // All partial loads up front while they fit in registers: P <= 8 with up to two
+            // chunks per thread, P <= 16 with one.
+            if (a.P <= 8 && nchr == 1) CAAT_K3R(8, 1);
+            else if (a.P <= 8 && nchr == 2) CAAT_K3R(8, 2);
+            else if (a.P <= 16 && nchr == 1) CAAT_K3R(16, 1);
+            else if (nchr == 1) CAAT_K3R(0, 1);
+            else if (nchr == 2) CAAT_K3R(0, 2);
+            else CAAT_K3R(0, 4);
 #undef CAAT_K3R
             return hipGetLastError();
         }
