@@ -444,6 +444,44 @@ def bench_block(args, w, T, p):
 COPY_BYTES = 512 << 20
 
 
+def per_gpu_share(w, T, p, steps, warmup):
+    """One rank's shard at its real shape (P_launch = 1): the kernels one GPU of a P-GPU
+    deployment would run for its share of the path (the collective itself aside).  The
+    MLP shard is a P = 1 sublayer with ffn / P channels; the out-projection's per-rank
+    GEMM (h / P -> h) is the row-parallel GEMM of a P = 1 sublayer with ffn = h / P.  K3
+    runs on the rank's own rows, with the shared channels taken from its own GEMM where
+    a deployment would take them from the exchange."""
+    import dataclasses
+    import torch
+    from partial_activation_sync_amd import runner
+    from partial_activation_sync_amd import workloads as W
+
+    shard = dataclasses.replace(w, name=w.name + "-shard", P=1, ffn=w.f_s,
+                                sublayers=(W.MLP,), replicated_x=False)
+    run = runner.Run(shard, runner.make_inputs(shard, T=T), p=p, store_resid=True)
+    ks = list(zip(("mlp.K1", "mlp.K2", "mlp.K3"), run.mlp_steps()))
+    if W.ATTN_OUT in w.sublayers:
+        proj = dataclasses.replace(shard, ffn=w.h // w.P, act="gelu")
+        prun = runner.Run(proj, runner.make_inputs(proj, T=T), p=p, store_resid=True)
+        _, k2, k3 = prun.mlp_steps()
+        ks = [("attn.K2", k2), ("attn.K3", k3)] + ks
+    for _ in range(warmup):
+        for _, k in ks:
+            k()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ks) + 1)] for _ in range(steps)]
+    for s in range(steps):
+        ev[s][0].record()
+        for i, (_, k) in enumerate(ks):
+            k()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    ms = {name: round(sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps, 4)
+          for i, (name, _) in enumerate(ks)}
+    step = sum(ev[s][0].elapsed_time(ev[s][len(ks)]) for s in range(steps)) / steps
+    return ms, step
+
+
 def calibrate_copy():
     """A plain device-to-device copy of COPY_BYTES, five times: under rocprofv3 --pmc
     its FETCH_SIZE / WRITE_SIZE per dispatch give the counters' scale factor."""
@@ -602,6 +640,38 @@ def main():
     roof["algorithmic_per_launch"] = flops if flops else nbytes
     roof["traffic"] = traffic_for(src, traffic_key(w.name, T, dom))
 
+    # Per sublayer: sum of the kernels' roofline times (each kernel at the larger of its
+    # FLOP time at the MFMA peak and its byte time at the HBM peak) over the measured time.
+    subs = {}
+    for name, ms in kern_ms.items():
+        flops, nbytes = kernel_work(w, T, name, store_resid=True, n_s=run.mlp.n_s)
+        roof_ms = max(flops / (PEAK["mfma"] * 1e12), nbytes / (PEAK["hbm"] * 1e9)) * 1e3
+        sub = "attn_out" if name.startswith("attn") else "mlp"
+        e = subs.setdefault(sub, {"ms": 0.0, "roof_ms": 0.0})
+        e["ms"] += ms
+        e["roof_ms"] += roof_ms
+    for e in subs.values():
+        e["frac"] = round(e["roof_ms"] / e["ms"], 4)
+        e["ms"] = round(e["ms"], 4)
+        e["roof_ms"] = round(e["roof_ms"], 4)
+    log(f"[bench] sublayer roofline fractions: {subs}")
+
+    # Derived, not measured: what a P-GPU deployment would exchange per rank and sublayer
+    # for the shared block (reduce-scatter + all-gather, 2 T n_s b), against a full
+    # all-reduce of all h channels.
+    b = 2 if w.dtype == "bf16" else 4
+    n_s = run.mlp.n_s
+    exchange = {"per_rank_per_sublayer_bytes": 2 * T * n_s * b,
+                "full_sync_bytes": 2 * T * w.h * b,
+                "reduction": round(1.0 - n_s / w.h, 4)}
+
+    share = None
+    if w.P > 1 and T > 64:
+        share_ms, share_step = per_gpu_share(w, T, p, K, args.warmup)
+        share = {"kernels_ms": share_ms, "step_ms": round(share_step, 4),
+                 "emulated_step_ms_per_rank": round(ms_per_step / w.P, 4)}
+        log(f"[bench] one rank's shard (P_launch = 1): {share}")
+
     base = None
     if args.cpu_budget > 0:
         log("[bench] timing the oracle on host cores ...")
@@ -621,6 +691,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": base,
         "kernels": detail,
+        "sublayers": subs,
+        "exchange_derived": exchange,
+        "per_gpu_share": share,
     }
     print(json.dumps(line), flush=True)
 
