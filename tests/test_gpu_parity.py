@@ -281,6 +281,34 @@ def test_row_gemm_reduce_matches_oracle(wname, T, p):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("P,h,T", [(8, 4096, 1), (8, 8192, 3), (16, 4096, 5), (16, 8192, 2),
+                                   (4, 16384, 2), (3, 4096, 64), (2, 264, 7)])
+def test_partial_sync_norm_small_batch(dtype, P, h, T):
+    """K3 for T <= 64 (one workgroup per token and rank) on every rank-count and row-width
+    dispatch: all of a thread's loads first for P <= 8 (one or two chunks per thread) and
+    for P <= 16 (one chunk), one rank at a time otherwise; LayerNorm with beta and a
+    private scale, against the oracle's reduce + norm."""
+    _say(f"[case] partial_sync_norm {dtype} P={P} h={h} T={T}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s = caat.Sublayer(h, 8 * P, P, 0.37, norm="layernorm", act="gelu", dtype=dtype, s_priv=1.5)
+    Z = synth.normal((P, T, h), synth.PARTIALS, dtype=dt)
+    R = synth.normal((P, T, h), synth.RESID, dtype=dt)
+    gamma = synth.normal((h,), synth.GAMMA, std=0.1, mean=1.0, dtype=dt)
+    beta = synth.normal((h,), synth.BETA, std=0.1, dtype=dt)
+    out = torch.empty((P, T, h), dtype=dt, device="cuda")
+    out_resid = torch.empty_like(out)
+    caat.caat_partial_sync_norm(s.handle, T, Z.cuda(), R.cuda(), gamma.cuda(), beta.cuda(),
+                                out, out_resid)
+    torch.cuda.synchronize()
+    ref_out, ref_res = oracle.partial_sync_norm(Z, R, gamma, beta=beta, norm=oracle.LAYERNORM,
+                                                n_s=s.n_s, s_priv=1.5)
+    from tests.oracle_ref import rel_err
+    e1, e2 = rel_err(out, ref_out), rel_err(out_resid, ref_res)
+    _say(f"   errors out {e1:.2e} out_resid {e2:.2e}")
+    assert e1 <= TOL[dtype] and e2 <= TOL[dtype], (e1, e2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("P,h,T,p", [(8, 4096, 5, 0.5), (4, 768, 33, 0.25), (2, 256, 64, 1.0),
                                      (3, 264, 7, 0.0)])
 def test_sync_norm_matches_oracle(dtype, P, h, T, p):
