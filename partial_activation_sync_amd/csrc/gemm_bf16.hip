@@ -480,11 +480,26 @@ bool gemm_bf16_supported(const GemmArgs &a) {
 // least two full waves of such tiles on the 256 CUs, or one full wave with a long
 // contraction; else 128 x 128 with 4 waves so that smaller problems still spread over
 // every CU.
+//
+// Where the big tiles would leave most of a last round empty, the small ones can finish
+// first although they run at lower efficiency: with R rounds of big tiles (one per CU)
+// against r rounds of small ones (two per CU, each a quarter of the work), the small
+// tiles take r / 2 / E128 big-tile rounds, E128 = 0.77 being their measured efficiency
+// relative to the big tiles (7B K1 shape: 939 against 1225 TFLOP/s).  They are chosen
+// when that is less (a lone 7B K1 shard: 352 big tiles, 2 rounds, against
+// 1408 small ones, 3 rounds: 177 against 186 us).
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s) {
     const int ncol256 = (a.epi == EPI_SWIGLU) ? 128 : 256;
+    const int ncol128 = (a.epi == EPI_SWIGLU) ? 64 : 128;
     const long tiles256 = (long)a.P * ((a.N + ncol256 - 1) / ncol256) * ((a.T + 255) / 256);
     const long ktot = (long)a.K * a.kseg;
-    if (tiles256 >= 512 || (tiles256 >= 256 && ktot >= 4096)) return launch<256, 256, 4, 2>(a, s);
+    if (tiles256 >= 512 || (tiles256 >= 256 && ktot >= 4096)) {
+        const long tiles128 = (long)a.P * ((a.N + ncol128 - 1) / ncol128) * ((a.T + 127) / 128);
+        const long cus = cu_count();
+        const double big = (double)((tiles256 + cus - 1) / cus);
+        const double small = (double)((tiles128 + 2 * cus - 1) / (2 * cus)) * 0.5 / 0.77;
+        if (small >= big) return launch<256, 256, 4, 2>(a, s);
+    }
     return launch<128, 128, 2, 2>(a, s);
 }
 
