@@ -581,7 +581,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    step_ms = sum(ev[s][0].elapsed_time(ev[s][nk]) for s in range(K)) / K
+    per_step = sorted(ev[s][0].elapsed_time(ev[s][nk]) for s in range(K))
+    step_ms = sum(per_step) / K
+    step_stats = {"mean": round(step_ms, 4), "median": round(per_step[K // 2] if K % 2 else
+                                                           (per_step[K // 2 - 1] + per_step[K // 2]) / 2, 4),
+                  "min": round(per_step[0], 4), "max": round(per_step[-1], 4)}
     span_ms = ev[0][0].elapsed_time(ev[K - 1][nk]) / K
     kern_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
                for i, (name, _) in enumerate(kernels)}
@@ -691,6 +695,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": base,
         "kernels": detail,
+        "step_ms_stats": step_stats,
         "sublayers": subs,
         "exchange_derived": exchange,
         "per_gpu_share": share,

@@ -53,8 +53,10 @@ def test_bench_forward_default_line():
     for k in ("value", "unit", "cores", "kind", "sample"):
         assert k in base, k
     assert base["kind"] == "oracle" and base["value"] > 0 and base["cores"] >= 1
-    for k in ("sublayers", "exchange_derived", "per_gpu_share"):
+    for k in ("sublayers", "exchange_derived", "per_gpu_share", "step_ms_stats"):
         assert d.get(k) is not None, k
+    st = d["step_ms_stats"]
+    assert st["min"] <= st["median"] <= st["max"] and st["min"] <= st["mean"] <= st["max"]
     assert d["exchange_derived"]["reduction"] == pytest.approx(1 - d["config"]["n_s"] / d["config"]["h"],
                                                                abs=1e-4)
 
