@@ -24,7 +24,6 @@ average duration again comes from the timed steps.
 Prints ONE JSON line on stdout (details on stderr).
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -102,9 +101,6 @@ def kernel_work_bwd(w, T, sub, step):
     raise KeyError(step)
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
 
 
 def traffic_key(workload, T, kernel_name):
@@ -124,6 +120,7 @@ def kernel_source(name, T):
 def traffic_for(kernel_file, key):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     measurement, if it was taken on the kernel source as it is now (else None)."""
+    from partial_activation_sync_amd.rocprof_summary import code_sha256
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -131,7 +128,7 @@ def traffic_for(kernel_file, key):
         rec = json.load(open(path)).get(key)
     except (ValueError, OSError):
         return None
-    if not rec or rec.get("source_sha256") != source_sha(kernel_file):
+    if not rec or rec.get("code_sha256") != code_sha256(kernel_file):
         return None
     return rec.get("bytes_per_launch")
 
@@ -423,9 +420,13 @@ def bench_block(args, w, T, p):
     dom = max(("qkv", "attn"), key=lambda k: ms[k])
     flops, nbytes = kernel_work_block(w, T, dom)
     achieved = flops / ms[dom] / 1e9
+    src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
+                       "attention.hip" if dom == "attn" else
+                       "gemm_decode.hip" if T <= 64 else "gemm_bf16.hip")
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK["mfma"],
             "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma"], 4), "kernel": dom,
-            "algorithmic_per_launch": flops, "traffic": None}
+            "algorithmic_per_launch": flops,
+            "traffic": traffic_for(src, traffic_key(w.name + ":block", T, dom))}
     line = {
         "metric": METRIC_BLOCK, "value": round(T / (span_ms / 1e3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(span_ms, 4),

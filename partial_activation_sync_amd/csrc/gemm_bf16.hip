@@ -27,8 +27,9 @@
 //     per lane (an activation epilogue can store the raw pre-activation too, for a
 //     backward pass that then need not recompute it), while the workgroup's next tile's
 //     first K step already loads into L0: the grid is at most one workgroup per
-//     resident slot, so a tile's prologue latency, the drain of its stores and the
-//     workgroup launch gap hide under the previous tile's epilogue.
+//     resident slot, so a tile's prologue latency and the workgroup launch gap hide
+//     under the previous tile's epilogue (the wait for those first loads still covers
+//     the previous tile's stores: vector loads and stores share one counter).
 // Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
 // range of tiles, which share operand rows.
 //

@@ -2,15 +2,18 @@
 
     python -m partial_activation_sync_amd.rocprof_summary stats <dir> <title> <command>
     python -m partial_activation_sync_amd.rocprof_summary traffic <fetch_dir> <write_dir>
-           <copy_fetch_dir> <copy_write_dir> <copy_bytes> <kernel_regex> <key> <source_file>
+           <copy_fetch_dir> <copy_write_dir> <copy_bytes> <select> <key> <source_file>
 
 ``stats`` prints a markdown table of per-kernel call counts and durations from the
 ``*_kernel_stats.csv`` of a ``--kernel-trace --stats`` run.  ``traffic`` reads the
 ``*_counter_collection.csv`` of four ``--pmc`` runs (FETCH_SIZE and WRITE_SIZE, in KiB
-per dispatch, for the kernel and for a plain copy of known size), scales each counter
+per dispatch, for the kernel and for a plain copy of known size), takes the median over
+the dispatches ``select`` names (a kernel-name regex, or a sequence of them with the
+index of the launch wanted; see ``_select``), scales each counter
 by the copy's known bytes / its reading, and merges the per-launch HBM bytes of the
-kernel into profiles/traffic.json under ``key``, with the SHA-256 of the kernel source
-the counters were taken on.
+kernel into profiles/traffic.json under ``key``, with the SHA-256 of the code the counters
+were taken on (the kernel source and its local headers, comments and whitespace left
+out, so that a comment edit keeps the record valid).
 """
 import csv
 import glob
@@ -22,6 +25,39 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+_TOKENS = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|\s+|[^\s"\'/]+|.',
+                     re.S)
+
+
+def _code(path):
+    text = open(path, encoding="utf-8").read()
+    out = []
+    for m in _TOKENS.finditer(text):
+        t = m.group(0)
+        out.append(" " if t.startswith("//") or t.startswith("/*") or t.isspace() else t)
+    return re.sub(r" +", " ", "".join(out)).strip()
+
+
+def code_sha256(path):
+    """SHA-256 of a C/C++/HIP source and the local headers it includes (``#include "..."``,
+    followed recursively), with comments dropped and each run of whitespace made one
+    space: it changes when the code does, not when only a comment does."""
+    seen, order, todo = set(), [], [os.path.abspath(path)]
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.add(f)
+        code = _code(f)
+        order.append(code)
+        for inc in re.findall(r'# ?include "([^"]+)"', code):
+            for g in (os.path.join(os.path.dirname(f), inc), os.path.join(ROOT, "include", inc)):
+                if os.path.exists(g):
+                    todo.append(os.path.abspath(g))
+                    break
+    return hashlib.sha256("\n".join(order).encode()).hexdigest()
 
 
 def _one(pattern):
@@ -45,29 +81,49 @@ def stats(d, title, command):
     return "\n".join(out) + "\n"
 
 
-def _counter(d, name, kernel_regex):
-    vals = []
-    for r in csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))):
-        if r["Counter_Name"] == name and re.search(kernel_regex, r["Kernel_Name"]):
-            vals.append(float(r["Counter_Value"]) * 1024.0)   # KiB -> bytes
+def _select(rows, select):
+    """The dispatches that ``select`` names, in dispatch order.  ``select`` is a kernel-name
+    regex (every matching dispatch), or ``re_0;re_1;...;re_m@i``: each run of m + 1
+    consecutive dispatches whose names match re_0 .. re_m in turn gives its i-th one (a
+    launch picked out by its neighbours, where one kernel serves several steps)."""
+    pats, _, idx = select.partition("@")
+    pats = [re.compile(x) for x in pats.split(";")]
+    idx = int(idx or 0)
+    if not 0 <= idx < len(pats):
+        raise ValueError(f"index {idx} outside the sequence {select}")
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    out, j = [], 0
+    while j + len(pats) <= len(rows):
+        if all(p.search(rows[j + k]["Kernel_Name"]) for k, p in enumerate(pats)):
+            out.append(rows[j + idx])
+            j += len(pats)
+        else:
+            j += 1
+    return out
+
+
+def _counter(d, name, select):
+    rows = [r for r in csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv"))))
+            if r["Counter_Name"] == name]
+    vals = [float(r["Counter_Value"]) * 1024.0 for r in _select(rows, select)]   # KiB -> bytes
     if not vals:
-        raise ValueError(f"no {name} rows for {kernel_regex} in {d}")
+        raise ValueError(f"no {name} rows for {select} in {d}")
     return statistics.median(vals), len(vals)
 
 
-def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, kernel_regex, key, src):
+def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, select, key, src):
     copy_bytes = float(copy_bytes)
     cf, _ = _counter(cfetch_dir, "FETCH_SIZE", "copy|Copy|elementwise")
     cw, _ = _counter(cwrite_dir, "WRITE_SIZE", "copy|Copy|elementwise")
-    kf, nf = _counter(fetch_dir, "FETCH_SIZE", kernel_regex)
-    kw, nw = _counter(write_dir, "WRITE_SIZE", kernel_regex)
+    kf, nf = _counter(fetch_dir, "FETCH_SIZE", select)
+    kw, nw = _counter(write_dir, "WRITE_SIZE", select)
     sf, sw = copy_bytes / cf, copy_bytes / cw
     rec = {
         "fetch_bytes": kf * sf, "write_bytes": kw * sw,
         "bytes_per_launch": kf * sf + kw * sw,
         "fetch_scale": sf, "write_scale": sw,
-        "dispatches": [nf, nw], "kernel_regex": kernel_regex,
-        "source_sha256": hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest(),
+        "dispatches": [nf, nw], "kernel_regex": select,
+        "code_sha256": code_sha256(os.path.join(ROOT, src)),
         "source": src,
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")

@@ -74,3 +74,32 @@ def test_bench_refuses_more_than_one_gpu():
     r = _bench("--gpus", "2", timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stdout + r.stderr
+
+
+def test_code_sha_ignores_comments_only(tmp_path):
+    """The stored HBM-traffic record stays valid across comment edits of the kernel source
+    and lapses when its code changes."""
+    from partial_activation_sync_amd.rocprof_summary import code_sha256
+    base = 'int f(int a) {\n  // sum\n  return a + 1; /* one */\n}\nconst char *s = "// kept";\n'
+    variants = {
+        "same": base,
+        "comment": base.replace("// sum", "// the sum of a and one").replace("/* one */", ""),
+        "blank": base.replace("\n  return", "\n\n      return"),
+        "code": base.replace("a + 1", "a + 2"),
+        "string": base.replace('"// kept"', '"// gone"'),
+    }
+    sha = {}
+    for k, text in variants.items():
+        f = tmp_path / f"{k}.hip"
+        f.write_text(text)
+        sha[k] = code_sha256(str(f))
+    assert sha["same"] == sha["comment"] == sha["blank"]
+    assert sha["code"] != sha["same"] and sha["string"] != sha["same"]
+    # A local header the source includes is part of its code.
+    (tmp_path / "h.h").write_text("#define ONE 1 // one\n")
+    (tmp_path / "m.hip").write_text('#include "h.h"\nint g() { return ONE; }\n')
+    before = code_sha256(str(tmp_path / "m.hip"))
+    (tmp_path / "h.h").write_text("#define ONE 1 /* still one */\n")
+    assert code_sha256(str(tmp_path / "m.hip")) == before
+    (tmp_path / "h.h").write_text("#define ONE 2\n")
+    assert code_sha256(str(tmp_path / "m.hip")) != before
