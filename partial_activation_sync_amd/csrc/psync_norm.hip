@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void k_psync_norm(
 // sum S, the residual rows r = resid + z and the row statistics are then computed
 // from registers (r is recomputed rather than kept, which is a few VALU ops), with one
 // block reduction of a P-vector per statistic.  One memory round trip per token.
-template <int PMAX, int NCH, int NORM, typename TIO>
+template <int PMAX, int NCH, int NORM, typename TIO, bool NT>
 __global__ __launch_bounds__(512) void k_psync_norm_1p(
     int P, int T, int h, int n_s, float s_priv, float eps,
     const TIO *__restrict__ partials, const TIO *__restrict__ resid,
@@ -190,6 +190,17 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
     const TIO *__restrict__ Sg, int s_ld)
 {
     __shared__ float red[2][MAX_WAVES_1P * PMAX];
+    // NT: the rows are read and written with the nontemporal forms (launches that move
+    // more than the last-level cache holds); otherwise the ordinary forms, which are
+    // faster on rows a previous kernel left in the caches.
+    auto ld = [&](Raw<TIO> &x, const TIO *q) {
+        if constexpr (NT) x.load_nt(q);
+        else x.load(q);
+    };
+    auto st = [&](TIO *q, const float (&v)[8]) {
+        if constexpr (NT) Vec8<TIO>::store_nt(q, v);
+        else Vec8<TIO>::store(q, v);
+    };
     const int t = blockIdx.x;
     const int nchunk = h >> 3;
     const size_t rank_stride = (size_t)T * h;
@@ -209,7 +220,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
     Raw<TIO> zr[PMAX][NCH], rr[PMAX][NCH], sr[NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j)
-        if (Sg != nullptr && valid[j] && ch0[j] < n_s) sr[j].load(Sg + (size_t)t * s_ld + ch0[j]);
+        if (Sg != nullptr && valid[j] && ch0[j] < n_s) ld(sr[j], Sg + (size_t)t * s_ld + ch0[j]);
 #pragma unroll
     for (int m = 0; m < PMAX; ++m) {
         if (m >= P) break;
@@ -217,9 +228,9 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
         for (int j = 0; j < NCH; ++j) {
             if (!valid[j]) continue;
             const size_t off = m * rank_stride + row + ch0[j];
-            if (Sg == nullptr || ch0[j] + 8 > n_s) zr[m][j].load(partials + off);
+            if (Sg == nullptr || ch0[j] + 8 > n_s) ld(zr[m][j], partials + off);
             else zr[m][j].zero();
-            rr[m][j].load(resid + off);
+            ld(rr[m][j], resid + off);
         }
     }
 
@@ -314,8 +325,8 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
             rrow(m, j, r);
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = (r[e] - mean[m]) * inv[m] * gm[e] + bt[e];
-            Vec8<TIO>::store(out + off, o);
-            if (out_resid != nullptr) Vec8<TIO>::store(out_resid + off, r);
+            st(out + off, o);
+            if (out_resid != nullptr) st(out_resid + off, r);
         }
     }
 }
@@ -486,9 +497,16 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
         int th = (nchunk + nch - 1) / nch;
         th = (th + 63) / 64 * 64;
         const dim3 block(th);
-#define CAAT_K3S(PM, N)                                                                           \
-    hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
-                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
+        // Bytes the launch reads and writes (partials, residual, two outputs), against the
+        // 256 MB Infinity Cache.
+        const bool nt = 4.0 * (double)a.P * a.T * a.h * sizeof(TIO) > 256.0 * 1024 * 1024;
+#define CAAT_K3S(PM, N)                                                                        \
+    if (nt)                                                                                    \
+        hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, true>), grid, block, 0, s, a.P, \
+                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld); \
+    else                                                                                       \
+        hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, false>), grid, block, 0, s, a.P, \
+                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
         switch (pmax * 16 + nch) {
         case 1 * 16 + 1: CAAT_K3S(1, 1); break;
         case 1 * 16 + 2: CAAT_K3S(1, 2); break;

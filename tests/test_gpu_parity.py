@@ -286,8 +286,20 @@ def test_row_gemm_reduce_matches_oracle(wname, T, p):
 def test_partial_sync_norm_small_batch(dtype, P, h, T):
     """K3 for T <= 64 (one workgroup per token and rank) on every rank-count and row-width
     dispatch: all of a thread's loads first for P <= 8 (one or two chunks per thread) and
-    for P <= 16 (one chunk), one rank at a time otherwise; LayerNorm with beta and a
-    private scale, against the oracle's reduce + norm."""
+    for P <= 16 (one chunk), one rank at a time otherwise."""
+    _partial_sync_norm_case(dtype, P, h, T)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_partial_sync_norm_streaming(dtype):
+    """K3 for T > 64 (one workgroup per token) on partials of every rank, at a size whose
+    launch moves more than 256 MB (nontemporal row loads and stores), ragged T."""
+    _partial_sync_norm_case(dtype, 8, 4096, 1100)
+
+
+def _partial_sync_norm_case(dtype, P, h, T):
+    """caat_partial_sync_norm with LayerNorm, beta and a private scale, against the
+    oracle's reduce + norm."""
     _say(f"[case] partial_sync_norm {dtype} P={P} h={h} T={T}")
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     s = caat.Sublayer(h, 8 * P, P, 0.37, norm="layernorm", act="gelu", dtype=dtype, s_priv=1.5)
@@ -310,10 +322,12 @@ def test_partial_sync_norm_small_batch(dtype, P, h, T):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("P,h,T,p", [(8, 4096, 5, 0.5), (4, 768, 33, 0.25), (2, 256, 64, 1.0),
-                                     (3, 264, 7, 0.0)])
+                                     (3, 264, 7, 0.0), (8, 4096, 1100, 0.5), (4, 2048, 300, 0.25)])
 def test_sync_norm_matches_oracle(dtype, P, h, T, p):
     """K3 on a given S and private partials equals the oracle's reduce + norm on partials
-    whose shared columns hold S on rank 0 and zeros on the other ranks."""
+    whose shared columns hold S on rank 0 and zeros on the other ranks.  T = 1100 at P = 8,
+    h = 4096 moves more than 256 MB per launch and takes the nontemporal row loads and
+    stores; T = 300 at P = 4, h = 2048 takes the ordinary ones."""
     _say(f"[case] sync_norm {dtype} P={P} h={h} T={T} p={p}")
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     s = caat.Sublayer(h, 8 * P, P, p, norm="layernorm", act="gelu", dtype=dtype, s_priv=1.5)
