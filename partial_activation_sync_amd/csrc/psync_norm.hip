@@ -175,7 +175,6 @@ __global__ __launch_bounds__(256) void k_psync_norm(
     }
 }
 
-// Raw 16-byte chunk of 8 values (bf16: one uint4; fp32: two).
 // Single-pass variant for P <= PMAX: every load of the token (all ranks' partials and
 // residuals) is issued at once into registers, in their storage format; the shared
 // sum S, the residual rows r = resid + z and the row statistics are then computed
