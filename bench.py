@@ -43,22 +43,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(w, T, name, store_resid, n_s):
-    """Algorithmic FLOPs and HBM bytes of one launch of a kernel of the path."""
+def kernel_work(w, T, name, store_resid, n_s, fused):
+    """Algorithmic FLOPs and HBM bytes of one step of the path ("attn.K2", "mlp.K1", ...),
+    or of one of the two row-parallel launches of the fused path ("mlp.K2.shared",
+    "mlp.K2.private").  fused: the library sums the shared channels inside the row GEMM
+    (caat_forward_fused) and K3 reads S [T][n_s] once plus every rank's private columns."""
     P, h, fs = w.P, w.h, w.f_s
     b = 2 if w.dtype == "bf16" else 4
     F1 = 2 * fs if w.act == "swiglu" else fs
     E = P * T * h
     if name == "mlp.K1":
         return 2.0 * P * T * h * F1, b * (P * T * h + P * F1 * h + P * T * fs)
-    # Partials written by K2 and read by K3: all P x T x h values, or, on the fused path
-    # (n_s % 8 == 0 and T > 64), S [T][n_s] once plus the private columns of every rank.
-    part = P * T * (h - n_s) + T * n_s if (n_s % 8 == 0 and T > 64) else E
-    if name == "mlp.K2":
-        return 2.0 * P * T * fs * h, b * (P * T * fs + P * h * fs + part)
-    if name == "attn.K2":
-        k = h // P
+    part = P * T * (h - n_s) + T * n_s if fused else E
+    k = fs if name.startswith("mlp") else h // P
+    if name.endswith("K2"):
         return 2.0 * P * T * k * h, b * (P * T * k + P * h * k + part)
+    if name.endswith("K2.shared"):
+        return 2.0 * P * T * k * n_s, b * (P * T * k + P * n_s * k + T * n_s)
+    if name.endswith("K2.private"):
+        return (2.0 * P * T * k * (h - n_s),
+                b * (P * T * k + P * (h - n_s) * k + P * T * (h - n_s)))
     if name.endswith("K3"):
         return 0.0, b * (part + E + E + (E if store_resid else 0) + 2 * h)
     raise KeyError(name)
@@ -107,11 +111,13 @@ def traffic_key(workload, T, kernel_name):
     return f"{workload}:T={T}:{kernel_name}"
 
 
-def kernel_source(name, T):
-    """The source file of the kernel a step launches (GEMMs at T <= 64 tokens take the
-    weight-streaming decode kernels)."""
+def kernel_source(name, T, dtype):
+    """The source file of the kernel a step launches (fp32 GEMMs: the FMA kernel; bf16
+    GEMMs at T <= 64 tokens: the weight-streaming decode kernels)."""
     if name.endswith("K3"):
         f = "psync_norm.hip"
+    elif dtype != "bf16":
+        f = "gemm_f32.hip"
     else:
         f = "gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"
     return os.path.join(ROOT, "partial_activation_sync_amd", "csrc", f)
@@ -151,16 +157,17 @@ def cpu_baseline(w, inputs, p, budget_s):
     for _ in range(2):
         rows = synth.sample_rows(T, n)
         t0 = time.perf_counter()
-        reference(w, inputs, rows=rows, p=p)
+        ref = reference(w, inputs, rows=rows, p=p)
         dt = time.perf_counter() - t0
         if dt >= 0.6 * budget_s or n >= T:
             break
         n = int(min(T, n * budget_s / max(dt, 1e-9)))
     del torch
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(),
+    base = {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"{len(rows)} of {T} token rows of {w.name} (all {w.P} ranks, every "
                       f"sublayer), fp64, {dt:.1f} s; rows are independent, so tokens/s = rows / s"}
+    return base, rows, ref
 
 
 def cpu_baseline_backward(w, inputs, p, budget_s):
@@ -445,42 +452,119 @@ def bench_block(args, w, T, p):
 COPY_BYTES = 512 << 20
 
 
+def _events(n):
+    """n timing events, each recorded once so that torch creates its HIP event."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()
+    return ev
+
+
+def timed_steps(run, K, warmup, rotate=1):
+    """K steps of Run.step through caat_forward_timed: the library records an event after
+    each of its steps (FWD_STEPS) on the stream it launches on.  Returns the per-step
+    wall span (ms, from the first step's start to the last step's end, / K), the sorted
+    per-step durations, and {sublayer: {step: mean ms}} over the K steps."""
+    import torch
+    import partial_activation_sync_amd as caat
+
+    subs = (["attn"] if run.attn is not None else []) + ["mlp"]
+    n = len(caat.FWD_STEPS)
+    for i in range(warmup):
+        run.step(copy=i % rotate)
+    torch.cuda.synchronize()
+    start = _events(K)
+    ev = [{sub: _events(n) for sub in subs} for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        start[k].record()
+        raw = {sub: [e.cuda_event for e in ev[k][sub]] for sub in subs}
+        run.step(events_attn=raw.get("attn"), events_mlp=raw["mlp"], copy=k % rotate)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    last = ev[K - 1][subs[-1]][n - 1]
+    span = start[0].elapsed_time(last) / K
+    per_step = sorted(start[k].elapsed_time(ev[k][subs[-1]][n - 1]) for k in range(K))
+    ms = {sub: {name: 0.0 for name in caat.FWD_STEPS} for sub in subs}
+    for k in range(K):
+        prev = start[k]
+        for sub in subs:
+            for i, name in enumerate(caat.FWD_STEPS):
+                ms[sub][name] += prev.elapsed_time(ev[k][sub][i]) / K
+                prev = ev[k][sub][i]
+    return span, per_step, ms, wall / K
+
+
+def launch_names(sub, fused, n_s, h):
+    """{FWD_STEPS name: reported kernel name} for the steps of a sublayer that launch a
+    kernel (the out-projection has no K1; the fused path splits K2 into two launches,
+    the shared one absent at n_s = 0 and the private one at n_s = h)."""
+    out = {}
+    if sub == "mlp":
+        out["K1"] = "mlp.K1"
+    if fused:
+        if n_s > 0:
+            out["K2"] = f"{sub}.K2.shared"
+        if n_s < h:
+            out["K2_private"] = f"{sub}.K2.private"
+    else:
+        out["K2"] = f"{sub}.K2"
+    out["K3"] = f"{sub}.K3"
+    return out
+
+
 def per_gpu_share(w, T, p, steps, warmup):
     """One rank's shard at its real shape (P_launch = 1): the kernels one GPU of a P-GPU
     deployment would run for its share of the path (the collective itself aside).  The
     MLP shard is a P = 1 sublayer with ffn / P channels; the out-projection's per-rank
-    GEMM (h / P -> h) is the row-parallel GEMM of a P = 1 sublayer with ffn = h / P.  K3
-    runs on the rank's own rows, with the shared channels taken from its own GEMM where
-    a deployment would take them from the exchange."""
+    GEMM (h / P -> h) is the row-parallel GEMM of a P = 1 sublayer with ffn = h / P, whose
+    first GEMM is not counted.  K3 runs on the rank's own rows, with the shared channels
+    taken from its own GEMM where a deployment would take them from the exchange."""
     import dataclasses
-    import torch
     from partial_activation_sync_amd import runner
     from partial_activation_sync_amd import workloads as W
 
     shard = dataclasses.replace(w, name=w.name + "-shard", P=1, ffn=w.f_s,
                                 sublayers=(W.MLP,), replicated_x=False)
-    run = runner.Run(shard, runner.make_inputs(shard, T=T), p=p, store_resid=True)
-    ks = list(zip(("mlp.K1", "mlp.K2", "mlp.K3"), run.mlp_steps()))
+    runs = [("mlp", runner.Run(shard, runner.make_inputs(shard, T=T), p=p, store_resid=True))]
     if W.ATTN_OUT in w.sublayers:
         proj = dataclasses.replace(shard, ffn=w.h // w.P, act="gelu")
-        prun = runner.Run(proj, runner.make_inputs(proj, T=T), p=p, store_resid=True)
-        _, k2, k3 = prun.mlp_steps()
-        ks = [("attn.K2", k2), ("attn.K3", k3)] + ks
-    for _ in range(warmup):
-        for _, k in ks:
-            k()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ks) + 1)] for _ in range(steps)]
-    for s in range(steps):
-        ev[s][0].record()
-        for i, (_, k) in enumerate(ks):
-            k()
-            ev[s][i + 1].record()
-    torch.cuda.synchronize()
-    ms = {name: round(sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps, 4)
-          for i, (name, _) in enumerate(ks)}
-    step = sum(ev[s][0].elapsed_time(ev[s][len(ks)]) for s in range(steps)) / steps
-    return ms, step
+        runs.insert(0, ("attn", runner.Run(proj, runner.make_inputs(proj, T=T), p=p,
+                                           store_resid=True)))
+    ms = {}
+    for sub, run in runs:
+        _, _, st, _ = timed_steps(run, steps, warmup)
+        st = st["mlp"]
+        if sub == "attn":
+            ms["attn.K2"] = st["K2"] + st["K2_private"]
+            ms["attn.K3"] = st["K3"]
+        else:
+            ms["mlp.K1"] = st["K1"]
+            ms["mlp.K2"] = st["K2"] + st["K2_private"]
+            ms["mlp.K3"] = st["K3"]
+    return {k: round(v, 4) for k, v in ms.items()}, sum(ms.values())
+
+
+def source_sha():
+    """The git commit when the tree is a checkout, else None; and a SHA-256 over the
+    library's sources, its header and this script, which identifies the code either way."""
+    import hashlib
+    import subprocess
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                              text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        head = None
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "partial_activation_sync_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files += [os.path.join(ROOT, "include", "caat.h"), os.path.abspath(__file__)]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return head, h.hexdigest()
 
 
 def calibrate_copy():
@@ -517,6 +601,8 @@ def main():
                          "recompute it with a GEMM")
     ap.add_argument("--pass", dest="pass_", choices=("forward", "backward", "block"), default="forward",
                     help="time the forward (default) or the backward of the path")
+    ap.add_argument("--no-share", action="store_true",
+                    help="skip the one-rank (P_launch = 1) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (HBM counter calibration)")
     args = ap.parse_args()
@@ -542,6 +628,8 @@ def main():
         return bench_backward(args, w, T, p)
     if args.pass_ == "block":
         return bench_block(args, w, T, p)
+    import partial_activation_sync_amd as caat
+
     log(f"[bench] {w.name} T={T} p={p} P={w.P} h={w.h} ffn={w.ffn} act={w.act} norm={w.norm}")
     t0 = time.perf_counter()
     inputs = runner.make_inputs(w, T=T)
@@ -551,45 +639,29 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s); "
         f"weights {wbytes / 1e6:.1f} MB x {rotate} copies")
-
-    def kernel_list(copy):
-        ks = []
-        if run.attn is not None:
-            k2, k3 = run.attn_steps(copy)
-            ks += [("attn.K2", k2), ("attn.K3", k3)]
-        k1, k2, k3 = run.mlp_steps(copy)
-        ks += [("mlp.K1", k1), ("mlp.K2", k2), ("mlp.K3", k3)]
-        return ks
-
-    lists = [kernel_list(c) for c in range(rotate)]
-    kernels = lists[0]
-
-    for i in range(args.warmup):
-        for _, k in lists[i % rotate]:
-            k()
-    torch.cuda.synchronize()
+    n_s = run.mlp.n_s
+    subs = (["attn"] if run.attn is not None else []) + ["mlp"]
+    # The path the library takes for each sublayer (the fused row-parallel GEMM or not),
+    # asked of it.
+    handles = {"attn": run.attn, "mlp": run.mlp}
+    fused = {sub: caat.caat_forward_fused(handles[sub].handle, T) for sub in subs}
 
     K = args.steps
-    nk = len(kernels)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for s in range(K):
-        ev[s][0].record()
-        for i, (_, k) in enumerate(lists[s % rotate]):
-            k()
-            ev[s][i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    per_step = sorted(ev[s][0].elapsed_time(ev[s][nk]) for s in range(K))
-    step_ms = sum(per_step) / K
-    step_stats = {"mean": round(step_ms, 4), "median": round(per_step[K // 2] if K % 2 else
-                                                           (per_step[K // 2 - 1] + per_step[K // 2]) / 2, 4),
+    span_ms, per_step, step_ms, wall = timed_steps(run, K, args.warmup, rotate)
+    step_mean = sum(per_step) / K
+    step_stats = {"mean": round(step_mean, 4),
+                  "median": round(per_step[K // 2] if K % 2 else
+                                  (per_step[K // 2 - 1] + per_step[K // 2]) / 2, 4),
                   "min": round(per_step[0], 4), "max": round(per_step[-1], 4)}
-    span_ms = ev[0][0].elapsed_time(ev[K - 1][nk]) / K
-    kern_ms = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)) / K
-               for i, (name, _) in enumerate(kernels)}
+    # Per launch (the fused K2 is two launches), and per step of the method (K2 whole).
+    launch_ms, kern_ms = {}, {}
+    for sub in subs:
+        for step, name in launch_names(sub, fused[sub], n_s, w.h).items():
+            launch_ms[name] = step_ms[sub][step]
+        if sub == "mlp":
+            kern_ms["mlp.K1"] = step_ms[sub]["K1"]
+        kern_ms[f"{sub}.K2"] = step_ms[sub]["K2"] + step_ms[sub]["K2_private"]
+        kern_ms[f"{sub}.K3"] = step_ms[sub]["K3"]
     ms_per_step = span_ms
     eager_ms = span_ms
 
@@ -600,89 +672,105 @@ def main():
         for c in range(rotate):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _, k in lists[c]:
-                    k()
+                run.step(copy=c)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % rotate].replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for s in range(K):
-            graphs[s % rotate].replay()
+        for k in range(K):
+            graphs[k % rotate].replay()
         e1.record()
         torch.cuda.synchronize()
         ms_per_step = e0.elapsed_time(e1) / K
         log(f"[bench] {K} graph replays: {ms_per_step:.4f} ms/step (eager {eager_ms:.4f})")
     value = T / (ms_per_step / 1e3)
-    log(f"[bench] {K} steps: {eager_ms:.4f} ms/step (events), wall {wall / K * 1e3:.3f} ms/step")
+    log(f"[bench] {K} steps: {eager_ms:.4f} ms/step (events), wall {wall * 1e3:.3f} ms/step")
 
-    detail = {}
-    for name, ms in kern_ms.items():
-        flops, nbytes = kernel_work(w, T, name, store_resid=True, n_s=run.mlp.n_s)
-        d = {"ms": round(ms, 4), "share": round(ms / step_ms, 3)}
+    work = lambda name: kernel_work(w, T, name, store_resid=True, n_s=n_s,
+                                    fused=fused[name.split(".")[0]])
+
+    def describe(name, ms):
+        flops, nbytes = work(name)
+        d = {"ms": round(ms, 4), "share": round(ms / step_mean, 3)}
         if flops:
             d["TFLOP/s"] = round(flops / ms / 1e9, 1)
             d["mfma_frac"] = round(flops / ms / 1e9 / PEAK["mfma"], 3)
         d["GB/s"] = round(nbytes / ms / 1e6, 1)
         d["hbm_frac"] = round(nbytes / ms / 1e6 / PEAK["hbm"], 3)
-        detail[name] = d
-        log(f"[bench]   {name:8s} {ms:8.4f} ms  {d}")
+        return d
 
-    dom = max(kern_ms, key=kern_ms.get)
-    flops, nbytes = kernel_work(w, T, dom, store_resid=True, n_s=run.mlp.n_s)
-    src = kernel_source(dom, T)
+    detail = {name: describe(name, ms) for name, ms in kern_ms.items()}
+    for name, ms in launch_ms.items():
+        if name not in detail:
+            detail[name] = describe(name, ms)
+    for name, d in detail.items():
+        log(f"[bench]   {name:16s} {d['ms']:8.4f} ms  {d}")
+
+    # The roofline object is the dominant single launch's.
+    dom = max(launch_ms, key=launch_ms.get)
+    flops, nbytes = work(dom)
+    src = kernel_source(dom, T, w.dtype)
     ridge = PEAK["mfma"] * 1e12 / (PEAK["hbm"] * 1e9)   # FLOP per byte where the roofs meet
     if flops and flops / nbytes >= ridge:
-        achieved = flops / kern_ms[dom] / 1e9
+        achieved = flops / launch_ms[dom] / 1e9
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK["mfma"],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma"], 4)}
     else:
-        achieved = nbytes / kern_ms[dom] / 1e6
+        achieved = nbytes / launch_ms[dom] / 1e6
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"],
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm"], 4)}
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = flops if flops else nbytes
     roof["traffic"] = traffic_for(src, traffic_key(w.name, T, dom))
 
-    # Per sublayer: sum of the kernels' roofline times (each kernel at the larger of its
-    # FLOP time at the MFMA peak and its byte time at the HBM peak) over the measured time.
-    subs = {}
-    for name, ms in kern_ms.items():
-        flops, nbytes = kernel_work(w, T, name, store_resid=True, n_s=run.mlp.n_s)
+    # Per sublayer: sum of the launches' roofline times (each at the larger of its FLOP
+    # time at the MFMA peak and its byte time at the HBM peak) over the measured time.
+    sublayers = {}
+    for name, ms in launch_ms.items():
+        flops, nbytes = work(name)
         roof_ms = max(flops / (PEAK["mfma"] * 1e12), nbytes / (PEAK["hbm"] * 1e9)) * 1e3
-        sub = "attn_out" if name.startswith("attn") else "mlp"
-        e = subs.setdefault(sub, {"ms": 0.0, "roof_ms": 0.0})
+        e = sublayers.setdefault("attn_out" if name.startswith("attn") else "mlp",
+                                 {"ms": 0.0, "roof_ms": 0.0})
         e["ms"] += ms
         e["roof_ms"] += roof_ms
-    for e in subs.values():
+    for e in sublayers.values():
         e["frac"] = round(e["roof_ms"] / e["ms"], 4)
         e["ms"] = round(e["ms"], 4)
         e["roof_ms"] = round(e["roof_ms"], 4)
-    log(f"[bench] sublayer roofline fractions: {subs}")
+    log(f"[bench] sublayer roofline fractions: {sublayers}")
 
     # Derived, not measured: what a P-GPU deployment would exchange per rank and sublayer
     # for the shared block (reduce-scatter + all-gather, 2 T n_s b), against a full
     # all-reduce of all h channels.
     b = 2 if w.dtype == "bf16" else 4
-    n_s = run.mlp.n_s
     exchange = {"per_rank_per_sublayer_bytes": 2 * T * n_s * b,
                 "full_sync_bytes": 2 * T * w.h * b,
                 "reduction": round(1.0 - n_s / w.h, 4)}
 
     share = None
-    if w.P > 1 and T > 64:
+    if w.P > 1 and T > 64 and not args.no_share:
         share_ms, share_step = per_gpu_share(w, T, p, K, args.warmup)
         share = {"kernels_ms": share_ms, "step_ms": round(share_step, 4),
                  "emulated_step_ms_per_rank": round(ms_per_step / w.P, 4)}
         log(f"[bench] one rank's shard (P_launch = 1): {share}")
 
-    base = None
+    base, parity = None, None
     if args.cpu_budget > 0:
         log("[bench] timing the oracle on host cores ...")
-        base = cpu_baseline(w, inputs, p, args.cpu_budget)
+        base, rows, ref = cpu_baseline(w, inputs, p, args.cpu_budget)
         log(f"[bench] cpu baseline: {base}")
+        # The timed run's own outputs (the last step read weight copy (K - 1) % rotate;
+        # every copy holds the same values) on the oracle's sampled rows.
+        from tests.oracle_ref import TOL, compare
+        errs = compare(w, run.outputs(), ref, rows=rows)
+        parity = {"rows": len(rows), "tol": TOL[w.dtype],
+                  "max_abs_err_over_max_abs": {k: float(f"{v:.3e}") for k, v in errs.items()},
+                  "ok": all(v <= TOL[w.dtype] for v in errs.values())}
+        log(f"[bench] parity of the timed outputs against the oracle: {parity}")
 
+    head, code_sha = source_sha()
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -690,16 +778,20 @@ def main():
         "dtype": w.dtype, "data": "synthetic: seeded N(0,1) activations, N(0,0.02^2) weights",
         "config": {"workload": w.name, "P": w.P, "h": w.h, "ffn": w.ffn, "T": T, "p": p,
                    "weight_copies": rotate, "hip_graph": bool(args.graph),
-                   "n_s": run.mlp.n_s, "act": w.act, "norm": w.norm,
+                   "n_s": n_s, "fused_row_gemm": fused, "act": w.act, "norm": w.norm,
                    "sublayers": list(w.sublayers),
                    "parallelism": f"tp{w.P} emulated on 1 GPU"},
         "roofline": roof,
         "cpu_baseline": base,
+        "parity": parity,
         "kernels": detail,
         "step_ms_stats": step_stats,
-        "sublayers": subs,
+        "sublayers": sublayers,
         "exchange_derived": exchange,
         "per_gpu_share": share,
+        "git_sha": head,
+        "code_sha256": code_sha,
+        "entry_point": "caat_forward_timed (= caat_forward_ex with step events)",
     }
     print(json.dumps(line), flush=True)
 

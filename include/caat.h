@@ -42,6 +42,11 @@
  *     launch; a call that returns an error has enqueued nothing.  A failed launch
  *     returns CAAT_EDEVICE.  Faults during execution surface at the caller's next
  *     synchronisation of the stream.  No C++ exception crosses this interface.
+ *     Two environment variables, read on the host by every call that would launch
+ *     (after its argument checks, before any HIP call), force the device error paths
+ *     for tests: CAAT_FAULT=launch makes the call return CAAT_EDEVICE, as a failed
+ *     launch does, with nothing enqueued; CAAT_ARCH=<gfx name> other than gfx950
+ *     makes it return CAAT_EUNSUPPORTED, as on another architecture.
  *   Concurrency: calls on one handle that overlap on different streams must use
  *     different workspaces (one handle per stream).
  */
@@ -126,6 +131,27 @@ typedef struct {
  * out-projection (CAAT_NONE) must come through here, since its input is not [P][T][h]. */
 int caat_forward_ex(caat_handle handle, const caat_args *args);
 
+/* The steps of a sublayer forward, in launch order (for caat_forward_timed's events):
+ *   0 column-parallel GEMM + activation (nothing for CAAT_NONE)
+ *   1 row-parallel GEMM: every rank's partials, or, on the fused path (n_s % 8 == 0,
+ *     T > 64), the GEMM whose accumulators sum the shared channels over the ranks
+ *   2 fused path: the GEMM of the private channels (nothing otherwise)
+ *   3 partial channel-reduce (or S on the fused path), private scaling, residual, norm */
+#define CAAT_FWD_STEPS 4
+
+/* Which row-parallel path a forward over T tokens takes: 1 when the shared channels
+ * are summed over the ranks inside the GEMM (steps 1 and 2 above, then K3 on S), 0 when
+ * every rank's partials are written and K3 sums them; CAAT_EINVAL for a NULL handle or
+ * T < 1.  Host only. */
+int caat_forward_fused(caat_handle handle, int T);
+
+/* caat_forward_ex that also records caller-created hipEvent_t events[k] on the stream
+ * after step k (k < n_events; a NULL entry is skipped), so that a caller can time each
+ * step of exactly this call.  The kernels and the results are those of caat_forward_ex.
+ * CAAT_EINVAL for n_events < 0, or n_events > 0 with events == NULL. */
+int caat_forward_timed(caat_handle handle, const caat_args *args, void *const *events,
+                       int n_events);
+
 /* caat_forward_ex for training (MLP only): the same outputs, and preact [P][T][F1]
  * (caller-owned, 16-byte aligned) receives the raw pre-activation x W1^T (SwiGLU: the
  * gate columns [0, f_s), then the up columns), the operand of sigma' in the backward of
@@ -151,7 +177,9 @@ int caat_row_gemm(caat_handle handle, int T, const void *in, const void *W2, voi
  *   partials [P][T][h] columns [n_s, h) only: Zt_m[t][l],            l >= n_s
  * Columns [0, n_s) of partials are not written.  S may be NULL when n_s == 0 and
  * partials may be NULL when n_s == h.  Needs n_s % 8 == 0, else CAAT_EUNSUPPORTED.
- * caat_forward / caat_forward_ex take this path when n_s % 8 == 0 and T > 64. */
+ * caat_forward / caat_forward_ex take this path when n_s % 8 == 0 and T > 64, unless
+ * the concatenated contraction is too long for the kernel's 32-bit offsets (bf16: past
+ * 2^31 bytes of P T k2 inputs, where this call returns CAAT_EUNSUPPORTED). */
 int caat_row_gemm_reduce(caat_handle handle, int T, const void *in, const void *W2, void *S,
                          void *partials, void *stream);
 

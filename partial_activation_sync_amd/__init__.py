@@ -66,6 +66,7 @@ class caat_block_args(ctypes.Structure):
                 ("n_events", ctypes.c_int)]
 
 
+FWD_STEPS = ("K1", "K2", "K2_private", "K3")
 BLOCK_STEPS = ("qkv", "vT", "attn", "attn_sublayer", "mlp_sublayer")
 BWD_STEPS = ("norm", "W2T", "dY", "a", "act", "W1T", "dx", "daT_xT", "dW1", "YT_dZtT", "dW2")
 
@@ -90,6 +91,9 @@ def lib():
         L.caat_set_workspace.argtypes = [vp, vp, sz]
         L.caat_forward.argtypes = [vp, i, vp, vp, vp, vp, vp, vp]
         L.caat_forward_ex.argtypes = [vp, ctypes.POINTER(caat_args)]
+        L.caat_forward_timed.argtypes = [vp, ctypes.POINTER(caat_args),
+                                         ctypes.POINTER(ctypes.c_void_p), i]
+        L.caat_forward_fused.argtypes = [vp, i]
         L.caat_forward_train.argtypes = [vp, ctypes.POINTER(caat_args), vp]
         L.caat_column_gemm_act.argtypes = [vp, i, vp, vp, vp, vp]
         L.caat_row_gemm.argtypes = [vp, i, vp, vp, vp, vp]
@@ -110,7 +114,9 @@ def lib():
         L.caat_error_string.restype = ctypes.c_char_p
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
-                     "caat_forward_ex", "caat_forward_train", "caat_column_gemm_act",
+                     "caat_forward_ex", "caat_forward_timed", "caat_forward_fused",
+                     "caat_forward_train",
+                     "caat_column_gemm_act",
                      "caat_row_gemm",
                      "caat_partial_sync_norm", "caat_row_gemm_reduce", "caat_sync_norm",
                      "caat_backward", "caat_partial_sync_norm_backward", "caat_attention",
@@ -198,6 +204,26 @@ def caat_forward_ex(handle, T, inp, W1, W2, gamma, out, resid=None, beta=None, o
     a = caat_args(int(T), _ptr(inp), _ptr(resid), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(beta),
                   _ptr(out), _ptr(out_resid), _stream(stream))
     return _check(lib().caat_forward_ex(handle, ctypes.byref(a)), "caat_forward_ex")
+
+
+def caat_forward_fused(handle, T) -> bool:
+    """Whether a forward over T tokens sums the shared channels inside the row GEMM."""
+    rc = lib().caat_forward_fused(handle, int(T))
+    if rc < 0:
+        raise CaatError("caat_forward_fused", rc)
+    return bool(rc)
+
+
+def caat_forward_timed(handle, T, inp, W1, W2, gamma, out, events, resid=None, beta=None,
+                       out_resid=None, stream=None):
+    """caat_forward_ex that records raw hipEvent_t handles (ints; None entries skipped)
+    after each of FWD_STEPS."""
+    a = caat_args(int(T), _ptr(inp), _ptr(resid), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(beta),
+                  _ptr(out), _ptr(out_resid), _stream(stream))
+    ev = (ctypes.c_void_p * len(events))(*events)
+    return _check(lib().caat_forward_timed(handle, ctypes.byref(a),
+                                           ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)),
+                                           len(events)), "caat_forward_timed")
 
 
 def caat_forward_train(handle, T, inp, W1, W2, gamma, out, preact, resid=None, beta=None,
@@ -345,9 +371,11 @@ class Sublayer:
             raise ValueError(f"{name}: dtype {t.dtype}, expected {self.torch_dtype}")
 
     def forward(self, inp, W1, W2, gamma, out, resid=None, beta=None, out_resid=None, stream=None,
-                preact=None):
+                preact=None, events=None):
         """preact (MLP only): a [P][T][F1] tensor that also receives the raw pre-activation
-        (caat_forward_train), for a backward that then skips its recompute GEMM."""
+        (caat_forward_train), for a backward that then skips its recompute GEMM.
+        events: raw hipEvent_t handles recorded after each of FWD_STEPS
+        (caat_forward_timed)."""
         P, h = self.P, self.h
         T = inp.shape[1]
         self._expect(inp, (P, T, self.kin), "in")
@@ -365,8 +393,14 @@ class Sublayer:
             if self.act == NONE:
                 raise ValueError("preact: the out-projection has no pre-activation")
             self._expect(preact, (P, T, F1), "preact")
+            if events is not None:
+                raise ValueError("events: not with preact")
             return caat_forward_train(self.handle, T, inp, W1, W2, gamma, out, preact,
                                       resid=resid, beta=beta, out_resid=out_resid, stream=stream)
+        if events is not None:
+            return caat_forward_timed(self.handle, T, inp, W1 if self.act != NONE else None, W2,
+                                      gamma, out, events, resid=resid, beta=beta,
+                                      out_resid=out_resid, stream=stream)
         return caat_forward_ex(self.handle, T, inp, W1 if self.act != NONE else None, W2, gamma,
                                out, resid=resid, beta=beta, out_resid=out_resid, stream=stream)
 

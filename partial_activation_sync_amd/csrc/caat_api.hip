@@ -7,6 +7,7 @@
 // (residual + normalization), with every rank on one device (§3.2, logical devices).
 #include <math.h>
 #include <new>
+#include <stdlib.h>
 #include <string.h>
 
 #include "caat_internal.h"
@@ -18,8 +19,19 @@ namespace {
 constexpr int MAX_DEVICES = 64;
 int g_arch_ok[MAX_DEVICES];  // 0 unknown, 1 gfx950, -1 other
 
-// Whether the current device is gfx950; cached per device ordinal.
+// Whether the current device is gfx950; cached per device ordinal.  Two host-side test
+// hooks come first, read from the environment on every call before any HIP call, so that
+// the error paths can be driven without a fault on the GPU:
+//   CAAT_FAULT=launch   the call fails as a failed launch does (CAAT_EDEVICE), having
+//                       enqueued nothing;
+//   CAAT_ARCH=<name>    the device is taken to be that architecture: anything but gfx950
+//                       gives CAAT_EUNSUPPORTED (gfx950 falls through to the real query).
 int device_check() {
+    const char *fault = getenv("CAAT_FAULT");
+    if (fault != nullptr && strcmp(fault, "launch") == 0) return CAAT_EDEVICE;
+    const char *arch = getenv("CAAT_ARCH");
+    if (arch != nullptr && arch[0] != '\0' && strncmp(arch, "gfx950", 6) != 0)
+        return CAAT_EUNSUPPORTED;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return CAAT_EDEVICE;
     if (dev < 0 || dev >= MAX_DEVICES) return CAAT_EUNSUPPORTED;
@@ -51,7 +63,6 @@ bool fused_ok(const caat_ctx *c) { return c->n_s % 8 == 0; }
 // shared columns of every rank (T x n_s x (P - 1) values written and read).  Decode
 // batches (T <= 64) keep the per-rank GEMM: their partials are a few MB, and the
 // single shared GEMM would spread its weight stream over too few workgroups.
-bool fused_for(const caat_ctx *c, int T) { return fused_ok(c) && T > 64; }
 size_t s_bytes(const caat_ctx *c, int T) {
     return fused_ok(c) ? align256((size_t)T * c->n_s * esize(c)) : 0;
 }
@@ -132,6 +143,17 @@ caat::GemmArgs private_args(const caat_ctx *c, int T, const void *in, const void
 }
 
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s);
+
+// The fused path needs its K-concatenated GEMM to stay within the bf16 kernel's 32-bit
+// byte offsets (the X span is P T k2 elements); past that the per-rank GEMM, whose spans
+// are P times shorter, still runs.
+bool fused_for(const caat_ctx *c, int T) {
+    if (!fused_ok(c) || T <= 64) return false;
+    if (c->dtype == CAAT_BF16 && c->n_s > 0 &&
+        !caat::gemm_bf16_supported(shared_args(c, T, nullptr, nullptr, nullptr)))
+        return false;
+    return true;
+}
 
 // Row-parallel GEMM with the shared channels reduced over ranks inside the GEMM.
 int run_row_reduce(const caat_ctx *c, int T, const void *in, const void *W2, void *S, void *Z,
@@ -248,8 +270,10 @@ CAAT_API int caat_set_workspace(caat_handle handle, void *dev_ptr, size_t bytes)
 namespace {
 
 // The forward of one sublayer; preact (nullable, MLP only) also receives the raw
-// pre-activation x W1^T, [P][T][F1].
-int forward_impl(caat_handle c, const caat_args *a, void *preact) {
+// pre-activation x W1^T, [P][T][F1].  events (nullable): hipEvent_t recorded on the
+// stream after each step (CAAT_FWD_STEPS), for the caller's timing.
+int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *events,
+                 int n_events) {
     if (c == nullptr || a == nullptr) return CAAT_EINVAL;
     const int T = a->T;
     if (T < 1) return CAAT_EINVAL;
@@ -259,6 +283,7 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact) {
     if (!aligned16_or_null(a->resid) || !aligned16_or_null(a->beta) ||
         !aligned16_or_null(a->out_resid))
         return CAAT_EINVAL;
+    if (n_events < 0 || (n_events > 0 && events == nullptr)) return CAAT_EINVAL;
     const void *resid = a->resid;
     if (resid == nullptr) {
         if (c->act == CAAT_NONE) return CAAT_EINVAL;  // H is [P][T][h/P]: not a residual
@@ -271,11 +296,18 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact) {
     if (rc != CAAT_OK) return rc;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(a->stream);
+    auto mark = [&](int k) -> int {
+        if (k >= n_events || events[k] == nullptr) return CAAT_OK;
+        return hipEventRecord(reinterpret_cast<hipEvent_t>(events[k]), s) == hipSuccess
+                   ? CAAT_OK : CAAT_EDEVICE;
+    };
+#define CAAT_TRY(call) do { const int rc_ = (call); if (rc_ != CAAT_OK) return rc_; } while (0)
     char *ws = reinterpret_cast<char *>(c->ws);
     void *Y = ws;
     void *Z = ws + y_bytes(c, T);
     void *S = ws + y_bytes(c, T) + partial_bytes(c, T);
     const void *gemm_in = a->in;
+    // 0: the column-parallel GEMM and its activation (MLP only).
     if (c->act != CAAT_NONE) {
         caat::GemmArgs g = col_args(c, T, a->in, a->W1, Y);
         if (preact != nullptr) {
@@ -284,33 +316,51 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact) {
                 g.pre = preact; g.pre_stride = (size_t)T * c->F1; g.ld_pre = c->F1;
             } else {
                 // Other kernels: the same contraction as the backward's recompute.
-                rc = run_gemm(c, preact_args(c, T, a->W1, a->in, preact), s);
-                if (rc != CAAT_OK) return rc;
+                CAAT_TRY(run_gemm(c, preact_args(c, T, a->W1, a->in, preact), s));
             }
         }
-        rc = run_gemm(c, g, s);
-        if (rc != CAAT_OK) return rc;
+        CAAT_TRY(run_gemm(c, g, s));
         gemm_in = Y;
     }
+    CAAT_TRY(mark(0));
     if (fused_for(c, T)) {
-        rc = run_row_reduce(c, T, gemm_in, a->W2, S, Z, s);
-        if (rc != CAAT_OK) return rc;
-        return run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s, S);
+        // 1, 2: the shared channels summed over ranks inside one GEMM, then the private
+        // channels of every rank; 3: reduce-free K3 on S and the private partials.
+        if (c->n_s > 0) CAAT_TRY(run_gemm(c, shared_args(c, T, gemm_in, a->W2, S), s));
+        CAAT_TRY(mark(1));
+        if (c->n_s < c->h) CAAT_TRY(run_gemm(c, private_args(c, T, gemm_in, a->W2, Z), s));
+        CAAT_TRY(mark(2));
+        CAAT_TRY(run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s, S));
+        return mark(3);
     }
-    rc = run_gemm(c, row_args(c, T, gemm_in, a->W2, Z), s);
-    if (rc != CAAT_OK) return rc;
-    return run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s);
+    // 1: every rank's partials; 3: the partial channel-reduce, residual and norm.
+    CAAT_TRY(run_gemm(c, row_args(c, T, gemm_in, a->W2, Z), s));
+    CAAT_TRY(mark(1));
+    CAAT_TRY(mark(2));
+    CAAT_TRY(run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s));
+    return mark(3);
+#undef CAAT_TRY
 }
 
 }  // namespace
 
 CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
-    return forward_impl(c, a, nullptr);
+    return forward_impl(c, a, nullptr, nullptr, 0);
+}
+
+CAAT_API int caat_forward_fused(caat_handle c, int T) {
+    if (c == nullptr || T < 1) return CAAT_EINVAL;
+    return fused_for(c, T) ? 1 : 0;
+}
+
+CAAT_API int caat_forward_timed(caat_handle c, const caat_args *a, void *const *events,
+                                int n_events) {
+    return forward_impl(c, a, nullptr, events, n_events);
 }
 
 CAAT_API int caat_forward_train(caat_handle c, const caat_args *a, void *preact) {
     if (c == nullptr || c->act == CAAT_NONE || !aligned16(preact)) return CAAT_EINVAL;
-    return forward_impl(c, a, preact);
+    return forward_impl(c, a, preact, nullptr, 0);
 }
 
 CAAT_API int caat_forward(caat_handle c, int T, const void *x, const void *W1, const void *W2,

@@ -17,8 +17,7 @@ import torch
 
 from . import synth
 from .workloads import ATTN_OUT, MLP, Workload
-from . import (Sublayer, caat_column_gemm_act, caat_partial_sync_norm, caat_row_gemm,
-               caat_row_gemm_reduce, caat_sync_norm)
+from . import Sublayer
 
 WEIGHT_STD = 0.02
 
@@ -83,18 +82,23 @@ class Run:
         self.out = torch.empty((P, T, h), dtype=dt, device=device)
         self.out_resid = torch.empty((P, T, h), dtype=dt, device=device) if store_resid else None
 
-    def step(self, stream=None, preact=None):
-        """One forward of the whole path (out-projection sublayer, then the MLP).  preact:
-        a [P][T][F1] tensor that receives the MLP's pre-activation (a training forward)."""
-        d = self.dev
+    def step(self, stream=None, preact=None, events_attn=None, events_mlp=None, copy=0):
+        """One forward of the whole path (out-projection sublayer, then the MLP), through
+        caat_forward_ex, or caat_forward_timed when events are given (raw hipEvent_t
+        handles recorded after each of the library's FWD_STEPS of that sublayer).
+        preact: a [P][T][F1] tensor that receives the MLP's pre-activation (a training
+        forward).  copy: which weight copy to read (see weight_copies)."""
+        d = dict(self.dev, **self.weight_sets[copy])
         if self.attn is not None:
             self.attn.forward(d["ctx"], None, d["Wo"], d["gamma"], self.attn_out, resid=d["x0"],
-                              beta=d["beta"], out_resid=self.attn_out_resid, stream=stream)
+                              beta=d["beta"], out_resid=self.attn_out_resid, stream=stream,
+                              events=events_attn)
             mlp_in, mlp_resid = self.attn_out, self.attn_out_resid
         else:
             mlp_in, mlp_resid = d["x"], d["x"]
         self.mlp.forward(mlp_in, d["W1"], d["W2"], d["gamma"], self.out, resid=mlp_resid,
-                         beta=d["beta"], out_resid=self.out_resid, stream=stream, preact=preact)
+                         beta=d["beta"], out_resid=self.out_resid, stream=stream, preact=preact,
+                         events=events_mlp)
 
     def outputs(self):
         o = {"out": self.out}
@@ -104,54 +108,6 @@ class Run:
             o["attn_out"] = self.attn_out
             o["attn_out_resid"] = self.attn_out_resid
         return o
-
-    # The steps of each sublayer as separate calls, for per-kernel timing.  They are the
-    # calls caat_forward_ex makes: K1, the row-parallel GEMM with the shared channels
-    # reduced inside it (when n_s % 8 == 0 and T > 64; else the plain one), and K3.
-    def _buffers(self, sub, kin):
-        key = id(sub)
-        if not hasattr(self, "_bufs"):
-            self._bufs = {}
-        if key not in self._bufs:
-            P, T, h, dt = self.w.P, self.T, self.w.h, torch_dtype(self.w)
-            dev = self.out.device
-            self._bufs[key] = {
-                "Y": torch.empty((P, T, kin), dtype=dt, device=dev) if kin else None,
-                "Z": torch.empty((P, T, h), dtype=dt, device=dev),
-                "S": torch.empty((T, max(sub.n_s, 8)), dtype=dt, device=dev),
-            }
-        return self._bufs[key]
-
-    def _row_and_norm(self, sub, inp, W2, resid, gamma, beta, out, out_resid, b):
-        T = self.T
-        if sub.n_s % 8 == 0 and T > 64:   # the path caat_forward_ex takes
-            S = b["S"] if sub.n_s > 0 else None
-            Z = b["Z"] if sub.n_s < self.w.h else None
-            k2 = lambda: caat_row_gemm_reduce(sub.handle, T, inp, W2, S, Z)
-            k3 = lambda: caat_sync_norm(sub.handle, T, S, Z, resid, gamma, beta, out, out_resid)
-        else:
-            Z = b["Z"]
-            k2 = lambda: caat_row_gemm(sub.handle, T, inp, W2, Z)
-            k3 = lambda: caat_partial_sync_norm(sub.handle, T, Z, resid, gamma, beta, out, out_resid)
-        return k2, k3
-
-    def mlp_steps(self, copy=0):
-        """Callables for K1, K2 and K3 of the MLP sublayer."""
-        d, s = dict(self.dev, **self.weight_sets[copy]), self.mlp
-        b = self._buffers(s, self.w.f_s)
-        mlp_in = self.attn_out if self.attn is not None else d["x"]
-        mlp_resid = self.attn_out_resid if self.attn is not None else d["x"]
-        k1 = lambda: caat_column_gemm_act(s.handle, self.T, mlp_in, d["W1"], b["Y"])
-        k2, k3 = self._row_and_norm(s, b["Y"], d["W2"], mlp_resid, d["gamma"], d["beta"],
-                                    self.out, self.out_resid, b)
-        return k1, k2, k3
-
-    def attn_steps(self, copy=0):
-        """Callables for K2 and K3 of the out-projection sublayer."""
-        d, s = dict(self.dev, **self.weight_sets[copy]), self.attn
-        b = self._buffers(s, 0)
-        return self._row_and_norm(s, d["ctx"], d["Wo"], d["x0"], d["gamma"], d["beta"],
-                                  self.attn_out, self.attn_out_resid, b)
 
 
 class BackwardRun:

@@ -216,3 +216,110 @@ def test_error_strings():
     with pytest.raises(caat.CaatError) as e:
         caat.caat_create(7, 8, 1, 0.5, 0, 0, 1)
     assert e.value.code == caat.EINVAL
+
+
+def _launching_calls(L, hd, att, fake, ws_bytes):
+    """Every entry point that would launch, with arguments that pass their checks."""
+    caat.caat_set_workspace(hd, fake, ws_bytes)
+    caat.caat_set_workspace(att, fake, ws_bytes)
+    a = caat.caat_args(4, fake, fake, fake, fake, fake, None, fake, None, None)
+    ev = (ctypes.c_void_p * 1)(None)
+    evp = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    return {
+        "caat_forward": lambda: L.caat_forward(hd, 4, fake, fake, fake, fake, fake, None),
+        "caat_forward_ex": lambda: L.caat_forward_ex(hd, ctypes.byref(a)),
+        "caat_forward_ex (out-projection)": lambda: L.caat_forward_ex(att, ctypes.byref(a)),
+        "caat_forward_timed": lambda: L.caat_forward_timed(hd, ctypes.byref(a), evp, 1),
+        "caat_forward_train": lambda: L.caat_forward_train(hd, ctypes.byref(a), fake),
+        "caat_column_gemm_act": lambda: L.caat_column_gemm_act(hd, 4, fake, fake, fake, None),
+        "caat_row_gemm": lambda: L.caat_row_gemm(hd, 4, fake, fake, fake, None),
+        "caat_row_gemm_reduce": lambda: L.caat_row_gemm_reduce(hd, 4, fake, fake, fake, fake, None),
+        "caat_sync_norm": lambda: L.caat_sync_norm(hd, 4, fake, fake, fake, fake, None, fake,
+                                                   None, None),
+        "caat_partial_sync_norm": lambda: L.caat_partial_sync_norm(hd, 4, fake, fake, fake, None,
+                                                                   fake, None, None),
+    }
+
+
+@pytest.mark.parametrize("var,val,code", [("CAAT_ARCH", "gfx942", caat.EUNSUPPORTED),
+                                          ("CAAT_ARCH", "gfx90a", caat.EUNSUPPORTED),
+                                          ("CAAT_FAULT", "launch", caat.EDEVICE)])
+def test_device_error_hooks(monkeypatch, var, val, code):
+    """The host-side hooks drive the device error paths of every launching entry point
+    after its argument checks and before any HIP call (no GPU, nothing launched):
+    CAAT_ARCH names another architecture -> CAAT_EUNSUPPORTED, CAAT_FAULT=launch ->
+    CAAT_EDEVICE.  Argument errors still come first."""
+    L = caat.lib()
+    fake = 0x10000
+    hd = caat.caat_create(256, 1024, 2, 0.5, caat.LAYERNORM, caat.GELU, caat.BF16)
+    att = caat.caat_create(256, 0, 2, 0.5, caat.RMSNORM, caat.NONE, caat.BF16)
+    try:
+        calls = _launching_calls(L, hd, att, fake, 1 << 30)
+        monkeypatch.setenv(var, val)
+        for name, call in calls.items():
+            assert call() == code, name
+        assert L.caat_forward(hd, 0, fake, fake, fake, fake, fake, None) == caat.EINVAL
+        assert L.caat_row_gemm(hd, 4, fake + 2, fake, fake, None) == caat.EINVAL
+        caat.caat_set_workspace(hd, fake, 16)
+        assert L.caat_forward(hd, 4, fake, fake, fake, fake, fake, None) == caat.EWORKSPACE
+    finally:
+        caat.caat_destroy(hd)
+        caat.caat_destroy(att)
+
+
+def test_arch_hook_gfx950_falls_through(monkeypatch):
+    """CAAT_ARCH=gfx950 does not force success: the real device query still runs (here,
+    with no GPU, it fails with CAAT_EDEVICE; on a GPU it passes)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a GPU")
+    L = caat.lib()
+    hd = caat.caat_create(256, 1024, 2, 0.5, caat.LAYERNORM, caat.GELU, caat.BF16)
+    try:
+        caat.caat_set_workspace(hd, 0x10000, 1 << 30)
+        monkeypatch.setenv("CAAT_ARCH", "gfx950")
+        assert L.caat_forward(hd, 4, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, None) == caat.EDEVICE
+    finally:
+        caat.caat_destroy(hd)
+
+
+def test_forward_path_query():
+    """caat_forward_fused: the shared channels are summed inside the row GEMM only for
+    n_s % 8 == 0 and T > 64, and only while the K-concatenated GEMM fits the bf16
+    kernel's 32-bit offsets (P T k2 2 bytes < 2^31); otherwise the per-rank GEMM and
+    K3's reduce."""
+    L = caat.lib()
+    mlp = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+    att = caat.caat_create(4096, 0, 8, 0.5, caat.RMSNORM, caat.NONE, caat.BF16)
+    odd = caat.caat_create(4096, 11008, 8, 0.37, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+    f32 = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.F32)
+    try:
+        assert caat.caat_forward_fused(mlp, 64) is False
+        assert caat.caat_forward_fused(mlp, 65) is True
+        assert caat.caat_forward_fused(mlp, 8192) is True
+        assert caat.caat_forward_fused(odd, 8192) is False
+        limit = (1 << 31) // (8 * 1376 * 2)          # largest T with P T k2 2 < 2^31, + 1
+        assert caat.caat_forward_fused(mlp, limit - 1) is True
+        assert caat.caat_forward_fused(mlp, limit + 1) is False
+        assert caat.caat_forward_fused(att, limit + 1) is True      # k2 = h / P = 512
+        assert caat.caat_forward_fused(f32, limit + 1) is True      # the fp32 kernel
+        assert L.caat_forward_fused(None, 8) == caat.EINVAL
+        assert L.caat_forward_fused(mlp, 0) == caat.EINVAL
+    finally:
+        for hd in (mlp, att, odd, f32):
+            caat.caat_destroy(hd)
+
+
+def test_forward_timed_checks_events():
+    L = caat.lib()
+    fake = 0x10000
+    hd = caat.caat_create(256, 1024, 2, 0.5, caat.LAYERNORM, caat.GELU, caat.BF16)
+    try:
+        a = caat.caat_args(4, fake, fake, fake, fake, fake, None, fake, None, None)
+        assert L.caat_forward_timed(hd, ctypes.byref(a), None, 2) == caat.EINVAL
+        ev = (ctypes.c_void_p * 1)(None)
+        evp = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+        assert L.caat_forward_timed(hd, ctypes.byref(a), evp, -1) == caat.EINVAL
+        assert L.caat_forward_timed(hd, ctypes.byref(a), evp, 1) == caat.EWORKSPACE
+    finally:
+        caat.caat_destroy(hd)

@@ -157,30 +157,134 @@ def test_out_projection_edge_shapes(dtype):
 # ---------------------------------------------------------------------------
 # The channel mask, bit-exact; cross-rank identity at p = 1; determinism
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("P", [1, 2, 4, 8])
-@pytest.mark.parametrize("h", [256, 4096])
-def test_mask_bit_exact(dtype, P, h):
-    """Integer-coded partials Zt_m = 2^m, resid = 0: out_resid = 2^P - 1 on shared
-    channels and 2^m * s_priv on private ones, exactly (representable in bf16)."""
-    T = 3
+def _code(dtype, P, m):
+    """Integer code of rank m's partials: 2^m, whose sum over the ranks, 2^P - 1, is exact
+    in the storage dtype for P <= 8 (bf16) or P <= 16 (fp32); for bf16 with P > 8, m + 1
+    (sum P (P + 1) / 2 <= 136, exact)."""
+    return float(m + 1) if (dtype == "bf16" and P > 8) else 2.0 ** m
+
+
+def _coded_out_resid(dtype, P, T, h, n_s, s_priv, shared=None):
+    """out_resid for integer-coded partials and a zero residual: the sum of the codes on
+    the shared channels (or `shared`, when S is given), code(m) * s_priv on the private
+    ones (Eq. 22 / 24: l < floor(h p) reduced, §4 private scaling)."""
+    want = torch.empty((P, T, h), dtype=torch.float64)
+    tot = sum(_code(dtype, P, m) for m in range(P))
+    for m in range(P):
+        want[m, :, :n_s] = tot if shared is None else shared
+        want[m, :, n_s:] = _code(dtype, P, m) * s_priv
+    return want
+
+
+MASK_KERNEL_CASES = [(dt, P, h, T) for dt in ("bf16", "f32") for P in (1, 2, 4, 8)
+                     for h in (256, 4096) for T in (3, 100, 1100)
+                     if not (h == 4096 and T == 1100 and P < 8)]
+# The multi-pass K3 (rows too wide for one register pass): fp32 with P = 16, bf16 with
+# P = 16 at h = 8192, at T > 64 (and the per-rank kernel at T <= 64).
+MASK_KERNEL_CASES += [("f32", 16, 4096, 100), ("bf16", 16, 8192, 100), ("bf16", 16, 8192, 3),
+                      ("f32", 16, 4096, 3)]
+
+
+@pytest.mark.parametrize("dtype,P,h,T", MASK_KERNEL_CASES)
+def test_mask_bit_exact(dtype, P, h, T):
+    """Integer-coded partials Zt_m = code(m), resid = 0, through caat_partial_sync_norm:
+    out_resid = the codes' sum on shared channels and code(m) * s_priv on private ones,
+    exactly.  T <= 64: one workgroup per (token, rank); T > 64: one per token, with the
+    nontemporal row loads past 256 MB per launch (h = 4096, T = 1100)."""
+    _say(f"[case] mask K3 {dtype} P={P} h={h} T={T}")
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     for n_s in sorted({0, 1, 63, 64, 65, 179, h - 1, h}):
         p = n_s / h
         s = caat.Sublayer(h, 8 * P, P, p, norm="rmsnorm", act="gelu", dtype=dtype, s_priv=2.0)
         assert s.n_s == n_s
-        Z = torch.stack([torch.full((T, h), 2.0 ** m, dtype=dt) for m in range(P)]).cuda()
+        Z = torch.stack([torch.full((T, h), _code(dtype, P, m), dtype=dt, device="cuda")
+                         for m in range(P)])
         resid = torch.zeros((P, T, h), dtype=dt, device="cuda")
         gamma = torch.ones(h, dtype=dt, device="cuda")
         out = torch.empty_like(resid)
         out_resid = torch.empty_like(resid)
         caat.caat_partial_sync_norm(s.handle, T, Z, resid, gamma, None, out, out_resid)
         torch.cuda.synchronize()
-        want = torch.empty((P, T, h), dtype=torch.float64)
-        for m in range(P):
-            want[m, :, :n_s] = 2.0 ** P - 1
-            want[m, :, n_s:] = 2.0 ** m * 2.0
-        assert torch.equal(out_resid.double().cpu(), want), (P, h, n_s)
+        want = _coded_out_resid(dtype, P, T, h, n_s, 2.0)
+        assert torch.equal(out_resid.double().cpu(), want), (P, h, T, n_s)
+
+
+@pytest.mark.parametrize("dtype,P,h,T", [("bf16", 8, 4096, 3), ("bf16", 8, 4096, 200),
+                                         ("bf16", 8, 4096, 1100), ("f32", 16, 4096, 100),
+                                         ("bf16", 8, 16384, 100), ("f32", 4, 768, 65)])
+def test_sync_norm_mask_bit_exact(dtype, P, h, T):
+    """caat_sync_norm (shared channels from S, private ones from the partials) on integer
+    codes: out_resid = S on [0, n_s) and code(m) * s_priv on [n_s, h), exactly."""
+    _say(f"[case] mask sync_norm {dtype} P={P} h={h} T={T}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for n_s in sorted({0, 8, 64, h // 2 - 8, h // 2, h // 2 + 8, h - 8, h}):
+        s = caat.Sublayer(h, 8 * P, P, n_s / h, norm="layernorm", act="gelu", dtype=dtype,
+                          s_priv=2.0)
+        assert s.n_s == n_s
+        S = torch.full((T, max(n_s, 8)), 100.0, dtype=dt, device="cuda")
+        Z = torch.stack([torch.full((T, h), _code(dtype, P, m), dtype=dt, device="cuda")
+                         for m in range(P)])
+        Z[:, :, :n_s] = float("nan")          # the shared columns must not be read
+        resid = torch.zeros((P, T, h), dtype=dt, device="cuda")
+        gamma = torch.ones(h, dtype=dt, device="cuda")
+        out = torch.empty_like(resid)
+        out_resid = torch.empty_like(resid)
+        caat.caat_sync_norm(s.handle, T, S if n_s else None, Z if n_s < h else None, resid,
+                            gamma, None, out, out_resid)
+        torch.cuda.synchronize()
+        want = _coded_out_resid(dtype, P, T, h, n_s, 2.0, shared=100.0)
+        assert torch.equal(out_resid.double().cpu(), want), (P, h, T, n_s)
+
+
+def _forward_mask_cases():
+    cases = []
+    h = 4096
+    # bf16, P = 8: the fused path (n_s % 8 == 0: S from the K-concatenated GEMM) and the
+    # per-rank path with K3's reduce (n_s % 8 != 0), at T > 64; the decode kernels and
+    # the per-rank K3 at T = 3.
+    for T in (3, 65, 200):
+        for n_s in (0, 8, 64, 2040, 2048, 2056, h - 8, h, 1, 63, 65, 179, h - 1):
+            cases.append(("bf16", 8, h, T, n_s))
+    # The nontemporal K3 forms (more than 256 MB per launch).
+    cases += [("bf16", 8, h, 1100, 2048), ("bf16", 8, h, 1100, 2047)]
+    # Rows too wide for one register pass: the multi-pass K3.
+    for n_s in (0, 8, 8192, 8191, 16383, 16384):
+        cases.append(("bf16", 8, 16384, 100, n_s))
+    # fp32 with 16 ranks (the multi-pass K3; codes up to 2^15).
+    for n_s in (0, 8, 2048, 2047, 4095, 4096):
+        cases.append(("f32", 16, h, 100, n_s))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,P,h,T,n_s", _forward_mask_cases())
+def test_forward_mask_bit_exact(dtype, P, h, T, n_s):
+    """The whole out-projection sublayer through caat_forward_ex on integer codes: the
+    head outputs H_m have a 1 in column 0 and zeros elsewhere, and column 0 of O_m is
+    code(m), so every partial is exactly code(m) (the other weight columns meet zeros).
+    With resid = 0 and s_priv = 2, out_resid must be the codes' sum on [0, n_s) and
+    2 code(m) on [n_s, h), bit for bit, on whichever path the library takes."""
+    _say(f"[case] mask forward {dtype} P={P} h={h} T={T} n_s={n_s}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    hp = h // P
+    s = caat.Sublayer(h, 0, P, n_s / h, norm="rmsnorm", act="none", dtype=dtype, s_priv=2.0)
+    assert s.n_s == n_s
+    H = torch.zeros((P, T, hp), dtype=dt, device="cuda")
+    H[:, :, 0] = 1.0
+    Wo = torch.full((P, h, hp), 1.5, dtype=dt, device="cuda")
+    for m in range(P):
+        Wo[m, :, 0] = _code(dtype, P, m)
+    resid = torch.zeros((P, T, h), dtype=dt, device="cuda")
+    gamma = torch.ones(h, dtype=dt, device="cuda")
+    out = torch.empty_like(resid)
+    out_resid = torch.full_like(resid, float("nan"))
+    s.forward(H, None, Wo, gamma, out, resid=resid, out_resid=out_resid)
+    torch.cuda.synchronize()
+    want = _coded_out_resid(dtype, P, T, h, n_s, 2.0)
+    got = out_resid.double().cpu()
+    if not torch.equal(got, want):
+        bad = (got != want).nonzero()[:5].tolist()
+        raise AssertionError(f"fused={caat.caat_forward_fused(s.handle, T)} first bad "
+                             f"(m, t, l): {bad}")
 
 
 def test_p1_ranks_bitwise_identical():
@@ -365,15 +469,12 @@ def test_graph_replay_matches_eager():
     replays) reproduces the eager outputs bitwise."""
     w = W.with_(W.DECODE_7B_BF16, T=8)
     run = runner.Run(w, runner.make_inputs(w, norm_params="random"))
-    steps = list(run.attn_steps()) + list(run.mlp_steps())
-    for k in steps:
-        k()
+    run.step()
     torch.cuda.synchronize()
     eager = {k: v.clone() for k, v in run.outputs().items()}
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for k in steps:
-            k()
+        run.step()
     for rep in range(3):
         for v in run.outputs().values():
             v.zero_()
@@ -382,3 +483,46 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for k, v in run.outputs().items():
             assert torch.equal(v, eager[k]), (rep, k)
+
+
+@pytest.mark.parametrize("T", [8192, 1, 64])
+def test_timed_step_is_the_product_path(T):
+    """The benchmark's timed step (caat_forward_timed, events after every step) gives
+    bitwise the outputs of caat_forward_ex on the same inputs, at the 7B prefill size the
+    headline is quoted on and at decode sizes."""
+    from bench import timed_steps
+    w = W.with_(W.PREFILL_7B_BF16 if T > 64 else W.DECODE_7B_BF16, T=T)
+    _say(f"[case] timed step vs caat_forward_ex {w.name} T={T}")
+    run = runner.Run(w, runner.make_inputs(w, norm_params="random"))
+    run.step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in run.outputs().items()}
+    for v in run.outputs().values():
+        v.fill_(float("nan"))
+    timed_steps(run, 2, 0)
+    torch.cuda.synchronize()
+    for k, v in run.outputs().items():
+        assert torch.equal(v, ref[k]), k
+    assert caat.caat_forward_fused(run.mlp.handle, T) == (T > 64)
+
+
+def test_fault_hook_forces_device_error(monkeypatch):
+    """CAAT_FAULT=launch (read on the host) makes a forward return CAAT_EDEVICE with
+    nothing enqueued; CAAT_ARCH=gfx942 makes it return CAAT_EUNSUPPORTED.  The GPU does
+    not fault: no kernel is launched in either case."""
+    w = W.with_(W.MLP_1P1B_BF16, T=70)
+    run = runner.Run(w, runner.make_inputs(w))
+    run.out.fill_(7.0)
+    torch.cuda.synchronize()
+    for var, val, code in (("CAAT_FAULT", "launch", caat.EDEVICE),
+                           ("CAAT_ARCH", "gfx942", caat.EUNSUPPORTED)):
+        monkeypatch.setenv(var, val)
+        with pytest.raises(caat.CaatError) as e:
+            run.step()
+        assert e.value.code == code
+        torch.cuda.synchronize()
+        assert bool((run.out == 7.0).all()), "an erroring call enqueued work"
+        monkeypatch.delenv(var)
+    run.step()
+    torch.cuda.synchronize()
+    assert not bool((run.out == 7.0).all())
