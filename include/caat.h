@@ -139,6 +139,24 @@ int caat_forward_ex(caat_handle handle, const caat_args *args);
  *   3 partial channel-reduce (or S on the fused path), private scaling, residual, norm */
 #define CAAT_FWD_STEPS 4
 
+/* Size of the library's static device workspace (caat_forward_scratch): 64 MiB per
+ * device, enough for caat_workspace_bytes(T) of a 7B decode batch (T <= 64: under 6 MB)
+ * or a 130M-sized prefill of 4096 tokens (54 MB). */
+#define CAAT_SCRATCH_BYTES (64u << 20)
+
+/* caat_forward_ex for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels and
+ * results, with the workspace taken from a static array inside the library instead of
+ * the handle's caat_set_workspace memory.  Allocates nothing, and calls nothing that
+ * allocates.  The array is CAAT_SCRATCH_BYTES per device, created when the library's
+ * code loads on that device and held until the process ends; its device address is
+ * looked up on the first call on each device.  Returns CAAT_EWORKSPACE when
+ * caat_workspace_bytes(handle, T) exceeds CAAT_SCRATCH_BYTES.  Every call on one device
+ * shares that device's array: calls that overlap on one device (different streams,
+ * handles or threads) race on it and must be serialized by the caller (one stream is
+ * enough).  Nothing in it needs clearing between calls. */
+int caat_forward_scratch(caat_handle handle, const caat_args *args);
+
 /* Which row-parallel path a forward over T tokens takes: 1 when the shared channels
  * are summed over the ranks inside the GEMM (steps 1 and 2 above, then K3 on S), 0 when
  * every rank's partials are written and K3 sums them; CAAT_EINVAL for a NULL handle or

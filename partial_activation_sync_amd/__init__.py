@@ -94,6 +94,7 @@ def lib():
         L.caat_forward_timed.argtypes = [vp, ctypes.POINTER(caat_args),
                                          ctypes.POINTER(ctypes.c_void_p), i]
         L.caat_forward_fused.argtypes = [vp, i]
+        L.caat_forward_scratch.argtypes = [vp, ctypes.POINTER(caat_args)]
         L.caat_forward_train.argtypes = [vp, ctypes.POINTER(caat_args), vp]
         L.caat_column_gemm_act.argtypes = [vp, i, vp, vp, vp, vp]
         L.caat_row_gemm.argtypes = [vp, i, vp, vp, vp, vp]
@@ -115,6 +116,7 @@ def lib():
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
                      "caat_forward_ex", "caat_forward_timed", "caat_forward_fused",
+                     "caat_forward_scratch",
                      "caat_forward_train",
                      "caat_column_gemm_act",
                      "caat_row_gemm",
@@ -204,6 +206,18 @@ def caat_forward_ex(handle, T, inp, W1, W2, gamma, out, resid=None, beta=None, o
     a = caat_args(int(T), _ptr(inp), _ptr(resid), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(beta),
                   _ptr(out), _ptr(out_resid), _stream(stream))
     return _check(lib().caat_forward_ex(handle, ctypes.byref(a)), "caat_forward_ex")
+
+
+SCRATCH_BYTES = 64 << 20   # CAAT_SCRATCH_BYTES
+
+
+def caat_forward_scratch(handle, T, inp, W1, W2, gamma, out, resid=None, beta=None,
+                         out_resid=None, stream=None):
+    """caat_forward_ex on the library's static device workspace (no allocation; the
+    handle's workspace is not used)."""
+    a = caat_args(int(T), _ptr(inp), _ptr(resid), _ptr(W1), _ptr(W2), _ptr(gamma), _ptr(beta),
+                  _ptr(out), _ptr(out_resid), _stream(stream))
+    return _check(lib().caat_forward_scratch(handle, ctypes.byref(a)), "caat_forward_scratch")
 
 
 def caat_forward_fused(handle, T) -> bool:

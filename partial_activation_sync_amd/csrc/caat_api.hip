@@ -6,6 +6,7 @@
 // App. A.2, Eq. 22 (MLP) / Eq. 24 (attention out-projection), followed by §4, Eq. 9
 // (residual + normalization), with every rank on one device (§3.2, logical devices).
 #include <math.h>
+#include <mutex>
 #include <new>
 #include <stdlib.h>
 #include <string.h>
@@ -13,6 +14,13 @@
 #include "caat_internal.h"
 
 #define CAAT_API extern "C" __attribute__((visibility("default")))
+
+// The static workspace of caat_forward_scratch, for callers that cannot allocate: one
+// copy per device, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory, so its device address is looked up once per device (with
+// that device current, scratch_address below) and only that address is ever handed to a
+// kernel.
+static __device__ __align__(256) unsigned char scratch[CAAT_SCRATCH_BYTES];
 
 namespace {
 
@@ -269,11 +277,31 @@ CAAT_API int caat_set_workspace(caat_handle handle, void *dev_ptr, size_t bytes)
 
 namespace {
 
+std::mutex g_scratch_mu;
+void *g_scratch[MAX_DEVICES];
+
+int scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CAAT_EDEVICE;
+    if (dev < 0 || dev >= MAX_DEVICES) return CAAT_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return CAAT_EDEVICE;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return CAAT_OK;
+}
+
 // The forward of one sublayer; preact (nullable, MLP only) also receives the raw
 // pre-activation x W1^T, [P][T][F1].  events (nullable): hipEvent_t recorded on the
 // stream after each step (CAAT_FWD_STEPS), for the caller's timing.
+int scratch_address(void **out);
+
 int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *events,
-                 int n_events) {
+                 int n_events, bool static_ws = false) {
     if (c == nullptr || a == nullptr) return CAAT_EINVAL;
     const int T = a->T;
     if (T < 1) return CAAT_EINVAL;
@@ -291,9 +319,15 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
     }
     if (!t_ok(c, T)) return CAAT_EUNSUPPORTED;
     const size_t need = caat_workspace_bytes(c, T);
-    if (c->ws == nullptr || c->ws_bytes < need) return CAAT_EWORKSPACE;
+    if (static_ws ? need > CAAT_SCRATCH_BYTES : (c->ws == nullptr || c->ws_bytes < need))
+        return CAAT_EWORKSPACE;
     int rc = device_check();
     if (rc != CAAT_OK) return rc;
+    void *wsp = c->ws;
+    if (static_ws) {
+        rc = scratch_address(&wsp);
+        if (rc != CAAT_OK) return rc;
+    }
 
     hipStream_t s = reinterpret_cast<hipStream_t>(a->stream);
     auto mark = [&](int k) -> int {
@@ -302,7 +336,7 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
                    ? CAAT_OK : CAAT_EDEVICE;
     };
 #define CAAT_TRY(call) do { const int rc_ = (call); if (rc_ != CAAT_OK) return rc_; } while (0)
-    char *ws = reinterpret_cast<char *>(c->ws);
+    char *ws = reinterpret_cast<char *>(wsp);
     void *Y = ws;
     void *Z = ws + y_bytes(c, T);
     void *S = ws + y_bytes(c, T) + partial_bytes(c, T);
@@ -346,6 +380,10 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
 
 CAAT_API int caat_forward_ex(caat_handle c, const caat_args *a) {
     return forward_impl(c, a, nullptr, nullptr, 0);
+}
+
+CAAT_API int caat_forward_scratch(caat_handle c, const caat_args *a) {
+    return forward_impl(c, a, nullptr, nullptr, 0, true);
 }
 
 CAAT_API int caat_forward_fused(caat_handle c, int T) {
