@@ -601,6 +601,9 @@ def main():
                          "recompute it with a GEMM")
     ap.add_argument("--pass", dest="pass_", choices=("forward", "backward", "block"), default="forward",
                     help="time the forward (default) or the backward of the path")
+    ap.add_argument("--mlp-only", action="store_true",
+                    help="pair workloads: time the MLP sublayer alone (input and residual "
+                         "x ~ N(0,1) per rank, same shapes)")
     ap.add_argument("--no-share", action="store_true",
                     help="skip the one-rank (P_launch = 1) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -621,6 +624,8 @@ def main():
     from partial_activation_sync_amd import workloads as W
 
     w = W.ALL[args.workload]
+    if args.mlp_only:
+        w = W.with_(w, name=w.name + ":mlp-only", sublayers=(W.MLP,))
     T = args.T or w.T
     p = w.p if args.p is None else args.p
     torch.cuda.set_device(0)

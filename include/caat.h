@@ -133,8 +133,9 @@ int caat_forward_ex(caat_handle handle, const caat_args *args);
 
 /* The steps of a sublayer forward, in launch order (for caat_forward_timed's events):
  *   0 column-parallel GEMM + activation (nothing for CAAT_NONE)
- *   1 row-parallel GEMM: every rank's partials, or, on the fused path (n_s % 8 == 0,
- *     T > 64), the GEMM whose accumulators sum the shared channels over the ranks
+ *   1 row-parallel GEMM: every rank's partials, or, on the fused path (see
+ *     caat_row_gemm_reduce and caat_forward_fused), the GEMM whose accumulators sum the
+ *     shared channels over the ranks
  *   2 fused path: the GEMM of the private channels (nothing otherwise)
  *   3 partial channel-reduce (or S on the fused path), private scaling, residual, norm */
 #define CAAT_FWD_STEPS 4
@@ -195,9 +196,11 @@ int caat_row_gemm(caat_handle handle, int T, const void *in, const void *W2, voi
  *   partials [P][T][h] columns [n_s, h) only: Zt_m[t][l],            l >= n_s
  * Columns [0, n_s) of partials are not written.  S may be NULL when n_s == 0 and
  * partials may be NULL when n_s == h.  Needs n_s % 8 == 0, else CAAT_EUNSUPPORTED.
- * caat_forward / caat_forward_ex take this path when n_s % 8 == 0 and T > 64, unless
- * the concatenated contraction is too long for the kernel's 32-bit offsets (bf16: past
- * 2^31 bytes of P T k2 inputs, where this call returns CAAT_EUNSUPPORTED). */
+ * caat_forward / caat_forward_ex take this path when n_s % 8 == 0, T > 64 and the
+ * shared-channel GEMM has at least 256 output tiles of 128 x 128, ceil(n_s / 128) x
+ * ceil(T / 128) >= 256 (or n_s == 0), unless the concatenated contraction is too long
+ * for the kernel's 32-bit offsets (bf16: past 2^31 bytes of P T k2 inputs, where this
+ * call returns CAAT_EUNSUPPORTED); caat_forward_fused tells which path a T takes. */
 int caat_row_gemm_reduce(caat_handle handle, int T, const void *in, const void *W2, void *S,
                          void *partials, void *stream);
 

@@ -152,12 +152,25 @@ caat::GemmArgs private_args(const caat_ctx *c, int T, const void *in, const void
 
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s);
 
-// The fused path needs its K-concatenated GEMM to stay within the bf16 kernel's 32-bit
-// byte offsets (the X span is P T k2 elements); past that the per-rank GEMM, whose spans
-// are P times shorter, still runs.
+// Whether caat_forward_ex sums the shared channels inside the row-parallel GEMM.  The
+// fused path saves writing and reading the shared columns of P - 1 ranks, but its
+// shared-channel GEMM has only ceil(n_s / 128) x ceil(T / 128) output tiles of 128 x 128,
+// each contracting over P k2: with fewer tiles than the 256 compute units it leaves CUs
+// idle and runs slower than the per-rank GEMM, whose P-fold more tiles split that
+// contraction rank by rank (K3 then sums the ranks).  Measured on the 130M pair
+// (n_s = 384, T = 4096: 96 tiles): row GEMM 52 against 26 us for the MLP, 18 against
+// 12 us for the out-projection; on the 1.1B MLP at p = 0.5 (512 tiles) the fused one
+// is faster, 183 against 208 us.  Decode batches (T <= 64) and n_s % 8 != 0 always take
+// the per-rank path.  The K-concatenated GEMM must also stay within the bf16 kernel's
+// 32-bit byte offsets (its X span is P T k2 elements).
+constexpr long FUSED_MIN_TILES = 256;
+
 bool fused_for(const caat_ctx *c, int T) {
     if (!fused_ok(c) || T <= 64) return false;
-    if (c->dtype == CAAT_BF16 && c->n_s > 0 &&
+    if (c->n_s == 0) return true;   // no shared GEMM: the private one is the per-rank GEMM
+    const long tiles = (long)((c->n_s + 127) / 128) * ((T + 127) / 128);
+    if (tiles < FUSED_MIN_TILES) return false;
+    if (c->dtype == CAAT_BF16 &&
         !caat::gemm_bf16_supported(shared_args(c, T, nullptr, nullptr, nullptr)))
         return false;
     return true;

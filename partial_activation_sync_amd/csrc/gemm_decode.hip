@@ -232,19 +232,35 @@ hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
 
 bool gemm_decode_applies(const GemmArgs &a) { return a.T <= 64; }
 
-// One 16-row weight block (32 rows for SwiGLU: gate and up) per wave with K split over
-// 4 waves while the token blocks are few and K is long enough for every wave to keep
-// two stages in flight; otherwise two blocks per wave (each token fragment read then
-// feeds twice the weight bytes) and one wave per workgroup.
+// Launch shapes, measured on the 7B decode GEMMs (three weight copies rotated so the
+// weights stream from HBM; K1: SwiGLU, N = 1376 per rank, K = 4096; K2: N = 4096,
+// K = 1376; out-projection: N = 4096, K = 512):
+//   * few token blocks and a long K: one weight block per wave (two for SwiGLU: gate and
+//     up) with K split over 4 waves, so every wave keeps two stages in flight (K1 at
+//     T <= 16 and K2 at T <= 8: 28.1 and 16.3 us at T = 1);
+//   * otherwise each token fragment read from L2 should feed more weight rows: for the
+//     SwiGLU epilogue two blocks per wave (64 weight rows), for the plain and GeLU ones
+//     four (64 rows) once T > 8 (K2 at T = 16 / 32 / 64: 21.7 / 25.8 / 34.8 -> 19.5 /
+//     22.0 / 25.7 us; the out-projection at T = 64: 13.5 -> 10.3 us), two (with K split
+//     over 4 waves when K >= 1024) at T 9 .. 16.
 hipError_t gemm_decode_bf16(const GemmArgs &a, hipStream_t s) {
-    const int tmax = (a.epi == EPI_SWIGLU) ? 16 : 8;
     const int jb = (a.T + 15) / 16;
-    if (a.K >= 1024 && a.T <= tmax) return launch_lds<1, 1, 4>(a, s);
+    const bool glu = a.epi == EPI_SWIGLU;
+    if (glu) {
+        if (a.K >= 1024 && a.T <= 16) return launch_lds<1, 1, 4>(a, s);
+        switch (jb) {
+        case 1: return launch_lds<2, 1, 1>(a, s);
+        case 2: return launch_lds<2, 2, 1>(a, s);
+        case 3: return launch_lds<2, 3, 1>(a, s);
+        default: return launch_lds<2, 4, 1>(a, s);
+        }
+    }
+    if (a.T <= 8) return a.K >= 1024 ? launch_lds<1, 1, 4>(a, s) : launch_lds<2, 1, 1>(a, s);
     switch (jb) {
-    case 1: return launch_lds<2, 1, 1>(a, s);
-    case 2: return launch_lds<2, 2, 1>(a, s);
-    case 3: return launch_lds<2, 3, 1>(a, s);
-    default: return launch_lds<2, 4, 1>(a, s);
+    case 1: return a.K >= 1024 ? launch_lds<2, 1, 4>(a, s) : launch_lds<4, 1, 1>(a, s);
+    case 2: return launch_lds<4, 2, 1>(a, s);
+    case 3: return launch_lds<4, 3, 1>(a, s);
+    default: return launch_lds<4, 4, 1>(a, s);
     }
 }
 

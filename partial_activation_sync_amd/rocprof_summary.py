@@ -4,6 +4,17 @@
     python -m partial_activation_sync_amd.rocprof_summary traffic <fetch_dir> <write_dir>
            <copy_fetch_dir> <copy_write_dir> <copy_bytes> <select> <key> <source_file>
 
+    python -m partial_activation_sync_amd.rocprof_summary mfma <dir> <title> <command>
+           [<name regex>=<label> ...]
+
+``mfma`` reads the ``*_counter_collection.csv`` of a run with ``--pmc
+SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE``
+and prints, per dispatch of each MFMA kernel, its duration, bf16 MFMA FLOPs (MOPS x
+512), the achieved rate, the clock (GRBM_GUI_ACTIVE per XCD over the duration) and the
+MFMA utilisation (busy cycles summed over the SIMDs / (GUI_ACTIVE per XCD x SIMDs), the
+MfmaUtil expression rocprofv3 lists), medians over the dispatches with the same launch
+position in the step.
+
 ``stats`` prints a markdown table of per-kernel call counts and durations from the
 ``*_kernel_stats.csv`` of a ``--kernel-trace --stats`` run.  ``traffic`` reads the
 ``*_counter_collection.csv`` of four ``--pmc`` runs (FETCH_SIZE and WRITE_SIZE, in KiB
@@ -135,9 +146,47 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, select, ke
     return rec
 
 
+def mfma(d, title, command, labels=(), simds=1024, xcds=8):
+    """Per MFMA dispatch (in launch order within a repeating step): duration, FLOPs from
+    SQ_INSTS_VALU_MFMA_MOPS_BF16, clock and MFMA utilisation; medians by position."""
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    by = {}
+    for r in rows:
+        e = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                  "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    # The library's kernels only (torch's fills and copies set up the inputs).
+    disp = [by[k] for k in sorted(by) if "caat" in by[k]["name"]]
+    # The step repeats: find its period from the kernel-name sequence.
+    names = [re.sub(r"\(.*", "", e["name"].replace("caat::(anonymous namespace)::", "")) for e in disp]
+    period = next(p for p in range(1, len(names) + 1)
+                  if all(names[i] == names[i % p] for i in range(len(names))))
+    lab = [(re.compile(k), v) for k, v in labels]
+    out = [f"# {title}", "", f"Command: `{command}`", "",
+           "| # | kernel | step | dispatches | duration (us) | MFMA TFLOP | TFLOP/s | of 2.5 PF "
+           "| clock (GHz) | MFMA busy at that clock |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for i in range(period):
+        grp = disp[i::period]
+        if not any(e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) > 0 for e in grp):
+            continue
+        us = statistics.median(e["ns"] for e in grp) / 1e3
+        fl = statistics.median(e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for e in grp) * 512
+        gui = statistics.median(e["GRBM_GUI_ACTIVE"] for e in grp) / xcds
+        busy = statistics.median(e["SQ_VALU_MFMA_BUSY_CYCLES"] for e in grp)
+        step = next((v for k, v in lab if k.search(f"{i}:{names[i]}")), "")
+        out.append(f"| {i} | `{names[i]}` | {step} | {len(grp)} | {us:.1f} | {fl / 1e12:.4f} | "
+                   f"{fl / us / 1e6:.0f} | {fl / us / 1e6 / 2500:.3f} | {gui / us / 1e3:.2f} | "
+                   f"{busy / (gui * simds):.3f} |")
+    return "\n".join(out) + "\n"
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2], sys.argv[3], sys.argv[4]), end="")
+    elif sys.argv[1] == "mfma":
+        print(mfma(sys.argv[2], sys.argv[3], sys.argv[4],
+                   [tuple(a.split("=", 1)) for a in sys.argv[5:]]), end="")
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:10]), indent=1))
     else:

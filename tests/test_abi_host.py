@@ -285,9 +285,9 @@ def test_arch_hook_gfx950_falls_through(monkeypatch):
 
 def test_forward_path_query():
     """caat_forward_fused: the shared channels are summed inside the row GEMM only for
-    n_s % 8 == 0 and T > 64, and only while the K-concatenated GEMM fits the bf16
-    kernel's 32-bit offsets (P T k2 2 bytes < 2^31); otherwise the per-rank GEMM and
-    K3's reduce."""
+    n_s % 8 == 0, T > 64 and at least 256 shared-GEMM tiles of 128 x 128 (or n_s = 0),
+    and only while the K-concatenated GEMM fits the bf16 kernel's 32-bit offsets
+    (P T k2 2 bytes < 2^31); otherwise the per-rank GEMM and K3's reduce."""
     L = caat.lib()
     mlp = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.BF16)
     att = caat.caat_create(4096, 0, 8, 0.5, caat.RMSNORM, caat.NONE, caat.BF16)
@@ -295,8 +295,20 @@ def test_forward_path_query():
     f32 = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.F32)
     try:
         assert caat.caat_forward_fused(mlp, 64) is False
-        assert caat.caat_forward_fused(mlp, 65) is True
+        assert caat.caat_forward_fused(mlp, 65) is False            # 16 x 1 tiles
+        assert caat.caat_forward_fused(mlp, 1920) is False          # 16 x 15 tiles
+        assert caat.caat_forward_fused(mlp, 1921) is True           # 16 x 16 tiles
         assert caat.caat_forward_fused(mlp, 8192) is True
+        zero = caat.caat_create(4096, 11008, 8, 0.0, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+        small = caat.caat_create(768, 3072, 4, 0.5, caat.LAYERNORM, caat.GELU, caat.BF16)
+        try:
+            assert caat.caat_forward_fused(zero, 65) is True         # no shared GEMM
+            assert caat.caat_forward_fused(zero, 64) is False
+            assert caat.caat_forward_fused(small, 4096) is False     # 3 x 32 tiles
+            assert caat.caat_forward_fused(small, 128 * 86) is True  # 3 x 86 tiles
+        finally:
+            caat.caat_destroy(zero)
+            caat.caat_destroy(small)
         assert caat.caat_forward_fused(odd, 8192) is False
         limit = (1 << 31) // (8 * 1376 * 2)          # largest T with P T k2 2 < 2^31, + 1
         assert caat.caat_forward_fused(mlp, limit - 1) is True

@@ -236,14 +236,50 @@ def test_sync_norm_mask_bit_exact(dtype, P, h, T):
         assert torch.equal(out_resid.double().cpu(), want), (P, h, T, n_s)
 
 
+@pytest.mark.parametrize("dtype,P,h,T", [("bf16", 8, 4096, 65), ("bf16", 8, 4096, 200),
+                                         ("bf16", 4, 768, 300), ("f32", 16, 4096, 100),
+                                         ("bf16", 8, 16384, 100)])
+def test_row_gemm_reduce_mask_bit_exact(dtype, P, h, T):
+    """The fused kernels called directly (caat_row_gemm_reduce, then caat_sync_norm) on
+    integer-coded out-projection inputs, for every n_s % 8 == 0 case whatever path the
+    forward would take: out_resid is the codes' sum on [0, n_s) and 2 code(m) after."""
+    _say(f"[case] mask row_gemm_reduce {dtype} P={P} h={h} T={T}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    hp = h // P
+    H = torch.zeros((P, T, hp), dtype=dt, device="cuda")
+    H[:, :, 0] = 1.0
+    Wo = torch.full((P, h, hp), 1.5, dtype=dt, device="cuda")
+    for m in range(P):
+        Wo[m, :, 0] = _code(dtype, P, m)
+    resid = torch.zeros((P, T, h), dtype=dt, device="cuda")
+    gamma = torch.ones(h, dtype=dt, device="cuda")
+    for n_s in sorted({0, 8, 64, h // 2 - 8, h // 2, h // 2 + 8, h - 8, h}):
+        s = caat.Sublayer(h, 0, P, n_s / h, norm="rmsnorm", act="none", dtype=dtype, s_priv=2.0)
+        assert s.n_s == n_s
+        S = torch.full((T, max(n_s, 8)), float("nan"), dtype=dt, device="cuda")
+        Z = torch.full((P, T, h), float("nan"), dtype=dt, device="cuda")
+        caat.caat_row_gemm_reduce(s.handle, T, H, Wo, S if n_s else None, Z if n_s < h else None)
+        out = torch.empty_like(resid)
+        out_resid = torch.empty_like(resid)
+        caat.caat_sync_norm(s.handle, T, S if n_s else None, Z if n_s < h else None, resid,
+                            gamma, None, out, out_resid)
+        torch.cuda.synchronize()
+        want = _coded_out_resid(dtype, P, T, h, n_s, 2.0)
+        assert torch.equal(out_resid.double().cpu(), want), (P, h, T, n_s)
+
+
 def _forward_mask_cases():
     cases = []
     h = 4096
-    # bf16, P = 8: the fused path (n_s % 8 == 0: S from the K-concatenated GEMM) and the
-    # per-rank path with K3's reduce (n_s % 8 != 0), at T > 64; the decode kernels and
-    # the per-rank K3 at T = 3.
+    # bf16, P = 8: the per-rank path with K3's reduce (n_s % 8 != 0, or too few shared-GEMM
+    # tiles) at T > 64, and the decode kernels with the per-rank K3 at T = 3.
     for T in (3, 65, 200):
         for n_s in (0, 8, 64, 2040, 2048, 2056, h - 8, h, 1, 63, 65, 179, h - 1):
+            cases.append(("bf16", 8, h, T, n_s))
+    # The fused path (S from the K-concatenated GEMM: n_s % 8 == 0 and at least 256
+    # shared-GEMM tiles), T = 2048 and a ragged T = 2000.
+    for T in (2000, 2048):
+        for n_s in (0, 1920, 2040, 2048, 2056, h - 8, h, 2047):
             cases.append(("bf16", 8, h, T, n_s))
     # The nontemporal K3 forms (more than 256 MB per launch).
     cases += [("bf16", 8, h, 1100, 2048), ("bf16", 8, h, 1100, 2047)]
@@ -281,6 +317,9 @@ def test_forward_mask_bit_exact(dtype, P, h, T, n_s):
     torch.cuda.synchronize()
     want = _coded_out_resid(dtype, P, T, h, n_s, 2.0)
     got = out_resid.double().cpu()
+    fused = caat.caat_forward_fused(s.handle, T)
+    assert fused == (n_s % 8 == 0 and T > 64 and
+                     (n_s == 0 or -(-n_s // 128) * -(-T // 128) >= 256)), fused
     if not torch.equal(got, want):
         bad = (got != want).nonzero()[:5].tolist()
         raise AssertionError(f"fused={caat.caat_forward_fused(s.handle, T)} first bad "
@@ -458,10 +497,26 @@ def test_sync_norm_matches_oracle(dtype, P, h, T, p):
     assert e1 <= tol and e2 <= tol
 
 
-def test_forward_p0_and_p1_fused():
-    for p in (0.0, 1.0):
-        w = W.with_(W.PREFILL_7B_BF16, T=70, p=p)
-        _run_and_compare(w, norm_params="random")
+@pytest.mark.parametrize("p", [0.0, 0.5, 1.0])
+def test_forward_fused_ragged(p):
+    """The fused row GEMM through the forward (at T = 2000 the shared GEMM has 16 x 16
+    tiles: the fused path) with a ragged last token tile, p = 0, 0.5 and 1, against the
+    oracle on sampled rows (the last token included)."""
+    T = 2000
+    w = W.with_(W.PREFILL_7B_BF16, T=T, p=p)
+    h = caat.Sublayer(w.h, w.ffn, w.P, p, norm=w.norm, act=w.act)
+    assert caat.caat_forward_fused(h.handle, T)
+    _run_and_compare(w, norm_params="random", rows=synth.sample_rows(T, 48))
+
+
+@pytest.mark.parametrize("p", [0.0, 1.0])
+def test_forward_per_rank_path_small_tiles(p):
+    """T = 70: too few shared-GEMM tiles for the fused path, so the per-rank GEMM and
+    K3's reduce run (p = 0 and 1 included)."""
+    w = W.with_(W.PREFILL_7B_BF16, T=70, p=p)
+    h = caat.Sublayer(w.h, w.ffn, w.P, p, norm=w.norm, act=w.act)
+    assert caat.caat_forward_fused(h.handle, 70) == (p == 0.0)
+    _run_and_compare(w, norm_params="random")
 
 
 def test_graph_replay_matches_eager():
