@@ -162,11 +162,21 @@ def cpu_baseline(w, inputs, p, budget_s):
         if dt >= 0.6 * budget_s or n >= T:
             break
         n = int(min(T, n * budget_s / max(dt, 1e-9)))
+    # A batch the oracle finishes well inside the budget (every row already sampled: the
+    # decode batches) is timed over repeated calls, so the sample is still ~budget_s.
+    reps = 1
+    if dt < 0.6 * budget_s:
+        reps = max(1, int(budget_s / max(dt, 1e-9)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            reference(w, inputs, rows=rows, p=p)
+        dt = time.perf_counter() - t0
     del torch
-    base = {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(),
+    what = f"{len(rows)} of {T} token rows" + (f", {reps} calls" if reps > 1 else "")
+    base = {"value": reps * len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"{len(rows)} of {T} token rows of {w.name} (all {w.P} ranks, every "
-                      f"sublayer), fp64, {dt:.1f} s; rows are independent, so tokens/s = rows / s"}
+            "sample": f"{what} of {w.name} (all {w.P} ranks, every sublayer), fp64, {dt:.1f} s; "
+                      f"rows are independent, so tokens/s = rows / s"}
     return base, rows, ref
 
 
