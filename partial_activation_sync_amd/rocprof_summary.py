@@ -15,6 +15,12 @@ MFMA utilisation (busy cycles summed over the SIMDs / (GUI_ACTIVE per XCD x SIMD
 MfmaUtil expression rocprofv3 lists), medians over the dispatches with the same launch
 position in the step.
 
+    python -m partial_activation_sync_amd.rocprof_summary steps <dir> [<label> ...]
+
+``steps`` reads the ``*_kernel_trace.csv`` of a ``--kernel-trace`` run and prints the mean,
+median and minimum duration of each launch position of the repeating step (the library's
+kernels only; the labels name the positions in order), and the mean gap between launches.
+
 ``stats`` prints a markdown table of per-kernel call counts and durations from the
 ``*_kernel_stats.csv`` of a ``--kernel-trace --stats`` run.  ``traffic`` reads the
 ``*_counter_collection.csv`` of four ``--pmc`` runs (FETCH_SIZE and WRITE_SIZE, in KiB
@@ -146,6 +152,50 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, select, ke
     return rec
 
 
+def _period(names):
+    """Length and count of the step that repeats from the first launch on: the shortest p
+    whose pattern holds for at least three steps (or the whole run), and how many whole
+    steps follow it from the start (a run may end with other kernels, e.g. timing of a
+    different pass)."""
+    for p in range(1, len(names) + 1):
+        span = min(len(names), 3 * p)
+        if all(names[i] == names[i % p] for i in range(span)):
+            n = 0
+            while (n + 1) * p <= len(names) and names[n * p:(n + 1) * p] == names[:p]:
+                n += 1
+            return p, n
+    return len(names), 1
+
+
+def _short(name):
+    return re.sub(r"\(.*", "", name.replace("caat::(anonymous namespace)::", ""))
+
+
+def steps(d, labels=()):
+    rows = [r for r in csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv"))))
+            if "caat" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [_short(r["Kernel_Name"]) for r in rows]
+    per, n = _period(names)
+    out = ["| # | step | kernel | launches | mean (us) | median (us) | min (us) |",
+           "|---|---|---|---|---|---|---|"]
+    total = 0.0
+    for i in range(per):
+        ds = [(int(rows[k * per + i]["End_Timestamp"]) - int(rows[k * per + i]["Start_Timestamp"])) / 1e3
+              for k in range(n)]
+        total += statistics.mean(ds)
+        lab = labels[i] if i < len(labels) else ""
+        out.append(f"| {i} | {lab} | `{names[i]}` | {n} | {statistics.mean(ds):.1f} | "
+                   f"{statistics.median(ds):.1f} | {min(ds):.1f} |")
+    gaps = [(int(rows[k + 1]["Start_Timestamp"]) - int(rows[k]["End_Timestamp"])) / 1e3
+            for k in range(n * per - 1) if (k + 1) % per]
+    out.append(f"| | sum | | | {total:.1f} | | |")
+    out.append("")
+    out.append(f"Mean gap between consecutive launches of a step: {statistics.mean(gaps):.2f} us "
+               f"(median {statistics.median(gaps):.2f}).")
+    return "\n".join(out) + "\n"
+
+
 def mfma(d, title, command, labels=(), simds=1024, xcds=8):
     """Per MFMA dispatch (in launch order within a repeating step): duration, FLOPs from
     SQ_INSTS_VALU_MFMA_MOPS_BF16, clock and MFMA utilisation; medians by position."""
@@ -158,9 +208,9 @@ def mfma(d, title, command, labels=(), simds=1024, xcds=8):
     # The library's kernels only (torch's fills and copies set up the inputs).
     disp = [by[k] for k in sorted(by) if "caat" in by[k]["name"]]
     # The step repeats: find its period from the kernel-name sequence.
-    names = [re.sub(r"\(.*", "", e["name"].replace("caat::(anonymous namespace)::", "")) for e in disp]
-    period = next(p for p in range(1, len(names) + 1)
-                  if all(names[i] == names[i % p] for i in range(len(names))))
+    names = [_short(e["name"]) for e in disp]
+    period, nsteps = _period(names)
+    disp = disp[:period * nsteps]
     lab = [(re.compile(k), v) for k, v in labels]
     out = [f"# {title}", "", f"Command: `{command}`", "",
            "| # | kernel | step | dispatches | duration (us) | MFMA TFLOP | TFLOP/s | of 2.5 PF "
@@ -184,6 +234,8 @@ def mfma(d, title, command, labels=(), simds=1024, xcds=8):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2], sys.argv[3], sys.argv[4]), end="")
+    elif sys.argv[1] == "steps":
+        print(steps(sys.argv[2], sys.argv[3:]), end="")
     elif sys.argv[1] == "mfma":
         print(mfma(sys.argv[2], sys.argv[3], sys.argv[4],
                    [tuple(a.split("=", 1)) for a in sys.argv[5:]]), end="")
