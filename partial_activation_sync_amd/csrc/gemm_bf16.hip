@@ -72,7 +72,9 @@ __device__ __forceinline__ float silu(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
-template <int BN, int BT, int WGN, int WGT, int EPI>
+// NST: LDS stages, 2 or 4.  With 4, three K steps are in flight while one is computed
+// (for the small tiles, whose short steps cannot cover a load's latency with one).
+template <int BN, int BT, int WGN, int WGT, int EPI, int NST>
 __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int tilesN, int tilesT)
 {
     constexpr int NW = WGN * WGT, NTH = 64 * NW;
@@ -86,9 +88,12 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     static_assert(SLOTS % NTH == 0 && (BN * 8) % NTH == 0, "tile must split evenly");
     static_assert(EPI != EPI_SWIGLU || IB % 2 == 0, "SwiGLU pairs need an even block count");
     static_assert(NMFMA >= NREAD, "interleave needs at least one MFMA per fragment read");
+    static_assert(NST == 2 || NST == 4, "two or four stages");
 
     __shared__ __attribute__((aligned(16))) uint4 L0[SLOTS];
     __shared__ __attribute__((aligned(16))) uint4 L1[SLOTS];
+    __shared__ __attribute__((aligned(16))) uint4 L2[NST > 2 ? SLOTS : 1];
+    __shared__ __attribute__((aligned(16))) uint4 L3[NST > 2 ? SLOTS : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -245,6 +250,28 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         CAAT_SCHED_FENCE();                                                                \
         CAAT_READ(0, Ln, 0);                                                               \
     } while (0)
+    // Four stages: step ks on Lb while steps ks + 1 and ks + 2 are in flight; Li (the stage
+    // of step ks - 1, released by that step's barrier) receives step ks + 3.  The wait lets
+    // only the two newest steps' loads (2 LOADS per lane) stay in flight, so step ks + 1
+    // (in Ln) has landed at the barrier.
+    constexpr int VM_NEXT = 2 * LOADS;
+    static_assert(NST == 2 || VM_NEXT < 64, "vmcnt range");
+    // s_waitcnt encoding on gfx9: vmcnt[3:0] and vmcnt[5:4] at bits 15:14, expcnt (7: no
+    // wait) at bits 6:4, lgkmcnt (0) at bits 11:8.
+    constexpr int WAIT_NEXT = (VM_NEXT & 15) | ((VM_NEXT >> 4) << 14) | (7 << 4);
+#define CAAT_STEP_MORE4(ks, Lb, Li, Ln)                                                    \
+    do {                                                                                   \
+        CAAT_ISSUE(min((ks) + 3, nsteps - 1), Li);                                         \
+        CAAT_READ(1, Lb, 1); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_READ(0, Lb, 2); CAAT_MMA(1, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_READ(1, Lb, 3); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_MMA(1, 0, IB);                                                                \
+        CAAT_SCHED_FENCE();                                                                \
+        __builtin_amdgcn_s_waitcnt(WAIT_NEXT);                                             \
+        __builtin_amdgcn_s_barrier();                                                      \
+        CAAT_SCHED_FENCE();                                                                \
+        CAAT_READ(0, Ln, 0);                                                               \
+    } while (0)
     // The last K step: no next step to load or read.
 #define CAAT_STEP_LAST(Lb)                                                                 \
     do {                                                                                   \
@@ -280,6 +307,10 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     uint32_t off[LOADS];
     CAAT_TILE_SETUP(tile, m, n0, t0, rW, rX, off);
     CAAT_ISSUE(0, L0);
+    if constexpr (NST == 4) {
+        CAAT_ISSUE(min(1, nsteps - 1), L1);
+        CAAT_ISSUE(min(2, nsteps - 1), L2);
+    }
     for (;;) {
         // The tile's first step has landed in L0; every wave has finished reading L1.
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -294,11 +325,33 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         // epilogue from the loop and one from the last step, as few as the accumulators
         // can take without spilling.
         int kt = 0;
-        for (; kt + 2 <= nsteps; kt += 2) {
-            CAAT_STEP_MORE(kt, L0, L1);
-            CAAT_STEP_MORE(kt + 1, L1, L0);
+        if constexpr (NST == 4) {
+            // Whole groups of four steps; the 1-3 remaining ones follow (step k is always
+            // in stage k % 4, and a clamped load index refills a stage nothing reads).
+            for (; kt + 4 <= nsteps; kt += 4) {
+                CAAT_STEP_MORE4(kt, L0, L3, L1);
+                CAAT_STEP_MORE4(kt + 1, L1, L0, L2);
+                CAAT_STEP_MORE4(kt + 2, L2, L1, L3);
+                CAAT_STEP_MORE4(kt + 3, L3, L2, L0);
+            }
+            const int rest = nsteps - kt;
+            if (rest == 1) {
+                CAAT_STEP_LAST(L0);
+            } else if (rest == 2) {
+                CAAT_STEP_MORE4(kt, L0, L3, L1);
+                CAAT_STEP_LAST(L1);
+            } else if (rest == 3) {
+                CAAT_STEP_MORE4(kt, L0, L3, L1);
+                CAAT_STEP_MORE4(kt + 1, L1, L0, L2);
+                CAAT_STEP_LAST(L2);
+            }
+        } else {
+            for (; kt + 2 <= nsteps; kt += 2) {
+                CAAT_STEP_MORE(kt, L0, L1);
+                CAAT_STEP_MORE(kt + 1, L1, L0);
+            }
+            if (kt < nsteps) CAAT_STEP_LAST(L0);
         }
-        if (kt < nsteps) CAAT_STEP_LAST(L0);
 
         // The last step may have refilled a stage nothing reads; let it land and let
         // every wave finish its fragment reads.  Then the next tile's first step goes
@@ -356,13 +409,19 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         if (more) {
             CAAT_TILE_SETUP(next, m2, n02, t02, rW2, rX2, off2);
             CAAT_ISSUE_T(0, L0, rW2, rX2, off2);
+            if constexpr (NST == 4) {
+                CAAT_ISSUE_T(min(1, nsteps - 1), L1, rW2, rX2, off2);
+                CAAT_ISSUE_T(min(2, nsteps - 1), L2, rW2, rX2, off2);
+            }
         }
+        // The output image: the stage the next tile's first steps leave free.
+        uint4 *const IMG = (NST == 4) ? L3 : L1;
         __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
         CAAT_UNROLL for (int ps = 0; ps < NPASS; ++ps) {
             CAAT_UNROLL for (int j = 0; j < JB; ++j) {
                 const int tb = wt * WT + j * 32;                     // the 32 tokens' first row
                 if (tb / PROWS != ps) continue;
-                uint2 *img = reinterpret_cast<uint2 *>(L1);
+                uint2 *img = reinterpret_cast<uint2 *>(IMG);
                 const int r = tb % PROWS + r32e;                      // image row of the token
                 const int sw = r & SWM, hs = (r >> 4) & 1;
                 if (EPI == EPI_SWIGLU) {
@@ -395,7 +454,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
             CAAT_UNROLL for (int it = 0; it < PROWS * CPR / NTH; ++it) {
                 const int q = it * NTH + te;
                 const int r = q / CPR, c = q % CPR;
-                uint4 v = L1[r * CPR + (c ^ (r & SWM))];
+                uint4 v = IMG[r * CPR + (c ^ (r & SWM))];
                 if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
                 const int t = t0 + ps * PROWS + r, n = n0 + c * 8;
                 if (t < T && n < N)
@@ -415,6 +474,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
 #undef CAAT_INTERLEAVE
 #undef CAAT_STEP_MORE
 #undef CAAT_STEP_LAST
+#undef CAAT_STEP_MORE4
 #undef CAAT_ISSUE
 #undef CAAT_ISSUE_T
 #undef CAAT_TILE_SETUP
@@ -434,13 +494,13 @@ int cu_count() {
 
 // One launch of a kernel instance: at most as many workgroups as fit on the device at
 // once (each then runs a sequence of tiles), and never more than the tiles.
-template <int BN, int BT, int WGN, int WGT, int EPI>
+template <int BN, int BT, int WGN, int WGT, int EPI, int NST>
 hipError_t launch_epi(const GemmArgs &a, int tilesN, int tilesT, hipStream_t s) {
     constexpr int NTH = 64 * WGN * WGT;
     static const int resident = [] {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void *>(&k_gemm_bf16<BN, BT, WGN, WGT, EPI>), NTH,
+                &n, reinterpret_cast<const void *>(&k_gemm_bf16<BN, BT, WGN, WGT, EPI, NST>), NTH,
                 0) != hipSuccess || n < 1)
             n = 1;
         return n;
@@ -448,20 +508,20 @@ hipError_t launch_epi(const GemmArgs &a, int tilesN, int tilesT, hipStream_t s) 
     const long total = (long)a.P * tilesN * tilesT;
     const long slots = (long)resident * cu_count();
     const dim3 grid((unsigned)(total < slots ? total : slots)), block(NTH);
-    hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI>), grid, block, 0, s, a, tilesN, tilesT);
+    hipLaunchKernelGGL((k_gemm_bf16<BN, BT, WGN, WGT, EPI, NST>), grid, block, 0, s, a, tilesN, tilesT);
     return hipGetLastError();
 }
 
-template <int BN, int BT, int WGN, int WGT>
+template <int BN, int BT, int WGN, int WGT, int NST>
 hipError_t launch(const GemmArgs &a, hipStream_t s) {
     const int ncol = (a.epi == EPI_SWIGLU) ? BN / 2 : BN;
     const int tilesN = (a.N + ncol - 1) / ncol;
     const int tilesT = (a.T + BT - 1) / BT;
     switch (a.epi) {
-    case EPI_GELU: return launch_epi<BN, BT, WGN, WGT, EPI_GELU>(a, tilesN, tilesT, s);
-    case EPI_GELU_TANH: return launch_epi<BN, BT, WGN, WGT, EPI_GELU_TANH>(a, tilesN, tilesT, s);
-    case EPI_SWIGLU: return launch_epi<BN, BT, WGN, WGT, EPI_SWIGLU>(a, tilesN, tilesT, s);
-    default: return launch_epi<BN, BT, WGN, WGT, EPI_STORE>(a, tilesN, tilesT, s);
+    case EPI_GELU: return launch_epi<BN, BT, WGN, WGT, EPI_GELU, NST>(a, tilesN, tilesT, s);
+    case EPI_GELU_TANH: return launch_epi<BN, BT, WGN, WGT, EPI_GELU_TANH, NST>(a, tilesN, tilesT, s);
+    case EPI_SWIGLU: return launch_epi<BN, BT, WGN, WGT, EPI_SWIGLU, NST>(a, tilesN, tilesT, s);
+    default: return launch_epi<BN, BT, WGN, WGT, EPI_STORE, NST>(a, tilesN, tilesT, s);
     }
 }
 
@@ -499,9 +559,18 @@ hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s) {
         const long cus = cu_count();
         const double big = (double)((tiles256 + cus - 1) / cus);
         const double small = (double)((tiles128 + 2 * cus - 1) / (2 * cus)) * 0.5 / 0.77;
-        if (small >= big) return launch<256, 256, 4, 2>(a, s);
+        if (small >= big) return launch<256, 256, 4, 2, 2>(a, s);
     }
-    return launch<128, 128, 2, 2>(a, s);
+    // Small tiles.  Two workgroups per CU (two stages each) cover each other's load
+    // latency; when there are no more tiles than CUs, each CU holds one workgroup anyway,
+    // and four stages (three K steps in flight, 128 KB of LDS) cover it instead: the 1.1B
+    // shared-channel GEMM at p = 0.25 (256 tiles, K = 8 x 704) 65.6 -> 52.0 us, the 130M one
+    // (96 tiles) 35.2 -> 28.1 us; with more tiles than CUs the four-stage form was slower
+    // everywhere (130M K1, 768 tiles: 34.8 against 43.4 us).
+    const long ncol = (a.epi == EPI_SWIGLU) ? 64 : 128;
+    const long tiles128 = (long)a.P * ((a.N + ncol - 1) / ncol) * ((a.T + 127) / 128);
+    if (tiles128 <= cu_count()) return launch<128, 128, 2, 2, 4>(a, s);
+    return launch<128, 128, 2, 2, 2>(a, s);
 }
 
 }  // namespace caat
