@@ -230,7 +230,17 @@ hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
-bool gemm_decode_applies(const GemmArgs &a) { return a.T <= 64; }
+// The weight-streaming kernel wins while few tokens feed each weight row; past that the
+// tiled MFMA kernel (64-token tiles, four stages) takes over: plain and GeLU epilogues
+// with a long contraction past 16 tokens (7B K2, K = 1376: 22.5 / 25.6 us at T = 33 / 64
+// against 20.6 / 21.6 us), SwiGLU past 48 (7B K1, K = 4096: 53.7 against 46.5 us at
+// T = 64; at T = 48 the two tie).  Short contractions (the out-projection, K = 512) stay
+// here at every T <= 64.
+bool gemm_decode_applies(const GemmArgs &a) {
+    if (a.T > 64) return false;
+    if (a.epi == EPI_SWIGLU) return a.T <= 48;
+    return a.K < 1024 || a.T <= 16;
+}
 
 // Launch shapes, measured on the 7B decode GEMMs (three weight copies rotated so the
 // weights stream from HBM; K1: SwiGLU, N = 1376 per rank, K = 4096; K2: N = 4096,

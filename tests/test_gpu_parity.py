@@ -72,10 +72,19 @@ def test_7b_decode_full(T):
 
 
 # Decode batch sizes between the benchmarked ones: each weight-streaming launch shape
-# (one or two weight blocks per wave, 1 to 4 token blocks, ragged last block).
-@pytest.mark.parametrize("T", [9, 16, 17, 40])
+# (one or two weight blocks per wave, 1 to 4 token blocks, ragged last block), and the
+# 64-token MFMA tiles that take over the long contractions past 16 tokens (K2) and the
+# SwiGLU GEMM past 48 (T = 17, 33, 40: K2 there; T = 49, 56: K1 too; ragged tiles).
+@pytest.mark.parametrize("T", [9, 16, 17, 33, 40, 49, 56])
 def test_7b_decode_launch_shapes(T):
     _run_and_compare(W.DECODE_7B_BF16, T=T, norm_params="random")
+
+
+def test_decode_mfma_tiles_more_than_cus():
+    """Wider layers than 7B at T = 56: 272 SwiGLU tiles of 64 tokens in K1 and 320 in K2,
+    more than the 256 CUs, so both take the two-stage form of the 64-token tiles."""
+    w = W.with_(W.DECODE_7B_BF16, h=5120, ffn=8 * 2176, heads=40)
+    _run_and_compare(w, T=56, norm_params="random")
 
 
 # ---------------------------------------------------------------------------
