@@ -112,15 +112,17 @@ def traffic_key(workload, T, kernel_name):
 
 
 def kernel_source(name, T, dtype):
-    """The source file of the kernel a step launches (fp32 GEMMs: the FMA kernel; bf16
-    GEMMs at T <= 64 tokens: the weight-streaming decode kernels)."""
+    """The source files of the kernel a step launches (fp32 GEMMs: the FMA kernel; bf16
+    GEMMs at T <= 64 tokens: the weight-streaming decode kernels, whose source also
+    holds the rule that hands some of them to the MFMA tile kernel, and that kernel)."""
+    csrc = os.path.join(ROOT, "partial_activation_sync_amd", "csrc")
     if name.endswith("K3"):
-        f = "psync_norm.hip"
-    elif dtype != "bf16":
-        f = "gemm_f32.hip"
-    else:
-        f = "gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"
-    return os.path.join(ROOT, "partial_activation_sync_amd", "csrc", f)
+        return [os.path.join(csrc, "psync_norm.hip")]
+    if dtype != "bf16":
+        return [os.path.join(csrc, "gemm_f32.hip")]
+    if T <= 64:
+        return [os.path.join(csrc, "gemm_decode.hip"), os.path.join(csrc, "gemm_bf16.hip")]
+    return [os.path.join(csrc, "gemm_bf16.hip")]
 
 
 def traffic_for(kernel_file, key):

@@ -58,10 +58,12 @@ def _code(path):
 
 
 def code_sha256(path):
-    """SHA-256 of a C/C++/HIP source and the local headers it includes (``#include "..."``,
-    followed recursively), with comments dropped and each run of whitespace made one
-    space: it changes when the code does, not when only a comment does."""
-    seen, order, todo = set(), [], [os.path.abspath(path)]
+    """SHA-256 of a C/C++/HIP source (or a list of them) and the local headers it includes
+    (``#include "..."``, followed recursively), with comments dropped and each run of
+    whitespace made one space: it changes when the code does, not when only a comment
+    does."""
+    paths = list(path) if isinstance(path, (list, tuple)) else [path]
+    seen, order, todo = set(), [], [os.path.abspath(p) for p in paths]
     while todo:
         f = todo.pop(0)
         if f in seen:
@@ -140,7 +142,7 @@ def traffic(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_bytes, select, ke
         "bytes_per_launch": kf * sf + kw * sw,
         "fetch_scale": sf, "write_scale": sw,
         "dispatches": [nf, nw], "kernel_regex": select,
-        "code_sha256": code_sha256(os.path.join(ROOT, src)),
+        "code_sha256": code_sha256([os.path.join(ROOT, f) for f in src.split("+")]),
         "source": src,
     }
     path = os.path.join(ROOT, "profiles", "traffic.json")

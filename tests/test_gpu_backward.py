@@ -195,14 +195,18 @@ def test_backward_pair_chain_matches_oracle():
         assert e <= TOL["bf16"], (k, e)
 
 
-@pytest.mark.parametrize("act,dtype,T", [("swiglu", "bf16", 192), ("gelu", "bf16", 130),
-                                         ("swiglu", "bf16", 24), ("gelu_tanh", "f32", 40)])
-def test_stored_preactivation(act, dtype, T):
+@pytest.mark.parametrize("act,dtype,T,h,ffn", [("swiglu", "bf16", 192, 256, 768),
+                                               ("gelu", "bf16", 130, 256, 768),
+                                               ("swiglu", "bf16", 24, 256, 768),
+                                               ("gelu_tanh", "f32", 40, 256, 768),
+                                               ("swiglu", "bf16", 57, 1024, 4 * 1400)])
+def test_stored_preactivation(act, dtype, T, h, ffn):
     """caat_forward_train: the same out / out_resid as caat_forward_ex bit for bit, the
     pre-activation x W1^T against the oracle's linear layer, and a backward fed with it
     bit-identical to the backward that recomputes it (T = 24: the weight-streaming
-    kernels, which fill the pre-activation with a separate GEMM)."""
-    P, h, ffn = 4, 256, 768
+    kernels, which fill the pre-activation with a separate GEMM; T = 57 at h = 1024: the
+    64-token MFMA tiles, whose epilogue stores it)."""
+    P = 4
     _say(f"[case] stored pre-activation act={act} {dtype} T={T}")
     d = _inputs(P, T, h, ffn, act, dtype, resid_given=True, dres_given=True)
     dev = {k: (v.cuda() if v is not None else None) for k, v in d.items()}

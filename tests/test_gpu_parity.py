@@ -358,8 +358,11 @@ def test_p_below_1_ranks_differ_only_in_private_channels():
         assert not torch.equal(r[m, :, n_s:], r[0, :, n_s:])
 
 
-def test_run_to_run_deterministic():
-    w = W.with_(W.PREFILL_7B_BF16, T=520)
+@pytest.mark.parametrize("wname,T", [("7b-prefill-pair-bf16", 520), ("7b-decode-pair-bf16", 64)])
+def test_run_to_run_deterministic(wname, T):
+    """Repeated forwards are bitwise identical (T = 64: the 64-token MFMA tiles of the
+    decode batch)."""
+    w = W.with_(W.ALL[wname], T=T)
     run = runner.Run(w, runner.make_inputs(w, norm_params="random"))
     run.step()
     first = {k: v.clone() for k, v in run.outputs().items()}
@@ -528,10 +531,11 @@ def test_forward_per_rank_path_small_tiles(p):
     _run_and_compare(w, norm_params="random")
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("T", [8, 64])
+def test_graph_replay_matches_eager(T):
     """One decode step captured as a HIP graph: every replay (with eager work between
-    replays) reproduces the eager outputs bitwise."""
-    w = W.with_(W.DECODE_7B_BF16, T=8)
+    replays) reproduces the eager outputs bitwise (T = 64: with the 64-token MFMA tiles)."""
+    w = W.with_(W.DECODE_7B_BF16, T=T)
     run = runner.Run(w, runner.make_inputs(w, norm_params="random"))
     run.step()
     torch.cuda.synchronize()
