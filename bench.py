@@ -313,10 +313,13 @@ def bench_backward(args, w, T, p):
                 "unit": "GB/s", "frac": round(achieved / PEAK["hbm"], 4)}
     roof["kernel"] = dom
     roof["algorithmic_per_launch"] = flops if flops else nbytes
-    src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
-                       "backward.hip" if not flops else
-                       ("gemm_tn.hip" if tn and name in ("dW1", "dW2") else
-                        "gemm_decode.hip" if T <= 64 else "gemm_bf16.hip"))
+    csrc = os.path.join(ROOT, "partial_activation_sync_amd", "csrc")
+    if not flops:
+        src = [os.path.join(csrc, "backward.hip")]
+    elif tn and name in ("dW1", "dW2"):
+        src = [os.path.join(csrc, "gemm_tn.hip")]
+    else:
+        src = kernel_source("K2", T, w.dtype)
     roof["traffic"] = traffic_for(src, traffic_key(w.name + ":bwd", T, dom))
     # What the stored pre-activation costs the forward: a training forward (K1's epilogue
     # also writes x W1^T) against the plain one, same inputs, same stream.
@@ -439,9 +442,8 @@ def bench_block(args, w, T, p):
     dom = max(("qkv", "attn"), key=lambda k: ms[k])
     flops, nbytes = kernel_work_block(w, T, dom)
     achieved = flops / ms[dom] / 1e9
-    src = os.path.join(ROOT, "partial_activation_sync_amd", "csrc",
-                       "attention.hip" if dom == "attn" else
-                       "gemm_decode.hip" if T <= 64 else "gemm_bf16.hip")
+    src = ([os.path.join(ROOT, "partial_activation_sync_amd", "csrc", "attention.hip")]
+           if dom == "attn" else kernel_source("K2", T, w.dtype))
     roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK["mfma"],
             "unit": "TFLOP/s", "frac": round(achieved / PEAK["mfma"], 4), "kernel": dom,
             "algorithmic_per_launch": flops,

@@ -68,7 +68,8 @@ bool gemm_tn_supported(const TnArgs &a);
 hipError_t gemm_tn_bf16(const TnArgs &a, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs &a, hipStream_t s);
 bool gemm_bf16_supported(const GemmArgs &a);
-// Weight-streaming variant for decode batches (T <= 64), bf16.
+// Weight-streaming variant for decode batches, bf16: the GEMMs of up to 64 tokens for
+// which gemm_decode_applies (the others take the MFMA kernel's 64-token tiles).
 bool gemm_decode_applies(const GemmArgs &a);
 hipError_t gemm_decode_bf16(const GemmArgs &a, hipStream_t s);
 
