@@ -89,6 +89,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     static_assert(EPI != EPI_SWIGLU || IB % 2 == 0, "SwiGLU pairs need an even block count");
     static_assert(NMFMA >= NREAD, "interleave needs at least one MFMA per fragment read");
     static_assert(NST == 2 || NST == 4, "two or four stages");
+    static_assert(NST == 2 || LOADS % 4 == 0, "four-stage loads go out in quarters");
 
     __shared__ __attribute__((aligned(16))) uint4 L0[SLOTS];
     __shared__ __attribute__((aligned(16))) uint4 L1[SLOTS];
@@ -197,6 +198,24 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
 #define CAAT_ISSUE(ks, Lb) CAAT_ISSUE_T(ks, Lb, rW, rX, off)
+    // A quarter of step ks's loads (load indices [q LOADS / 4, (q + 1) LOADS / 4)), for
+    // spreading a step's loads over the sub-steps of the step before.
+#define CAAT_ISSUE_Q(ks, Lb, q)                                                            \
+    do {                                                                                   \
+        constexpr int Q0_ = (q) * (LOADS / 4), Q1_ = ((q) + 1) * (LOADS / 4);              \
+        const int g_ = (ks) / nk;                                                          \
+        const int k0_ = ((ks) - g_ * nk) * BK;                                             \
+        const uint32_t sw_ = (uint32_t)((g_ * a.w_kseg + k0_) * 2u);                       \
+        const uint32_t sx_ = (uint32_t)((g_ * a.x_kseg + k0_) * 2u);                       \
+        const bool tail_ = ktail && k0_ + BK > K;                                          \
+        CAAT_UNROLL for (int i = Q0_; i < Q1_; ++i) {                                      \
+            const int c = cl ^ ((i * NW + wave) & 1);                                      \
+            const uint32_t o = (!tail_ || k0_ + c * 8 < K) ? off[i] : OOB;                 \
+            load_lds16(i < WLOADS ? rW : rX, (Lb) + (i * NW + wave) * 64, o,               \
+                       i < WLOADS ? sw_ : sx_);                                            \
+        }                                                                                  \
+        CAAT_SCHED_FENCE();                                                                \
+    } while (0)
 
     f32x16 acc[IB][JB];
     // Fragment registers: two sets, sub-steps alternate between them, carried across K
@@ -253,7 +272,12 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     // Four stages: step ks on Lb while steps ks + 1 and ks + 2 are in flight; Li (the stage
     // of step ks - 1, released by that step's barrier) receives step ks + 3.  The wait lets
     // only the two newest steps' loads (2 LOADS per lane) stay in flight, so step ks + 1
-    // (in Ln) has landed at the barrier.
+    // (in Ln) has landed at the barrier.  The four-stage tiles run one wave per SIMD, with
+    // no second wave to compute while a wave waits to issue its loads, so step ks + 3's
+    // loads go out a quarter at a time between the sub-steps' MFMAs (the 7B decode K1 at
+    // T = 64: 46.7 -> 42.0 us, a four-stage shared-channel GEMM 29.4 -> 24.6 us; with two
+    // waves per SIMD the same spread was 3-6 % slower, so the two-stage step keeps its
+    // loads together).
     constexpr int VM_NEXT = 2 * LOADS;
     static_assert(NST == 2 || VM_NEXT < 64, "vmcnt range");
     // s_waitcnt encoding on gfx9: vmcnt[3:0] and vmcnt[5:4] at bits 15:14, expcnt (7: no
@@ -261,10 +285,13 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     constexpr int WAIT_NEXT = (VM_NEXT & 15) | ((VM_NEXT >> 4) << 14) | (7 << 4);
 #define CAAT_STEP_MORE4(ks, Lb, Li, Ln)                                                    \
     do {                                                                                   \
-        CAAT_ISSUE(min((ks) + 3, nsteps - 1), Li);                                         \
+        CAAT_ISSUE_Q(min((ks) + 3, nsteps - 1), Li, 0);                                    \
         CAAT_READ(1, Lb, 1); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_ISSUE_Q(min((ks) + 3, nsteps - 1), Li, 1);                                    \
         CAAT_READ(0, Lb, 2); CAAT_MMA(1, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_ISSUE_Q(min((ks) + 3, nsteps - 1), Li, 2);                                    \
         CAAT_READ(1, Lb, 3); CAAT_MMA(0, 0, IB); CAAT_INTERLEAVE(NMFMA);                   \
+        CAAT_ISSUE_Q(min((ks) + 3, nsteps - 1), Li, 3);                                    \
         CAAT_MMA(1, 0, IB);                                                                \
         CAAT_SCHED_FENCE();                                                                \
         __builtin_amdgcn_s_waitcnt(WAIT_NEXT);                                             \
@@ -476,6 +503,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
 #undef CAAT_STEP_LAST
 #undef CAAT_STEP_MORE4
 #undef CAAT_ISSUE
+#undef CAAT_ISSUE_Q
 #undef CAAT_ISSUE_T
 #undef CAAT_TILE_SETUP
 }

@@ -231,15 +231,20 @@ hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 // The weight-streaming kernel wins while few tokens feed each weight row; past that the
-// tiled MFMA kernel (64-token tiles, four stages) takes over: plain and GeLU epilogues
-// with a long contraction past 16 tokens (7B K2, K = 1376: 22.5 / 25.6 us at T = 33 / 64
-// against 20.6 / 21.6 us), SwiGLU past 48 (7B K1, K = 4096: 53.7 against 46.5 us at
-// T = 64; at T = 48 the two tie).  Short contractions (the out-projection, K = 512) stay
-// here at every T <= 64.
+// tiled MFMA kernel (64-token tiles, four stages) takes over.  Measured on the 7B decode
+// shapes, three weight copies rotated, µs:
+//   * kernels alone (weight-streaming against 64-token tiles): K2 (K = 1376) 18.9 / 18.4
+//     at T = 12, 19.5 / 18.5 at T = 16; the out-projection (K = 512) 9.2 / 9.5 at T = 48,
+//     10.3 / 9.7 at T = 64; K1 (SwiGLU, K = 4096) 41.0 / 40.0 at T = 24, 52.2 / 42.0 at
+//     T = 64;
+//   * the replayed MLP step, both rules on one box: K2 on the tiles past 8 tokens took
+//     T = 12 / 16 from 58.7 / 62.1 to 57.6 / 60.2; K1 on the tiles at T = 24 / 32 was
+//     slower there (73.8 / 74.9 against 69.0 / 71.4) although faster alone, so SwiGLU
+//     stays weight-streaming up to 48 tokens; at T = 64 80.0 against 85.0.
 bool gemm_decode_applies(const GemmArgs &a) {
-    if (a.T > 64) return false;
-    if (a.epi == EPI_SWIGLU) return a.T <= 48;
-    return a.K < 1024 || a.T <= 16;
+    if (a.T > 48) return false;
+    if (a.K < 1024 || a.epi == EPI_SWIGLU) return true;
+    return a.T <= 8;
 }
 
 // Launch shapes, measured on the 7B decode GEMMs (three weight copies rotated so the
