@@ -30,6 +30,14 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint4 *lds,
         r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
+// load_lds16 with a cache policy (2: nontemporal, for data read once).
+template <int CPOL>
+__device__ __forceinline__ void load_lds16_pol(__amdgpu_buffer_rsrc_t r, uint4 *lds, uint32_t voff,
+                                               uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, CPOL);
+}
+
 // 16 bytes per lane into registers.
 __device__ __forceinline__ bf16x8 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));

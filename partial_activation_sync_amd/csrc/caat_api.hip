@@ -358,11 +358,14 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
     if (c->act != CAAT_NONE) {
         caat::GemmArgs g = col_args(c, T, a->in, a->W1, Y);
         if (preact != nullptr) {
-            if (c->dtype == CAAT_BF16 && !caat::gemm_decode_applies(g)) {
-                // The MFMA kernel's epilogue stores the pre-activation beside Y.
+            if (c->dtype == CAAT_BF16 && !caat::gemm_decode_applies(g) &&
+                !caat::gemm_bf16_rotates_k(g)) {
+                // The MFMA kernel's epilogue stores the pre-activation beside Y (in the
+                // K order of the backward's recompute GEMM).
                 g.pre = preact; g.pre_stride = (size_t)T * c->F1; g.ld_pre = c->F1;
             } else {
-                // Other kernels: the same contraction as the backward's recompute.
+                // Other kernels, and K orders rotated per tile: the backward's own
+                // recompute GEMM, so that the two agree bit for bit.
                 CAAT_TRY(run_gemm(c, preact_args(c, T, a->W1, a->in, preact), s));
             }
         }

@@ -68,6 +68,11 @@ bool gemm_tn_supported(const TnArgs &a);
 hipError_t gemm_tn_bf16(const TnArgs &a, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs &a, hipStream_t s);
 bool gemm_bf16_supported(const GemmArgs &a);
+// Whether the bf16 MFMA kernel walks each tile's K steps in a per-tile rotated order for
+// this GEMM (its 64-token tiles do): its sums then round differently from the same
+// contraction tiled another way, e.g. a pre-activation stored by the activation
+// epilogue against the backward's recompute as a plain GEMM.
+bool gemm_bf16_rotates_k(const GemmArgs &a);
 // Weight-streaming variant for decode batches, bf16: the GEMMs of up to 64 tokens for
 // which gemm_decode_applies (the others take the MFMA kernel's 64-token tiles).
 bool gemm_decode_applies(const GemmArgs &a);

@@ -170,17 +170,29 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         boff[kk] = BN * 8 + (wt * WT + r32) * 8 + ((kk * 2 + kh) ^ fr);
     }
 
+    // The 64-token tiles serve batches of at most 64 tokens, whose GEMMs read each weight
+    // once from HBM.  Each tile walks its K steps from its own starting step (tile mod
+    // nsteps, wrapping round): when every workgroup reads the same K offset at once, of
+    // rows a whole row apart, HBM delivered 4.4 TB/s in a probe of the bare weight stream
+    // against 6.0 TB/s with staggered offsets.  The activation GEMM's weight loads also
+    // carry the nontemporal hint.  7B decode K1 at T = 64: 42.1 -> 37.7 us with both; for
+    // K2 (K = 1376) the hint cost 3 us and the rotation nothing, so K2 rotates only.
+    constexpr bool ROTATE = BT == 64;
+    constexpr int WPOL = (BT == 64 && EPI != EPI_STORE) ? 2 : 0;
     const int nk = (K + BK - 1) / BK;          // K steps per segment
     const int nsteps = kseg * nk;              // K steps over all segments
     const bool ktail = (K % BK) != 0;
 
-    // Enqueue the loads of combined K step ks (segment ks / nk) of the tile with
-    // descriptors RW, RX and offsets OFF into LDS stage Lb.  Only a ragged last step of a
-    // segment masks chunks past K (they read as zero).
-#define CAAT_ISSUE_T(ks, Lb, RW, RX, OFF)                                                  \
+    // Enqueue the loads of combined K step ks of the tile with descriptors RW, RX, offsets
+    // OFF and K rotation ROT into LDS stage Lb: the tile's step ks reads combined step
+    // (ks + ROT) mod nsteps (segment / nk of it).  Only a ragged last step of a segment
+    // masks chunks past K (they read as zero).
+#define CAAT_ISSUE_T(ks, Lb, RW, RX, OFF, ROT)                                             \
     do {                                                                                   \
-        const int g_ = (ks) / nk;                                                          \
-        const int k0_ = ((ks) - g_ * nk) * BK;                                             \
+        int p_ = (ks) + (ROT);                                                             \
+        if (p_ >= nsteps) p_ -= nsteps;                                                    \
+        const int g_ = p_ / nk;                                                            \
+        const int k0_ = (p_ - g_ * nk) * BK;                                               \
         const uint32_t sw_ = (uint32_t)((g_ * a.w_kseg + k0_) * 2u);                       \
         const uint32_t sx_ = (uint32_t)((g_ * a.x_kseg + k0_) * 2u);                       \
         if (ktail && k0_ + BK > K) {                                                       \
@@ -188,31 +200,35 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
                 const int base = (i * NW + wave) * 64;                                     \
                 const int c = cl ^ ((i * NW + wave) & 1);                                  \
                 const uint32_t o = (k0_ + c * 8 < K) ? OFF[i] : OOB;                       \
-                load_lds16(i < WLOADS ? RW : RX, (Lb) + base, o, i < WLOADS ? sw_ : sx_);  \
+                if (i < WLOADS) load_lds16_pol<WPOL>(RW, (Lb) + base, o, sw_);             \
+                else load_lds16(RX, (Lb) + base, o, sx_);                                  \
             }                                                                              \
         } else {                                                                           \
-            CAAT_UNROLL for (int i = 0; i < LOADS; ++i)                                    \
-                load_lds16(i < WLOADS ? RW : RX, (Lb) + (i * NW + wave) * 64, OFF[i],      \
-                           i < WLOADS ? sw_ : sx_);                                        \
+            CAAT_UNROLL for (int i = 0; i < LOADS; ++i) {                                  \
+                if (i < WLOADS) load_lds16_pol<WPOL>(RW, (Lb) + (i * NW + wave) * 64, OFF[i], sw_); \
+                else load_lds16(RX, (Lb) + (i * NW + wave) * 64, OFF[i], sx_);             \
+            }                                                                              \
         }                                                                                  \
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
-#define CAAT_ISSUE(ks, Lb) CAAT_ISSUE_T(ks, Lb, rW, rX, off)
+#define CAAT_ISSUE(ks, Lb) CAAT_ISSUE_T(ks, Lb, rW, rX, off, rot)
     // A quarter of step ks's loads (load indices [q LOADS / 4, (q + 1) LOADS / 4)), for
     // spreading a step's loads over the sub-steps of the step before.
 #define CAAT_ISSUE_Q(ks, Lb, q)                                                            \
     do {                                                                                   \
         constexpr int Q0_ = (q) * (LOADS / 4), Q1_ = ((q) + 1) * (LOADS / 4);              \
-        const int g_ = (ks) / nk;                                                          \
-        const int k0_ = ((ks) - g_ * nk) * BK;                                             \
+        int p_ = (ks) + rot;                                                               \
+        if (p_ >= nsteps) p_ -= nsteps;                                                    \
+        const int g_ = p_ / nk;                                                            \
+        const int k0_ = (p_ - g_ * nk) * BK;                                               \
         const uint32_t sw_ = (uint32_t)((g_ * a.w_kseg + k0_) * 2u);                       \
         const uint32_t sx_ = (uint32_t)((g_ * a.x_kseg + k0_) * 2u);                       \
         const bool tail_ = ktail && k0_ + BK > K;                                          \
         CAAT_UNROLL for (int i = Q0_; i < Q1_; ++i) {                                      \
             const int c = cl ^ ((i * NW + wave) & 1);                                      \
             const uint32_t o = (!tail_ || k0_ + c * 8 < K) ? off[i] : OOB;                 \
-            load_lds16(i < WLOADS ? rW : rX, (Lb) + (i * NW + wave) * 64, o,               \
-                       i < WLOADS ? sw_ : sx_);                                            \
+            if (i < WLOADS) load_lds16_pol<WPOL>(rW, (Lb) + (i * NW + wave) * 64, o, sw_); \
+            else load_lds16(rX, (Lb) + (i * NW + wave) * 64, o, sx_);                      \
         }                                                                                  \
         CAAT_SCHED_FENCE();                                                                \
     } while (0)
@@ -329,6 +345,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     static_assert((BT / 2) * CPP <= SLOTS && (BT * CPP) % NTH == 0, "pre-activation image");
 
     int tile = xs + idx;
+    int rot = ROTATE ? tile % nsteps : 0;
     int m, n0, t0;
     __amdgpu_buffer_rsrc_t rW, rX;
     uint32_t off[LOADS];
@@ -435,10 +452,11 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         uint32_t off2[LOADS];
         if (more) {
             CAAT_TILE_SETUP(next, m2, n02, t02, rW2, rX2, off2);
-            CAAT_ISSUE_T(0, L0, rW2, rX2, off2);
+            const int rot2 = ROTATE ? next % nsteps : 0;
+            CAAT_ISSUE_T(0, L0, rW2, rX2, off2, rot2);
             if constexpr (NST == 4) {
-                CAAT_ISSUE_T(min(1, nsteps - 1), L1, rW2, rX2, off2);
-                CAAT_ISSUE_T(min(2, nsteps - 1), L2, rW2, rX2, off2);
+                CAAT_ISSUE_T(min(1, nsteps - 1), L1, rW2, rX2, off2, rot2);
+                CAAT_ISSUE_T(min(2, nsteps - 1), L2, rW2, rX2, off2, rot2);
             }
         }
         // The output image: the stage the next tile's first steps leave free.
@@ -494,6 +512,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         }
         if (!more) break;
         tile = next; m = m2; n0 = n02; t0 = t02; rW = rW2; rX = rX2;
+        rot = ROTATE ? tile % nsteps : 0;
         CAAT_UNROLL for (int i = 0; i < LOADS; ++i) off[i] = off2[i];
     }
 #undef CAAT_READ
@@ -554,6 +573,8 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool gemm_bf16_rotates_k(const GemmArgs &a) { return a.T <= 64; }
 
 bool gemm_bf16_supported(const GemmArgs &a) {
     // Byte offsets (over every K segment) are 32-bit and must stay below the OOB marker.

@@ -205,7 +205,7 @@ def test_stored_preactivation(act, dtype, T, h, ffn):
     pre-activation x W1^T against the oracle's linear layer, and a backward fed with it
     bit-identical to the backward that recomputes it (T = 24: the weight-streaming
     kernels, which fill the pre-activation with a separate GEMM; T = 57 at h = 1024: the
-    64-token MFMA tiles, whose epilogue stores it)."""
+    64-token MFMA tiles, whose per-tile K order also calls for that separate GEMM)."""
     P = 4
     _say(f"[case] stored pre-activation act={act} {dtype} T={T}")
     d = _inputs(P, T, h, ffn, act, dtype, resid_given=True, dres_given=True)
