@@ -235,16 +235,17 @@ hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
 // shapes, three weight copies rotated, µs:
 //   * kernels alone (weight-streaming against 64-token tiles): K2 (K = 1376) 18.9 / 18.4
 //     at T = 12, 19.5 / 18.5 at T = 16; the out-projection (K = 512) 9.2 / 9.5 at T = 48,
-//     10.3 / 9.7 at T = 64; K1 (SwiGLU, K = 4096) 41.0 / 40.0 at T = 24, 52.2 / 42.0 at
-//     T = 64;
-//   * the replayed MLP step, both rules on one box: K2 on the tiles past 8 tokens took
-//     T = 12 / 16 from 58.7 / 62.1 to 57.6 / 60.2; K1 on the tiles at T = 24 / 32 was
-//     slower there (73.8 / 74.9 against 69.0 / 71.4) although faster alone, so SwiGLU
-//     stays weight-streaming up to 48 tokens; at T = 64 80.0 against 85.0.
+//     10.3 / 9.7 at T = 64; K1 (SwiGLU, K = 4096) 32.3 against ~37 at T = 16;
+//   * the replayed MLP step, rules compared on one box: K2 on the tiles past 8 tokens took
+//     T = 12 / 16 from 58.7 / 62.1 to 57.6 / 60.2 us; K1 on the tiles past 16 tokens took
+//     T = 17 / 24 / 32 / 40 / 48 from 65.8 / 66.9 / 68.9 / 71.1 / 75.3 to 61.5 / 61.9 /
+//     63.3 / 65.0 / 66.8 us.
+// So: long contractions past 8 tokens (16 for SwiGLU, whose weight blocks carry two rows
+// per output), every GEMM past 48.
 bool gemm_decode_applies(const GemmArgs &a) {
     if (a.T > 48) return false;
-    if (a.K < 1024 || a.epi == EPI_SWIGLU) return true;
-    return a.T <= 8;
+    if (a.K < 1024) return true;
+    return a.T <= (a.epi == EPI_SWIGLU ? 16 : 8);
 }
 
 // Launch shapes, measured on the 7B decode GEMMs (three weight copies rotated so the

@@ -74,8 +74,8 @@ def test_7b_decode_full(T):
 # Decode batch sizes between the benchmarked ones: each weight-streaming launch shape
 # (one or two weight blocks per wave, 1 to 4 token blocks, ragged last block), and the
 # 64-token MFMA tiles that take over the plain long contractions past 8 tokens (K2:
-# T = 9 .. 40) and every GEMM past 48 (T = 49, 56: K1 and the out-projection too); ragged
-# tiles throughout.
+# T = 9, 16), the SwiGLU GEMM past 16 (T = 17, 33, 40) and every GEMM past 48 (T = 49,
+# 56: the out-projection too); ragged tiles throughout.
 @pytest.mark.parametrize("T", [5, 8, 9, 16, 17, 33, 40, 49, 56])
 def test_7b_decode_launch_shapes(T):
     _run_and_compare(W.DECODE_7B_BF16, T=T, norm_params="random")
