@@ -189,8 +189,11 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     // masks chunks past K (they read as zero).
 #define CAAT_ISSUE_T(ks, Lb, RW, RX, OFF, ROT)                                             \
     do {                                                                                   \
-        int p_ = (ks) + (ROT);                                                             \
-        if (p_ >= nsteps) p_ -= nsteps;                                                    \
+        int p_ = (ks);                                                                     \
+        if constexpr (ROTATE) {                                                            \
+            p_ += (ROT);                                                                   \
+            if (p_ >= nsteps) p_ -= nsteps;                                                \
+        }                                                                                  \
         const int g_ = p_ / nk;                                                            \
         const int k0_ = (p_ - g_ * nk) * BK;                                               \
         const uint32_t sw_ = (uint32_t)((g_ * a.w_kseg + k0_) * 2u);                       \
@@ -217,8 +220,11 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
 #define CAAT_ISSUE_Q(ks, Lb, q)                                                            \
     do {                                                                                   \
         constexpr int Q0_ = (q) * (LOADS / 4), Q1_ = ((q) + 1) * (LOADS / 4);              \
-        int p_ = (ks) + rot;                                                               \
-        if (p_ >= nsteps) p_ -= nsteps;                                                    \
+        int p_ = (ks);                                                                     \
+        if constexpr (ROTATE) {                                                            \
+            p_ += rot;                                                                     \
+            if (p_ >= nsteps) p_ -= nsteps;                                                \
+        }                                                                                  \
         const int g_ = p_ / nk;                                                            \
         const int k0_ = (p_ - g_ * nk) * BK;                                               \
         const uint32_t sw_ = (uint32_t)((g_ * a.w_kseg + k0_) * 2u);                       \
