@@ -605,8 +605,9 @@ bool gemm_bf16_supported(const GemmArgs &a) {
 // when that is less (a lone 7B K1 shard: 352 big tiles, 2 rounds, against
 // 1408 small ones, 3 rounds: 177 against 186 us).
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s) {
-    // Up to 64 tokens (decode batches with a long contraction): 64-token tiles, so that no
-    // MFMA works on rows past the batch, with the stage rule of the small tiles below.
+    // Up to 64 tokens (the decode GEMMs the weight-streaming kernel leaves to this one):
+    // 64-token tiles, so that no MFMA works on rows past the batch, with the stage rule of
+    // the small tiles below.
     if (a.T <= 64) {
         const long ncol = (a.epi == EPI_SWIGLU) ? 64 : 128;
         const long tiles64 = (long)a.P * ((a.N + ncol - 1) / ncol);
