@@ -164,6 +164,42 @@ def test_out_projection_edge_shapes(dtype):
     _run_and_compare(w, norm_params="random")
 
 
+def _random_cases(n=32, seed=20251203):
+    """Seeded random sublayer configurations (drawn once, so the test ids are stable): MLP
+    or out-projection + MLP pair, fp32 or bf16, every activation and norm, P 1..8, widths
+    that keep every contraction and output a multiple of 8, T from decode batches to a few
+    token tiles, any p, with or without the private scaling.  Sized so that the oracle
+    finishes each in about a second."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        pair = bool(rng.integers(2))
+        dtype = ("bf16", "f32")[int(rng.integers(2))]
+        P = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        h = 8 * P * int(rng.integers(1, 1024 // (8 * P) + 1)) if pair else 8 * int(rng.integers(4, 129))
+        fs = 8 * int(rng.integers(2, 193))
+        T = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 300))]))
+        act = ("gelu", "gelu_tanh", "swiglu")[int(rng.integers(3))]
+        norm = ("layernorm", "rmsnorm")[int(rng.integers(2))]
+        pv = round(float(rng.random()), 3)
+        scaled = bool(rng.integers(2))
+        F1 = 2 * fs if act == "swiglu" else fs
+        if P * T * h * (F1 + h) > 4e8:
+            continue
+        out.append((pair, dtype, P, h, P * fs, T, act, norm, pv, scaled))
+    return out
+
+
+@pytest.mark.parametrize("pair,dtype,P,h,ffn,T,act,norm,p,scaled", _random_cases())
+def test_random_sublayer_configs(pair, dtype, P, h, ffn, T, act, norm, p, scaled):
+    """Seeded random configurations through the product path against the oracle (random
+    gamma and beta; s_priv = sqrt(P) when scaled)."""
+    base = W.PAIR_130M_BF16 if pair else W.TINY_MLP_F32
+    w = W.with_(base, name=f"random-{'pair' if pair else 'mlp'}", dtype=dtype, P=P, h=h,
+                ffn=ffn, T=T, p=p, act=act, norm=norm, replicated_x=False)
+    _run_and_compare(w, s_priv=math.sqrt(P) if scaled else 1.0, norm_params="random")
+
+
 # ---------------------------------------------------------------------------
 # The channel mask, bit-exact; cross-rank identity at p = 1; determinism
 # ---------------------------------------------------------------------------
