@@ -37,6 +37,7 @@
 // columns ([g0..31, u0..31, g32..63, u32..63, ...]), so every wave holds matching
 // gate/up accumulators in the same lanes and applies silu(g) * u in registers.
 #include "caat_internal.h"
+#include "act.h"
 #include "bufload.h"
 
 // Scheduling directives and unroll pragmas exist only in the device pass; the host
@@ -59,18 +60,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int BK = 64;
 constexpr int SG_MFMA = 0x008, SG_DS_READ = 0x100;
 
-__device__ __forceinline__ float gelu_erf(float v) {
-    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-}
-__device__ __forceinline__ float gelu_tanh(float v) {
-    // tanh form of GeLU (Hendrycks and Gimpel): c = sqrt(2 / pi), cubic coefficient 0.044715
-    return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
-}
-// silu(g) = g / (1 + e^-g), the division as a hardware reciprocal (1 ulp; the result is
-// rounded to bf16).
-__device__ __forceinline__ float silu(float g) {
-    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-}
 
 // NST: LDS stages, 2 or 4.  With 4, three K steps are in flight while one is computed
 // (for the small tiles, whose short steps cannot cover a load's latency with one).

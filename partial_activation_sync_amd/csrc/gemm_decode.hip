@@ -12,6 +12,7 @@
 // LDS in a fixed order, then the epilogue (GeLU / SwiGLU / plain store) runs in wave 0.
 // Tokens beyond T and the K tail read as zero through the buffer range check.
 #include "caat_internal.h"
+#include "act.h"
 #include "bufload.h"
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -30,13 +31,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KSTEP = 32;   // K per MFMA
 
-__device__ __forceinline__ float gelu_erf(float v) {
-    return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
-}
-__device__ __forceinline__ float gelu_tanh(float v) {
-    return 0.5f * v * (1.0f + tanhf(0.79788456080286536f * (v + 0.044715f * v * v * v)));
-}
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // The weight copy of load_lds16 with the nontemporal hint (buffer_load ... nt lds): a
 // decode step reads each weight once, so the stream need not stay in the caches.  On the
