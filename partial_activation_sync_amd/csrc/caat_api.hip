@@ -150,6 +150,21 @@ caat::GemmArgs private_args(const caat_ctx *c, int T, const void *in, const void
     return g;
 }
 
+// The private channels straight into the residual output (bf16): the private GEMM's
+// epilogue writes out_resid[m][t][l] = resid[m][t][l] + s_priv * Zt_m[t][l] for l >= n_s
+// (Zt rounded to bf16 first, one fused multiply-add: what K3 computes from the stored
+// partials), so the private partials never go through memory and K3 reads those rows
+// once instead of the partials and the residual, and writes only the shared columns of
+// out_resid.  Per sublayer that removes a [P][T][h - n_s] round trip.
+caat::GemmArgs private_resid_args(const caat_ctx *c, int T, const void *in, const void *W2,
+                                  const void *resid, void *out_resid) {
+    caat::GemmArgs g = private_args(c, T, in, W2, out_resid);
+    g.epi = caat::EPI_RESID;
+    g.res = reinterpret_cast<const char *>(resid) + (size_t)c->n_s * esize(c);
+    g.s_res = c->s_priv;
+    return g;
+}
+
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s);
 
 // Whether caat_forward_ex sums the shared channels inside the row-parallel GEMM.  The
@@ -188,6 +203,8 @@ int run_row_reduce(const caat_ctx *c, int T, const void *in, const void *W2, voi
 }
 
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
+    if (g.epi == caat::EPI_RESID && (c->dtype != CAAT_BF16 || caat::gemm_decode_applies(g)))
+        return CAAT_EUNSUPPORTED;   // only the bf16 MFMA kernel has that epilogue
     if (c->dtype == CAAT_BF16) {
         if (!caat::gemm_bf16_supported(g)) return CAAT_EUNSUPPORTED;
         const hipError_t e = caat::gemm_decode_applies(g) ? caat::gemm_decode_bf16(g, s)
@@ -199,9 +216,9 @@ int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
 
 int run_psync(const caat_ctx *c, int T, const void *partials, const void *resid,
               const void *gamma, const void *beta, void *out, void *out_resid, hipStream_t s,
-              const void *S = nullptr) {
+              const void *S = nullptr, const void *priv_r = nullptr) {
     caat::PsyncArgs a{};
-    a.S = S; a.s_ld = c->n_s;
+    a.S = S; a.s_ld = c->n_s; a.priv_r = priv_r;
     a.P = c->P; a.T = T; a.h = c->h; a.n_s = c->n_s; a.norm = c->norm;
     a.s_priv = c->s_priv; a.eps = c->eps;
     a.partials = partials; a.resid = resid; a.gamma = gamma;
@@ -375,12 +392,21 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
     CAAT_TRY(mark(0));
     if (fused_for(c, T)) {
         // 1, 2: the shared channels summed over ranks inside one GEMM, then the private
-        // channels of every rank; 3: reduce-free K3 on S and the private partials.
+        // channels of every rank (bf16 with a residual output: added to the residual in
+        // the GEMM's epilogue, straight into out_resid); 3: reduce-free K3 on S and the
+        // private partials or rows.
+        const bool priv_direct = c->dtype == CAAT_BF16 && a->out_resid != nullptr &&
+                                 c->n_s < c->h &&
+                                 caat::psync_reads_final_private(c->P, c->h, c->dtype);
         if (c->n_s > 0) CAAT_TRY(run_gemm(c, shared_args(c, T, gemm_in, a->W2, S), s));
         CAAT_TRY(mark(1));
-        if (c->n_s < c->h) CAAT_TRY(run_gemm(c, private_args(c, T, gemm_in, a->W2, Z), s));
+        if (priv_direct)
+            CAAT_TRY(run_gemm(c, private_resid_args(c, T, gemm_in, a->W2, resid, a->out_resid), s));
+        else if (c->n_s < c->h)
+            CAAT_TRY(run_gemm(c, private_args(c, T, gemm_in, a->W2, Z), s));
         CAAT_TRY(mark(2));
-        CAAT_TRY(run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s, S));
+        CAAT_TRY(run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s, S,
+                           priv_direct ? a->out_resid : nullptr));
         return mark(3);
     }
     // 1: every rank's partials; 3: the partial channel-reduce, residual and norm.

@@ -29,7 +29,8 @@ struct caat_ctx {
 namespace caat {
 
 // Epilogues of the GEMM kernels.
-enum Epilogue { EPI_STORE = 0, EPI_GELU = 1, EPI_GELU_TANH = 2, EPI_SWIGLU = 3 };
+// EPI_RESID: out = res + s_res * bf16(acc), res laid out like out (bf16 MFMA kernel only).
+enum Epilogue { EPI_STORE = 0, EPI_GELU = 1, EPI_GELU_TANH = 2, EPI_SWIGLU = 3, EPI_RESID = 4 };
 
 // One batched "NT" GEMM: for every batch index m < P, token t < T and column n < N,
 //   acc = sum_{g < kseg} sum_{k < K} W[m][g][row(n)][k] * X[m][g][t][k]
@@ -51,6 +52,10 @@ struct GemmArgs {
     // [0, N), up columns [up_off, up_off + N)).  Only the bf16 MFMA kernel writes it.
     void *pre;      size_t pre_stride;
     int ld_pre;
+    // EPI_RESID: the addend, same batch stride and row stride as out, and the factor of
+    // the accumulator (rounded to bf16 first).
+    const void *res;
+    float s_res;
 };
 
 hipError_t gemm_bf16(const GemmArgs &a, hipStream_t s);
@@ -87,9 +92,17 @@ struct PsyncArgs {
     void *out, *out_resid;
     const void *S;
     int s_ld;
+    // With S: when non-null, the private channels' residual rows r are already final
+    // there (the private GEMM's epilogue added the residual; it is out_resid), so K3
+    // reads them instead of the partials and the residual, and does not write them.
+    // Only where psync_reads_final_private holds.
+    const void *priv_r;
 };
 
 hipError_t psync_norm(const PsyncArgs &a, int dtype, hipStream_t s);
+// Whether psync_norm accepts priv_r for P ranks and rows of h channels (bf16, where the
+// single-pass kernel runs; the multi-pass kernel for wider rows does not take them).
+bool psync_reads_final_private(int P, int h, int dtype);
 
 }  // namespace caat
 

@@ -167,7 +167,8 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
     // carry the nontemporal hint.  7B decode K1 at T = 64: 42.1 -> 37.7 us with both; for
     // K2 (K = 1376) the hint cost 3 us and the rotation nothing, so K2 rotates only.
     constexpr bool ROTATE = BT == 64;
-    constexpr int WPOL = (BT == 64 && EPI != EPI_STORE) ? 2 : 0;
+    constexpr bool ACT = EPI == EPI_GELU || EPI == EPI_GELU_TANH || EPI == EPI_SWIGLU;
+    constexpr int WPOL = (BT == 64 && ACT) ? 2 : 0;
     const int nk = (K + BK - 1) / BK;          // K steps per segment
     const int nsteps = kseg * nk;              // K steps over all segments
     const bool ktail = (K % BK) != 0;
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         int te = tid;
         asm volatile("" : "+v"(te));
         const int r32e = te & 31, khe = (te >> 5) & 1;
-        if (EPI != EPI_STORE && a.pre != nullptr) {
+        if (ACT && a.pre != nullptr) {
             // The raw pre-activation first, through an image over both stages (the first
             // half of the tokens in L0, the second in L1; all BN weight rows of the tile;
             // SwiGLU: the gate columns in image chunks [0, CPR), the up columns after).
@@ -457,7 +458,22 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         // The output image: the stage the next tile's first steps leave free.
         uint4 *const IMG = (NST == 4) ? L3 : L1;
         __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
+        constexpr int SITER = PROWS * CPR / NTH;         // 16-byte stores per thread and pass
         CAAT_UNROLL for (int ps = 0; ps < NPASS; ++ps) {
+            // EPI_RESID: this pass's addend chunks, loaded where this thread stores, ahead
+            // of the image so that their latency passes under it.
+            uint4 rv[EPI == EPI_RESID ? SITER : 1];
+            if constexpr (EPI == EPI_RESID) {
+                const __bf16 *Rm = reinterpret_cast<const __bf16 *>(a.res) + (size_t)m * a.o_stride;
+                CAAT_UNROLL for (int it = 0; it < SITER; ++it) {
+                    const int q = it * NTH + te;
+                    const int r = q / CPR, c = q % CPR;
+                    const int t = t0 + ps * PROWS + r, n = n0 + c * 8;
+                    rv[it] = (t < T && n < N)
+                                 ? *reinterpret_cast<const uint4 *>(Rm + (size_t)t * a.ldo + n)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
             CAAT_UNROLL for (int j = 0; j < JB; ++j) {
                 const int tb = wt * WT + j * 32;                     // the 32 tokens' first row
                 if (tb / PROWS != ps) continue;
@@ -491,11 +507,18 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
                 }
             }
             __syncthreads();
-            CAAT_UNROLL for (int it = 0; it < PROWS * CPR / NTH; ++it) {
+            CAAT_UNROLL for (int it = 0; it < SITER; ++it) {
                 const int q = it * NTH + te;
                 const int r = q / CPR, c = q % CPR;
                 uint4 v = IMG[r * CPR + (c ^ (r & SWM))];
                 if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+                if constexpr (EPI == EPI_RESID) {
+                    const bf16x8 z = __builtin_bit_cast(bf16x8, v), rr = __builtin_bit_cast(bf16x8, rv[it]);
+                    bf16x8 o;
+                    CAAT_UNROLL for (int e = 0; e < 8; ++e)
+                        o[e] = static_cast<__bf16>(static_cast<float>(rr[e]) + a.s_res * static_cast<float>(z[e]));
+                    v = __builtin_bit_cast(uint4, o);
+                }
                 const int t = t0 + ps * PROWS + r, n = n0 + c * 8;
                 if (t < T && n < N)
                     *reinterpret_cast<uint4 *>(O + (size_t)t * a.ldo + n) = v;
@@ -563,6 +586,7 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
     case EPI_GELU: return launch_epi<BN, BT, WGN, WGT, EPI_GELU, NST>(a, tilesN, tilesT, s);
     case EPI_GELU_TANH: return launch_epi<BN, BT, WGN, WGT, EPI_GELU_TANH, NST>(a, tilesN, tilesT, s);
     case EPI_SWIGLU: return launch_epi<BN, BT, WGN, WGT, EPI_SWIGLU, NST>(a, tilesN, tilesT, s);
+    case EPI_RESID: return launch_epi<BN, BT, WGN, WGT, EPI_RESID, NST>(a, tilesN, tilesT, s);
     default: return launch_epi<BN, BT, WGN, WGT, EPI_STORE, NST>(a, tilesN, tilesT, s);
     }
 }

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
     const TIO *__restrict__ partials, const TIO *__restrict__ resid,
     const TIO *__restrict__ gamma, const TIO *__restrict__ beta,
     TIO *__restrict__ out, TIO *__restrict__ out_resid,
-    const TIO *__restrict__ Sg, int s_ld)
+    const TIO *__restrict__ Sg, int s_ld, const TIO *priv_r)
 {
     __shared__ float red[2][MAX_WAVES_1P * PMAX];
     // NT: the rows are read and written with the nontemporal forms (launches that move
@@ -227,6 +227,12 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
         for (int j = 0; j < NCH; ++j) {
             if (!valid[j]) continue;
             const size_t off = m * rank_stride + row + ch0[j];
+            if (priv_r != nullptr && ch0[j] >= n_s) {
+                // r is final in priv_r: res + s_priv * 0.
+                zr[m][j].zero();
+                ld(rr[m][j], priv_r + off);
+                continue;
+            }
             if (Sg == nullptr || ch0[j] + 8 > n_s) ld(zr[m][j], partials + off);
             else zr[m][j].zero();
             ld(rr[m][j], resid + off);
@@ -260,7 +266,8 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
         rr[m][j].unpack(res);
         zr[m][j].unpack(z);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = res[e] + ((ch0[j] + e < n_s) ? S[j][e] : s_priv * z[e]);
+        for (int e = 0; e < 8; ++e)
+            r[e] = (ch0[j] + e < n_s) ? res[e] + S[j][e] : fmaf(s_priv, z[e], res[e]);
     };
 
     float mean[PMAX], inv[PMAX];
@@ -325,7 +332,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = (r[e] - mean[m]) * inv[m] * gm[e] + bt[e];
             st(out + off, o);
-            if (out_resid != nullptr) st(out_resid + off, r);
+            if (out_resid != nullptr && (priv_r == nullptr || ch0[j] < n_s)) st(out_resid + off, r);
         }
     }
 }
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_rank(
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            r[j][e] = res[e] + ((ch0 + e < n_s) ? S[e] : s_priv * z[e]);
+            r[j][e] = (ch0 + e < n_s) ? res[e] + S[e] : fmaf(s_priv, z[e], res[e]);
             acc[0] += (NORM == CAAT_LAYERNORM) ? r[j][e] : r[j][e] * r[j][e];
         }
     }
@@ -447,6 +454,18 @@ __global__ __launch_bounds__(512) void k_psync_norm_rank(
     }
 }
 
+// The single-pass kernel's shape for P ranks and rows of h channels (esize bytes per
+// element): PMAX (P rounded up to a power of two) and chunks per thread (up to 512
+// threads per token), and whether it is used.  Its registers for one token's raw inputs
+// are 2 * PMAX * NCH chunks of 16 (bf16) or 32 (fp32) bytes, kept <= 128 VGPRs.
+bool one_pass_shape(int P, int h, int esize, int *pmax, int *nch) {
+    *pmax = P <= 1 ? 1 : P <= 2 ? 2 : P <= 4 ? 4 : P <= 8 ? 8 : 16;
+    const int budget = esize == 2 ? 16 : 8;
+    *nch = 1;
+    while (*nch < 8 && h / 8 > *nch * 512) *nch *= 2;
+    return *pmax * *nch <= budget;
+}
+
 template <int NORM, typename TIO>
 hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     const int nchunk = a.h / 8;
@@ -462,7 +481,11 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     auto O = reinterpret_cast<TIO *>(a.out);
     auto OR = reinterpret_cast<TIO *>(a.out_resid);
     auto Sp = reinterpret_cast<const TIO *>(a.S);
-    if (a.T <= 64 && a.P > 1) {
+    auto PR = reinterpret_cast<const TIO *>(a.priv_r);
+    // Final private rows come only with S, on channel chunks that are all shared or all
+    // private (n_s % 8 == 0), and only to the single-pass kernel.
+    if (PR != nullptr && (Sp == nullptr || a.n_s % 8 != 0)) return hipErrorInvalidValue;
+    if (a.T <= 64 && a.P > 1 && PR == nullptr) {
         int nchr = 1;
         while (nchr < 4 && nchunk > nchr * 512) nchr *= 2;
         if (nchunk <= nchr * 512) {
@@ -484,14 +507,8 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    // Registers for one token's raw inputs: 2 * PMAX * NCH chunks of 16 (bf16) or 32
-    // (fp32) bytes; the single-pass kernel is used while that stays <= 128 VGPRs.
-    const int pmax = a.P <= 1 ? 1 : a.P <= 2 ? 2 : a.P <= 4 ? 4 : a.P <= 8 ? 8 : 16;
-    const int budget = sizeof(TIO) == 2 ? 16 : 8;
-    // Up to 512 threads per token here: fewer chunks per thread, fewer registers.
-    int nch1 = 1;
-    while (nch1 < 8 && nchunk > nch1 * 512) nch1 *= 2;
-    if (pmax * nch1 <= budget) {
+    int pmax, nch1;
+    if (one_pass_shape(a.P, a.h, (int)sizeof(TIO), &pmax, &nch1)) {
         const int nch = nch1;
         int th = (nchunk + nch - 1) / nch;
         th = (th + 63) / 64 * 64;
@@ -502,10 +519,11 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
 #define CAAT_K3S(PM, N)                                                                        \
     if (nt)                                                                                    \
         hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, true>), grid, block, 0, s, a.P, \
-                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld); \
+                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld, \
+                           PR);                                                                \
     else                                                                                       \
         hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, false>), grid, block, 0, s, a.P, \
-                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
+                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld, PR)
         switch (pmax * 16 + nch) {
         case 1 * 16 + 1: CAAT_K3S(1, 1); break;
         case 1 * 16 + 2: CAAT_K3S(1, 2); break;
@@ -527,6 +545,7 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
         return hipGetLastError();
     }
 multipass:
+    if (PR != nullptr) return hipErrorInvalidValue;   // only the single-pass kernel reads them
 #define CAAT_K3(N)                                                                     \
     hipLaunchKernelGGL((k_psync_norm<N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
                        a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
@@ -541,6 +560,11 @@ multipass:
 }
 
 }  // namespace
+
+bool psync_reads_final_private(int P, int h, int dtype) {
+    int pmax, nch;
+    return dtype == CAAT_BF16 && one_pass_shape(P, h, 2, &pmax, &nch);
+}
 
 hipError_t psync_norm(const PsyncArgs &a, int dtype, hipStream_t s) {
     if (dtype == CAAT_BF16)
