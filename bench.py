@@ -43,18 +43,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(w, T, name, store_resid, n_s, fused):
+def kernel_work(w, T, name, store_resid, n_s, fused, direct=False):
     """Algorithmic FLOPs and HBM bytes of one step of the path ("attn.K2", "mlp.K1", ...),
     or of one of the two row-parallel launches of the fused path ("mlp.K2.shared",
     "mlp.K2.private").  fused: the library sums the shared channels inside the row GEMM
-    (caat_forward_fused) and K3 reads S [T][n_s] once plus every rank's private columns."""
+    (caat_forward_fused) and K3 reads S [T][n_s] once plus every rank's private columns.
+    direct (caat_forward_private_in_epilogue, with store_resid): the private GEMM reads the
+    residual and writes out_resid's private columns, and K3 reads those rows back in place
+    of the partials and the residual and writes out_resid's shared columns only."""
     P, h, fs = w.P, w.h, w.f_s
     b = 2 if w.dtype == "bf16" else 4
     F1 = 2 * fs if w.act == "swiglu" else fs
     E = P * T * h
+    direct = direct and fused and store_resid
     if name == "mlp.K1":
         return 2.0 * P * T * h * F1, b * (P * T * h + P * F1 * h + P * T * fs)
-    part = P * T * (h - n_s) + T * n_s if fused else E
+    priv = P * T * (h - n_s)
+    part = (priv + T * n_s if fused else E) + (priv if direct else 0)
     k = fs if name.startswith("mlp") else h // P
     if name.endswith("K2"):
         return 2.0 * P * T * k * h, b * (P * T * k + P * h * k + part)
@@ -62,8 +67,10 @@ def kernel_work(w, T, name, store_resid, n_s, fused):
         return 2.0 * P * T * k * n_s, b * (P * T * k + P * n_s * k + T * n_s)
     if name.endswith("K2.private"):
         return (2.0 * P * T * k * (h - n_s),
-                b * (P * T * k + P * (h - n_s) * k + P * T * (h - n_s)))
+                b * (P * T * k + P * (h - n_s) * k + priv * (2 if direct else 1)))
     if name.endswith("K3"):
+        if direct:   # S, the residual (shared) and r (private) in; out, out_resid (shared) out
+            return 0.0, b * (T * n_s + E + E + P * T * n_s + 2 * h)
         return 0.0, b * (part + E + E + (E if store_resid else 0) + 2 * h)
     raise KeyError(name)
 
@@ -664,6 +671,7 @@ def main():
     # asked of it.
     handles = {"attn": run.attn, "mlp": run.mlp}
     fused = {sub: caat.caat_forward_fused(handles[sub].handle, T) for sub in subs}
+    direct = {sub: caat.caat_forward_private_in_epilogue(handles[sub].handle, T) for sub in subs}
 
     K = args.steps
     span_ms, per_step, step_ms, wall = timed_steps(run, K, args.warmup, rotate)
@@ -708,7 +716,8 @@ def main():
     log(f"[bench] {K} steps: {eager_ms:.4f} ms/step (events), wall {wall * 1e3:.3f} ms/step")
 
     work = lambda name: kernel_work(w, T, name, store_resid=True, n_s=n_s,
-                                    fused=fused[name.split(".")[0]])
+                                    fused=fused[name.split(".")[0]],
+                                    direct=direct[name.split(".")[0]])
 
     def describe(name, ms):
         flops, nbytes = work(name)
@@ -797,7 +806,8 @@ def main():
         "dtype": w.dtype, "data": "synthetic: seeded N(0,1) activations, N(0,0.02^2) weights",
         "config": {"workload": w.name, "P": w.P, "h": w.h, "ffn": w.ffn, "T": T, "p": p,
                    "weight_copies": rotate, "hip_graph": bool(args.graph),
-                   "n_s": n_s, "fused_row_gemm": fused, "act": w.act, "norm": w.norm,
+                   "n_s": n_s, "fused_row_gemm": fused, "private_rows_in_gemm": direct,
+                   "act": w.act, "norm": w.norm,
                    "sublayers": list(w.sublayers),
                    "parallelism": f"tp{w.P} emulated on 1 GPU"},
         "roofline": roof,

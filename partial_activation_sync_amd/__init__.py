@@ -94,6 +94,7 @@ def lib():
         L.caat_forward_timed.argtypes = [vp, ctypes.POINTER(caat_args),
                                          ctypes.POINTER(ctypes.c_void_p), i]
         L.caat_forward_fused.argtypes = [vp, i]
+        L.caat_forward_private_in_epilogue.argtypes = [vp, i]
         L.caat_forward_scratch.argtypes = [vp, ctypes.POINTER(caat_args)]
         L.caat_forward_train.argtypes = [vp, ctypes.POINTER(caat_args), vp]
         L.caat_column_gemm_act.argtypes = [vp, i, vp, vp, vp, vp]
@@ -116,6 +117,7 @@ def lib():
         for name in ("caat_create", "caat_destroy", "caat_set_eps", "caat_set_private_scale",
                      "caat_shared_channels", "caat_set_workspace", "caat_forward",
                      "caat_forward_ex", "caat_forward_timed", "caat_forward_fused",
+                     "caat_forward_private_in_epilogue",
                      "caat_forward_scratch",
                      "caat_forward_train",
                      "caat_column_gemm_act",
@@ -225,6 +227,15 @@ def caat_forward_fused(handle, T) -> bool:
     rc = lib().caat_forward_fused(handle, int(T))
     if rc < 0:
         raise CaatError("caat_forward_fused", rc)
+    return bool(rc)
+
+
+def caat_forward_private_in_epilogue(handle, T) -> bool:
+    """Whether a forward over T tokens with a residual output adds the private channels'
+    residual in the private GEMM's epilogue (K3 then reads those rows)."""
+    rc = lib().caat_forward_private_in_epilogue(handle, int(T))
+    if rc < 0:
+        raise CaatError("caat_forward_private_in_epilogue", rc)
     return bool(rc)
 
 

@@ -191,6 +191,13 @@ bool fused_for(const caat_ctx *c, int T) {
     return true;
 }
 
+// Whether a fused forward with a residual output writes the private channels' rows from
+// the private GEMM's epilogue (bf16; K3's single-pass kernel, which reads them, runs).
+bool private_direct_for(const caat_ctx *c, int T) {
+    return fused_for(c, T) && c->dtype == CAAT_BF16 && c->n_s < c->h &&
+           caat::psync_reads_final_private(c->P, c->h, c->dtype);
+}
+
 // Row-parallel GEMM with the shared channels reduced over ranks inside the GEMM.
 int run_row_reduce(const caat_ctx *c, int T, const void *in, const void *W2, void *S, void *Z,
                    hipStream_t s) {
@@ -395,9 +402,7 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
         // channels of every rank (bf16 with a residual output: added to the residual in
         // the GEMM's epilogue, straight into out_resid); 3: reduce-free K3 on S and the
         // private partials or rows.
-        const bool priv_direct = c->dtype == CAAT_BF16 && a->out_resid != nullptr &&
-                                 c->n_s < c->h &&
-                                 caat::psync_reads_final_private(c->P, c->h, c->dtype);
+        const bool priv_direct = a->out_resid != nullptr && private_direct_for(c, T);
         if (c->n_s > 0) CAAT_TRY(run_gemm(c, shared_args(c, T, gemm_in, a->W2, S), s));
         CAAT_TRY(mark(1));
         if (priv_direct)
@@ -431,6 +436,11 @@ CAAT_API int caat_forward_scratch(caat_handle c, const caat_args *a) {
 CAAT_API int caat_forward_fused(caat_handle c, int T) {
     if (c == nullptr || T < 1) return CAAT_EINVAL;
     return fused_for(c, T) ? 1 : 0;
+}
+
+CAAT_API int caat_forward_private_in_epilogue(caat_handle c, int T) {
+    if (c == nullptr || T < 1) return CAAT_EINVAL;
+    return private_direct_for(c, T) ? 1 : 0;
 }
 
 CAAT_API int caat_forward_timed(caat_handle c, const caat_args *a, void *const *events,

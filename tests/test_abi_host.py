@@ -322,6 +322,31 @@ def test_forward_path_query():
             caat.caat_destroy(hd)
 
 
+def test_private_in_epilogue_query():
+    """caat_forward_private_in_epilogue: on the fused path, in bf16, where K3's single-pass
+    kernel handles the rows (P = 8: up to 4096 channels), and with private channels left."""
+    L = caat.lib()
+    mlp = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+    full = caat.caat_create(4096, 11008, 8, 1.0, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+    wide = caat.caat_create(16384, 0, 8, 0.0, caat.RMSNORM, caat.NONE, caat.BF16)
+    wide2 = caat.caat_create(16384, 0, 2, 0.0, caat.RMSNORM, caat.NONE, caat.BF16)
+    f32 = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.F32)
+    try:
+        assert caat.caat_forward_private_in_epilogue(mlp, 8192) is True
+        assert caat.caat_forward_private_in_epilogue(mlp, 64) is False    # not fused
+        assert caat.caat_forward_private_in_epilogue(mlp, 1920) is False  # too few shared tiles
+        assert caat.caat_forward_private_in_epilogue(full, 8192) is False # no private channels
+        assert caat.caat_forward_private_in_epilogue(wide, 100) is False  # multi-pass K3
+        assert caat.caat_forward_fused(wide, 100) is True
+        assert caat.caat_forward_private_in_epilogue(wide2, 100) is True  # one pass at P = 2
+        assert caat.caat_forward_private_in_epilogue(f32, 8192) is False
+        assert L.caat_forward_private_in_epilogue(None, 8) == caat.EINVAL
+        assert L.caat_forward_private_in_epilogue(mlp, 0) == caat.EINVAL
+    finally:
+        for hd in (mlp, full, wide, wide2, f32):
+            caat.caat_destroy(hd)
+
+
 def test_forward_timed_checks_events():
     L = caat.lib()
     fake = 0x10000

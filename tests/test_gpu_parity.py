@@ -497,6 +497,7 @@ def test_forward_private_rows_from_gemm_epilogue(wname, T, p):
     s = caat.Sublayer(w.h, w.ffn, w.P, p, norm=w.norm, act="none" if attn else w.act,
                       dtype=w.dtype, s_priv=1.75)
     assert caat.caat_forward_fused(s.handle, T), "the case must take the fused path"
+    assert caat.caat_forward_private_in_epilogue(s.handle, T), "and the epilogue's private rows"
     inp, W1, W2, resid = (d["ctx"], None, d["Wo"], d["x0"]) if attn else (d["x"], d["W1"], d["W2"], d["x"])
     P, h, n_s = w.P, w.h, s.n_s
     out = torch.empty((P, T, h), dtype=dt, device="cuda")
