@@ -200,6 +200,45 @@ def test_random_sublayer_configs(pair, dtype, P, h, ffn, T, act, norm, p, scaled
     _run_and_compare(w, s_priv=math.sqrt(P) if scaled else 1.0, norm_params="random")
 
 
+def _random_fused_cases(n=8, seed=20251204):
+    """Seeded random bf16 MLP and pair configurations large enough for the fused path with
+    the private rows written by the private GEMM's epilogue (n_s % 8 == 0 and at least 256
+    shared-GEMM tiles of 128 x 128), T ragged against the tiles; the oracle runs on 48
+    sampled token rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        pair = bool(rng.integers(2))
+        P = int(rng.choice([2, 4, 8]))
+        h = int(rng.choice([1024, 2048, 4096]))
+        n_s = 8 * int(rng.integers(1, h // 8))
+        T = 128 * int(rng.integers(8, 40)) + int(rng.integers(0, 128))
+        if -(-n_s // 128) * -(-T // 128) < 256 or P * T * h > 2 ** 27:
+            continue
+        fs = 8 * int(rng.integers(8, 129))
+        act = ("gelu", "gelu_tanh", "swiglu")[int(rng.integers(3))]
+        norm = ("layernorm", "rmsnorm")[int(rng.integers(2))]
+        scaled = bool(rng.integers(2))
+        out.append((pair, P, h, P * fs, T, n_s / h, act, norm, scaled))
+    return out
+
+
+@pytest.mark.parametrize("pair,P,h,ffn,T,p,act,norm,scaled", _random_fused_cases())
+def test_random_fused_configs(pair, P, h, ffn, T, p, act, norm, scaled):
+    """The fused path with the epilogue's private rows on seeded random shapes, against the
+    oracle on sampled rows (random gamma and beta; s_priv = sqrt(P) when scaled)."""
+    base = W.PAIR_130M_BF16 if pair else W.TINY_MLP_F32
+    w = W.with_(base, name=f"random-fused-{'pair' if pair else 'mlp'}", dtype="bf16", P=P, h=h,
+                ffn=ffn, T=T, p=p, act=act, norm=norm, replicated_x=False)
+    hd = caat.Sublayer(h, ffn, P, p, act="none" if pair else act, dtype="bf16")
+    assert caat.caat_forward_private_in_epilogue(hd.handle, T)
+    if pair:
+        hm = caat.Sublayer(h, ffn, P, p, act=act, dtype="bf16")
+        assert caat.caat_forward_private_in_epilogue(hm.handle, T)
+    _run_and_compare(w, s_priv=math.sqrt(P) if scaled else 1.0, norm_params="random",
+                     rows=synth.sample_rows(T, 48))
+
+
 # ---------------------------------------------------------------------------
 # The channel mask, bit-exact; cross-rank identity at p = 1; determinism
 # ---------------------------------------------------------------------------
