@@ -48,18 +48,24 @@ def kernel_work(w, T, name, store_resid, n_s, fused, direct=False):
     or of one of the two row-parallel launches of the fused path ("mlp.K2.shared",
     "mlp.K2.private").  fused: the library sums the shared channels inside the row GEMM
     (caat_forward_fused) and K3 reads S [T][n_s] once plus every rank's private columns.
-    direct (caat_forward_private_in_epilogue, with store_resid): the private GEMM reads the
-    residual and writes out_resid's private columns, and K3 reads those rows back in place
-    of the partials and the residual and writes out_resid's shared columns only."""
+    direct (caat_forward_private_in_epilogue, with store_resid): the row GEMM reads the
+    residual and writes out_resid's private columns (fused: from n_s; per-rank: from n_s
+    rounded up to 8), and K3 reads those rows back in place of the partials and the
+    residual and writes out_resid's other columns only."""
     P, h, fs = w.P, w.h, w.f_s
     b = 2 if w.dtype == "bf16" else 4
     F1 = 2 * fs if w.act == "swiglu" else fs
     E = P * T * h
-    direct = direct and fused and store_resid
+    direct = direct and store_resid
     if name == "mlp.K1":
         return 2.0 * P * T * h * F1, b * (P * T * h + P * F1 * h + P * T * fs)
+    first = n_s if fused else (n_s + 7) // 8 * 8      # first column of the direct rows
     priv = P * T * (h - n_s)
-    part = (priv + T * n_s if fused else E) + (priv if direct else 0)
+    if direct and not fused:
+        # partials for columns below `first`, then read residual + write out_resid above
+        part = P * T * first + 2 * P * T * (h - first)
+    else:
+        part = (priv + T * n_s if fused else E) + (priv if direct else 0)
     k = fs if name.startswith("mlp") else h // P
     if name.endswith("K2"):
         return 2.0 * P * T * k * h, b * (P * T * k + P * h * k + part)
@@ -69,8 +75,10 @@ def kernel_work(w, T, name, store_resid, n_s, fused, direct=False):
         return (2.0 * P * T * k * (h - n_s),
                 b * (P * T * k + P * (h - n_s) * k + priv * (2 if direct else 1)))
     if name.endswith("K3"):
-        if direct:   # S, the residual (shared) and r (private) in; out, out_resid (shared) out
+        if direct and fused:   # S, the residual (shared), r (private) in; out, out_resid (shared) out
             return 0.0, b * (T * n_s + E + E + P * T * n_s + 2 * h)
+        if direct:             # partials + residual below `first`, r above; out, out_resid below
+            return 0.0, b * (P * T * first + E + E + P * T * first + 2 * h)
         return 0.0, b * (part + E + E + (E if store_resid else 0) + 2 * h)
     raise KeyError(name)
 

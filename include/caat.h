@@ -165,13 +165,14 @@ int caat_forward_scratch(caat_handle handle, const caat_args *args);
 int caat_forward_fused(caat_handle handle, int T);
 
 /* Whether a forward over T tokens that stores out_resid takes the private channels'
- * residual add into the private-channel GEMM (Eq. 9's r = R + Z on l >= n_s, with Z the
+ * residual add into the row-parallel GEMM (Eq. 9's r = R + Z on l >= n_s, with Z the
  * rank's own partial, §4 private scaling applied): that GEMM's epilogue writes those
- * columns of out_resid directly and K3 reads them back instead of the partials and the
- * residual.  1 on the fused path in bf16 where K3's single-pass kernel runs (rows of up
- * to 4096 channels at P = 8; 16384 at P <= 2), 0 otherwise (and whenever out_resid is
- * NULL); CAAT_EINVAL for a NULL handle or T < 1.  The outputs meet the same contract
- * either way.  Host only. */
+ * columns of out_resid directly (on the per-rank path, from n_s rounded up to a multiple
+ * of 8; the chunk that straddles n_s still goes through the partials) and K3 reads them
+ * back instead of the partials and the residual.  1 in bf16 for T > 64 where K3's
+ * single-pass kernel runs (rows of up to 4096 channels at P = 8; 16384 at P <= 2) and such
+ * private columns exist, 0 otherwise (and whenever out_resid is NULL); CAAT_EINVAL for a
+ * NULL handle or T < 1.  The outputs meet the same contract either way.  Host only. */
 int caat_forward_private_in_epilogue(caat_handle handle, int T);
 
 /* caat_forward_ex that also records caller-created hipEvent_t events[k] on the stream

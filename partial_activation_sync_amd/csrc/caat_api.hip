@@ -160,7 +160,24 @@ caat::GemmArgs private_resid_args(const caat_ctx *c, int T, const void *in, cons
                                   const void *resid, void *out_resid) {
     caat::GemmArgs g = private_args(c, T, in, W2, out_resid);
     g.epi = caat::EPI_RESID;
+    g.split = 0;
+    g.out2 = g.out;
     g.res = reinterpret_cast<const char *>(resid) + (size_t)c->n_s * esize(c);
+    g.s_res = c->s_priv;
+    return g;
+}
+
+// The per-rank row GEMM with the same treatment of the private channels: columns below
+// n_s rounded up to 8 are written to the partials (K3 sums their shared channels over
+// the ranks; a chunk that straddles n_s goes there whole), the rest straight into
+// out_resid as R + s_priv * Zt.
+caat::GemmArgs row_resid_args(const caat_ctx *c, int T, const void *in, const void *W2, void *Z,
+                              const void *resid, void *out_resid) {
+    caat::GemmArgs g = row_args(c, T, in, W2, Z);
+    g.epi = caat::EPI_RESID_SPLIT;
+    g.split = (c->n_s + 7) / 8 * 8;
+    g.out2 = out_resid;
+    g.res = resid;
     g.s_res = c->s_priv;
     return g;
 }
@@ -191,11 +208,23 @@ bool fused_for(const caat_ctx *c, int T) {
     return true;
 }
 
-// Whether a fused forward with a residual output writes the private channels' rows from
-// the private GEMM's epilogue (bf16; K3's single-pass kernel, which reads them, runs).
+// Whether a forward with a residual output writes the private channels' rows from the
+// row GEMM's epilogue (bf16, T > 64, K3's single-pass kernel, which reads them, runs, and
+// some private channel chunk is left: from n_s on when fused, else from n_s rounded up to
+// a whole chunk of 8).
+// On the per-rank path only for rows of at least 2^25 elements over all ranks: there the
+// bytes K3 saves outweigh the addend the GEMM's epilogue reads (1.1B MLP at p = 0.37,
+// T = 8192: 0.741 -> 0.726 ms per replayed step), while the 130M pair (2^23.6) went
+// 0.1225 -> 0.1240 ms, its short-K row GEMMs taking what K3 gave back.
+constexpr long PER_RANK_DIRECT_MIN = 1L << 25;
+
 bool private_direct_for(const caat_ctx *c, int T) {
-    return fused_for(c, T) && c->dtype == CAAT_BF16 && c->n_s < c->h &&
-           caat::psync_reads_final_private(c->P, c->h, c->dtype);
+    if (c->dtype != CAAT_BF16 || T <= 64) return false;   // the MFMA tiles and K3's one pass
+    if (!caat::psync_reads_final_private(c->P, c->h, c->dtype)) return false;
+    const bool fused = fused_for(c, T);
+    if (!fused && (long)c->P * T * c->h < PER_RANK_DIRECT_MIN) return false;
+    const int first = fused ? c->n_s : (c->n_s + 7) / 8 * 8;
+    return first < c->h;
 }
 
 // Row-parallel GEMM with the shared channels reduced over ranks inside the GEMM.
@@ -210,7 +239,8 @@ int run_row_reduce(const caat_ctx *c, int T, const void *in, const void *W2, voi
 }
 
 int run_gemm(const caat_ctx *c, const caat::GemmArgs &g, hipStream_t s) {
-    if (g.epi == caat::EPI_RESID && (c->dtype != CAAT_BF16 || caat::gemm_decode_applies(g)))
+    if ((g.epi == caat::EPI_RESID || g.epi == caat::EPI_RESID_SPLIT) &&
+        (c->dtype != CAAT_BF16 || caat::gemm_decode_applies(g)))
         return CAAT_EUNSUPPORTED;   // only the bf16 MFMA kernel has that epilogue
     if (c->dtype == CAAT_BF16) {
         if (!caat::gemm_bf16_supported(g)) return CAAT_EUNSUPPORTED;
@@ -414,11 +444,16 @@ int forward_impl(caat_handle c, const caat_args *a, void *preact, void *const *e
                            priv_direct ? a->out_resid : nullptr));
         return mark(3);
     }
-    // 1: every rank's partials; 3: the partial channel-reduce, residual and norm.
-    CAAT_TRY(run_gemm(c, row_args(c, T, gemm_in, a->W2, Z), s));
+    // 1: every rank's partials (bf16 with a residual output: the whole private chunks go
+    // straight into out_resid with the residual added); 3: the partial channel-reduce,
+    // residual and norm.
+    const bool priv_direct = a->out_resid != nullptr && private_direct_for(c, T);
+    CAAT_TRY(run_gemm(c, priv_direct ? row_resid_args(c, T, gemm_in, a->W2, Z, resid, a->out_resid)
+                                     : row_args(c, T, gemm_in, a->W2, Z), s));
     CAAT_TRY(mark(1));
     CAAT_TRY(mark(2));
-    CAAT_TRY(run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s));
+    CAAT_TRY(run_psync(c, T, Z, resid, a->gamma, a->beta, a->out, a->out_resid, s, nullptr,
+                       priv_direct ? a->out_resid : nullptr));
     return mark(3);
 #undef CAAT_TRY
 }

@@ -29,8 +29,11 @@ struct caat_ctx {
 namespace caat {
 
 // Epilogues of the GEMM kernels.
-// EPI_RESID: out = res + s_res * bf16(acc), res laid out like out (bf16 MFMA kernel only).
-enum Epilogue { EPI_STORE = 0, EPI_GELU = 1, EPI_GELU_TANH = 2, EPI_SWIGLU = 3, EPI_RESID = 4 };
+// EPI_RESID: out2 = res + s_res * bf16(acc) (one fused multiply-add) for every column;
+// EPI_RESID_SPLIT: the same for columns n >= split, out = bf16(acc) for the others.  res
+// and out2 are laid out like out (bf16 MFMA kernel only).
+enum Epilogue { EPI_STORE = 0, EPI_GELU = 1, EPI_GELU_TANH = 2, EPI_SWIGLU = 3, EPI_RESID = 4,
+                EPI_RESID_SPLIT = 5 };
 
 // One batched "NT" GEMM: for every batch index m < P, token t < T and column n < N,
 //   acc = sum_{g < kseg} sum_{k < K} W[m][g][row(n)][k] * X[m][g][t][k]
@@ -52,9 +55,12 @@ struct GemmArgs {
     // [0, N), up columns [up_off, up_off + N)).  Only the bf16 MFMA kernel writes it.
     void *pre;      size_t pre_stride;
     int ld_pre;
-    // EPI_RESID: the addend, same batch stride and row stride as out, and the factor of
-    // the accumulator (rounded to bf16 first).
+    // EPI_RESID(_SPLIT): the first column (a multiple of 8) that takes the addend (split
+    // only), the addend and that part's output (same batch stride and row stride as out),
+    // and the factor of the accumulator (rounded to bf16 first).
+    int split;
     const void *res;
+    void *out2;
     float s_res;
 };
 
@@ -92,10 +98,10 @@ struct PsyncArgs {
     void *out, *out_resid;
     const void *S;
     int s_ld;
-    // With S: when non-null, the private channels' residual rows r are already final
-    // there (the private GEMM's epilogue added the residual; it is out_resid), so K3
-    // reads them instead of the partials and the residual, and does not write them.
-    // Only where psync_reads_final_private holds.
+    // When non-null, the residual rows r of the private channel chunks (from n_s rounded
+    // up to 8; with S, n_s % 8 == 0) are already final there (the row GEMM's epilogue
+    // added the residual; it is out_resid), so K3 reads them instead of the partials and
+    // the residual, and does not write them.  Only where psync_reads_final_private holds.
     const void *priv_r;
 };
 

@@ -458,18 +458,22 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
         // The output image: the stage the next tile's first steps leave free.
         uint4 *const IMG = (NST == 4) ? L3 : L1;
         __bf16 *O = reinterpret_cast<__bf16 *>(a.out) + (size_t)m * a.o_stride;
+        // EPI_RESID: every column goes to out2 with the addend; EPI_RESID_SPLIT: the columns
+        // from a.split on, the others to out.
+        constexpr bool RES = EPI == EPI_RESID || EPI == EPI_RESID_SPLIT;
+        __bf16 *O2 = RES ? reinterpret_cast<__bf16 *>(a.out2) + (size_t)m * a.o_stride : O;
         constexpr int SITER = PROWS * CPR / NTH;         // 16-byte stores per thread and pass
         CAAT_UNROLL for (int ps = 0; ps < NPASS; ++ps) {
             // EPI_RESID: this pass's addend chunks, loaded where this thread stores, ahead
             // of the image so that their latency passes under it.
-            uint4 rv[EPI == EPI_RESID ? SITER : 1];
-            if constexpr (EPI == EPI_RESID) {
+            uint4 rv[RES ? SITER : 1];
+            if constexpr (RES) {
                 const __bf16 *Rm = reinterpret_cast<const __bf16 *>(a.res) + (size_t)m * a.o_stride;
                 CAAT_UNROLL for (int it = 0; it < SITER; ++it) {
                     const int q = it * NTH + te;
                     const int r = q / CPR, c = q % CPR;
                     const int t = t0 + ps * PROWS + r, n = n0 + c * 8;
-                    rv[it] = (t < T && n < N)
+                    rv[it] = (t < T && n < N && (EPI == EPI_RESID || n >= a.split))
                                  ? *reinterpret_cast<const uint4 *>(Rm + (size_t)t * a.ldo + n)
                                  : make_uint4(0u, 0u, 0u, 0u);
                 }
@@ -512,16 +516,20 @@ __global__ __launch_bounds__(64 * WGN * WGT) void k_gemm_bf16(GemmArgs a, int ti
                 const int r = q / CPR, c = q % CPR;
                 uint4 v = IMG[r * CPR + (c ^ (r & SWM))];
                 if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-                if constexpr (EPI == EPI_RESID) {
-                    const bf16x8 z = __builtin_bit_cast(bf16x8, v), rr = __builtin_bit_cast(bf16x8, rv[it]);
-                    bf16x8 o;
-                    CAAT_UNROLL for (int e = 0; e < 8; ++e)
-                        o[e] = static_cast<__bf16>(static_cast<float>(rr[e]) + a.s_res * static_cast<float>(z[e]));
-                    v = __builtin_bit_cast(uint4, o);
-                }
                 const int t = t0 + ps * PROWS + r, n = n0 + c * 8;
+                __bf16 *dst = O;
+                if constexpr (RES) {
+                    if (EPI == EPI_RESID || n >= a.split) {
+                        const bf16x8 z = __builtin_bit_cast(bf16x8, v), rr = __builtin_bit_cast(bf16x8, rv[it]);
+                        bf16x8 o;
+                        CAAT_UNROLL for (int e = 0; e < 8; ++e)
+                            o[e] = static_cast<__bf16>(fmaf(a.s_res, static_cast<float>(z[e]), static_cast<float>(rr[e])));
+                        v = __builtin_bit_cast(uint4, o);
+                        dst = O2;
+                    }
+                }
                 if (t < T && n < N)
-                    *reinterpret_cast<uint4 *>(O + (size_t)t * a.ldo + n) = v;
+                    *reinterpret_cast<uint4 *>(dst + (size_t)t * a.ldo + n) = v;
             }
             if (ps + 1 < NPASS) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -587,6 +595,8 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
     case EPI_GELU_TANH: return launch_epi<BN, BT, WGN, WGT, EPI_GELU_TANH, NST>(a, tilesN, tilesT, s);
     case EPI_SWIGLU: return launch_epi<BN, BT, WGN, WGT, EPI_SWIGLU, NST>(a, tilesN, tilesT, s);
     case EPI_RESID: return launch_epi<BN, BT, WGN, WGT, EPI_RESID, NST>(a, tilesN, tilesT, s);
+    case EPI_RESID_SPLIT:
+        return launch_epi<BN, BT, WGN, WGT, EPI_RESID_SPLIT, NST>(a, tilesN, tilesT, s);
     default: return launch_epi<BN, BT, WGN, WGT, EPI_STORE, NST>(a, tilesN, tilesT, s);
     }
 }

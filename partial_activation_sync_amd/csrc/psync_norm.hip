@@ -205,6 +205,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
     const size_t rank_stride = (size_t)T * h;
     const size_t row = (size_t)t * h;
     const float inv_h = 1.0f / (float)h;
+    const int ns8 = (n_s + 7) & ~7;   // with priv_r: the first chunk of final private rows
 
     int ch0[NCH];
     bool valid[NCH];
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
         for (int j = 0; j < NCH; ++j) {
             if (!valid[j]) continue;
             const size_t off = m * rank_stride + row + ch0[j];
-            if (priv_r != nullptr && ch0[j] >= n_s) {
+            if (priv_r != nullptr && ch0[j] >= ns8) {
                 // r is final in priv_r: res + s_priv * 0.
                 zr[m][j].zero();
                 ld(rr[m][j], priv_r + off);
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(512) void k_psync_norm_1p(
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = (r[e] - mean[m]) * inv[m] * gm[e] + bt[e];
             st(out + off, o);
-            if (out_resid != nullptr && (priv_r == nullptr || ch0[j] < n_s)) st(out_resid + off, r);
+            if (out_resid != nullptr && (priv_r == nullptr || ch0[j] < ns8)) st(out_resid + off, r);
         }
     }
 }
@@ -482,9 +483,9 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     auto OR = reinterpret_cast<TIO *>(a.out_resid);
     auto Sp = reinterpret_cast<const TIO *>(a.S);
     auto PR = reinterpret_cast<const TIO *>(a.priv_r);
-    // Final private rows come only with S, on channel chunks that are all shared or all
-    // private (n_s % 8 == 0), and only to the single-pass kernel.
-    if (PR != nullptr && (Sp == nullptr || a.n_s % 8 != 0)) return hipErrorInvalidValue;
+    // Final private rows go only to the single-pass kernel (checked below), on the chunks
+    // from n_s rounded up to 8 (with S, n_s % 8 == 0).
+    if (PR != nullptr && Sp != nullptr && a.n_s % 8 != 0) return hipErrorInvalidValue;
     if (a.T <= 64 && a.P > 1 && PR == nullptr) {
         int nchr = 1;
         while (nchr < 4 && nchunk > nchr * 512) nchr *= 2;

@@ -323,18 +323,28 @@ def test_forward_path_query():
 
 
 def test_private_in_epilogue_query():
-    """caat_forward_private_in_epilogue: on the fused path, in bf16, where K3's single-pass
-    kernel handles the rows (P = 8: up to 4096 channels), and with private channels left."""
+    """caat_forward_private_in_epilogue: in bf16 for T > 64, on the fused path or on the
+    per-rank path from P T h = 2^25 on, where K3's single-pass kernel handles the rows
+    (P = 8: up to 4096 channels), and with whole private chunks of 8 channels left (from
+    n_s on when fused, else from n_s rounded up to 8)."""
     L = caat.lib()
     mlp = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.BF16)
     full = caat.caat_create(4096, 11008, 8, 1.0, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+    odd = caat.caat_create(4096, 11008, 8, 0.37, caat.RMSNORM, caat.SWIGLU, caat.BF16)
+    last = caat.caat_create(4096, 11008, 8, 4095 / 4096, caat.RMSNORM, caat.SWIGLU, caat.BF16)
     wide = caat.caat_create(16384, 0, 8, 0.0, caat.RMSNORM, caat.NONE, caat.BF16)
     wide2 = caat.caat_create(16384, 0, 2, 0.0, caat.RMSNORM, caat.NONE, caat.BF16)
     f32 = caat.caat_create(4096, 11008, 8, 0.5, caat.RMSNORM, caat.SWIGLU, caat.F32)
     try:
-        assert caat.caat_forward_private_in_epilogue(mlp, 8192) is True
-        assert caat.caat_forward_private_in_epilogue(mlp, 64) is False    # not fused
-        assert caat.caat_forward_private_in_epilogue(mlp, 1920) is False  # too few shared tiles
+        assert caat.caat_forward_private_in_epilogue(mlp, 8192) is True   # fused
+        assert caat.caat_forward_private_in_epilogue(mlp, 1920) is True   # per-rank GEMM
+        assert caat.caat_forward_fused(mlp, 1920) is False
+        assert caat.caat_forward_private_in_epilogue(mlp, 1023) is False  # P T h < 2^25
+        assert caat.caat_forward_private_in_epilogue(mlp, 1024) is True
+        assert caat.caat_forward_private_in_epilogue(mlp, 64) is False    # decode shapes
+        assert caat.caat_forward_private_in_epilogue(odd, 8192) is True   # from 1520 on
+        assert caat.caat_shared_channels(last) == 4095
+        assert caat.caat_forward_private_in_epilogue(last, 8192) is False # no whole chunk
         assert caat.caat_forward_private_in_epilogue(full, 8192) is False # no private channels
         assert caat.caat_forward_private_in_epilogue(wide, 100) is False  # multi-pass K3
         assert caat.caat_forward_fused(wide, 100) is True
@@ -343,7 +353,7 @@ def test_private_in_epilogue_query():
         assert L.caat_forward_private_in_epilogue(None, 8) == caat.EINVAL
         assert L.caat_forward_private_in_epilogue(mlp, 0) == caat.EINVAL
     finally:
-        for hd in (mlp, full, wide, wide2, f32):
+        for hd in (mlp, full, odd, last, wide, wide2, f32):
             caat.caat_destroy(hd)
 
 

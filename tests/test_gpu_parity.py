@@ -366,8 +366,9 @@ def _forward_mask_cases():
     for T in (2000, 2048):
         for n_s in (0, 1920, 2040, 2048, 2056, h - 8, h, 2047):
             cases.append(("bf16", 8, h, T, n_s))
-    # The nontemporal K3 forms (more than 256 MB per launch).
-    cases += [("bf16", 8, h, 1100, 2048), ("bf16", 8, h, 1100, 2047)]
+    # The nontemporal K3 forms (more than 256 MB per launch); the per-rank row GEMM writing
+    # the whole private chunks into out_resid (P T h >= 2^25), with a chunk across n_s.
+    cases += [("bf16", 8, h, 1100, n_s) for n_s in (2048, 2047, 1, 65, 4089)]
     # Rows too wide for one register pass: the multi-pass K3.  Off the GPU for now: with
     # the private rows taken from the private GEMM's epilogue, the first of these cases
     # (n_s = 0) hit a memory access fault in the multi-pass K3 whose cause was not found.
@@ -519,14 +520,19 @@ def test_row_gemm_reduce_matches_oracle(wname, T, p):
 
 @pytest.mark.parametrize("wname,T,p", [("1.1b-mlp-bf16", 4096, 0.5), ("1.1b-mlp-bf16", 200, 0.0),
                                        ("130m-pair-bf16", 333, 0.0), ("7b-prefill-pair-bf16", 2048, 0.5),
-                                       ("7b-prefill-pair-bf16", 384, 0.0)])
+                                       ("7b-prefill-pair-bf16", 384, 0.0),
+                                       # the per-rank row GEMM (too few shared-GEMM tiles, or
+                                       # n_s % 8 != 0: the chunk across n_s keeps its partials)
+                                       ("1.1b-mlp-bf16", 2100, 0.5), ("1.1b-mlp-bf16", 2048, 0.37),
+                                       ("7b-prefill-pair-bf16", 1100, 0.61)])
 def test_forward_private_rows_from_gemm_epilogue(wname, T, p):
-    """On the fused path with a residual output, the private GEMM adds the residual in its
-    epilogue (out_resid = resid + s_priv * Zt on [n_s, h)) and K3 reads those rows.
-    out_resid must equal, bit for bit, what K3 computes from the stored private partials
-    (caat_row_gemm_reduce, then caat_sync_norm); out (whose private row statistics are
-    now taken from the stored bf16 rows) within one bf16 rounding of it.  In place
-    (out_resid = resid) gives the same bits."""
+    """With a residual output, the row GEMM adds the residual in its epilogue (out_resid =
+    resid + s_priv * Zt on the private channel chunks) and K3 reads those rows.  out_resid
+    must equal, bit for bit, what K3 computes from stored partials (fused path:
+    caat_row_gemm_reduce, then caat_sync_norm; per-rank path: caat_row_gemm, then
+    caat_partial_sync_norm); out (whose private row statistics are now taken from the stored
+    bf16 rows) within one bf16 rounding of it.  In place (out_resid = resid) gives the same
+    bits."""
     w = W.ALL[wname]
     _say(f"[case] private rows from the epilogue {wname} T={T} p={p}")
     inputs = runner.make_inputs(w, T=T, norm_params="random")
@@ -535,26 +541,30 @@ def test_forward_private_rows_from_gemm_epilogue(wname, T, p):
     attn = "ctx" in d
     s = caat.Sublayer(w.h, w.ffn, w.P, p, norm=w.norm, act="none" if attn else w.act,
                       dtype=w.dtype, s_priv=1.75)
-    assert caat.caat_forward_fused(s.handle, T), "the case must take the fused path"
-    assert caat.caat_forward_private_in_epilogue(s.handle, T), "and the epilogue's private rows"
+    fused = caat.caat_forward_fused(s.handle, T)
+    assert caat.caat_forward_private_in_epilogue(s.handle, T), "the case must take that path"
     inp, W1, W2, resid = (d["ctx"], None, d["Wo"], d["x0"]) if attn else (d["x"], d["W1"], d["W2"], d["x"])
     P, h, n_s = w.P, w.h, s.n_s
     out = torch.empty((P, T, h), dtype=dt, device="cuda")
     out_resid = torch.empty_like(out)
     s.forward(inp, W1, W2, d["gamma"], out, resid=resid, beta=d["beta"], out_resid=out_resid)
-    # The same sublayer through the per-step calls, private partials stored.
+    # The same sublayer through the per-step calls, partials stored.
     if attn:
         gin = inp
     else:
         gin = torch.empty((P, T, s.f_s), dtype=dt, device="cuda")
         caat.caat_column_gemm_act(s.handle, T, inp, W1, gin)
-    S = torch.empty((T, max(n_s, 8)), dtype=dt, device="cuda")
     Z = torch.empty((P, T, h), dtype=dt, device="cuda")
-    caat.caat_row_gemm_reduce(s.handle, T, gin, W2, S if n_s else None, Z)
     out2 = torch.empty_like(out)
     out_resid2 = torch.empty_like(out)
-    caat.caat_sync_norm(s.handle, T, S if n_s else None, Z, resid, d["gamma"], d["beta"], out2,
-                        out_resid2)
+    if fused:
+        S = torch.empty((T, max(n_s, 8)), dtype=dt, device="cuda")
+        caat.caat_row_gemm_reduce(s.handle, T, gin, W2, S if n_s else None, Z)
+        caat.caat_sync_norm(s.handle, T, S if n_s else None, Z, resid, d["gamma"], d["beta"],
+                            out2, out_resid2)
+    else:
+        caat.caat_row_gemm(s.handle, T, gin, W2, Z)
+        caat.caat_partial_sync_norm(s.handle, T, Z, resid, d["gamma"], d["beta"], out2, out_resid2)
     # In place: the residual output overwrites the residual.
     r3 = resid.clone()
     out3 = torch.empty_like(out)
