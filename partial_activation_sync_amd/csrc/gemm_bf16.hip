@@ -30,6 +30,9 @@
 //     resident slot, so a tile's prologue latency and the workgroup launch gap hide
 //     under the previous tile's epilogue (the wait for those first loads still covers
 //     the previous tile's stores: vector loads and stores share one counter).
+// The residual epilogues of the row GEMMs (EPI_RESID, EPI_RESID_SPLIT) read the rank's
+// residual chunk where each thread stores and write R + s_priv * bf16(acc) (Eq. 9's
+// r = R + Z on private channels) into the residual output instead of a partial.
 // Workgroups are mapped to tiles so that each XCD (own L2) works on one contiguous
 // range of tiles, which share operand rows.
 //

@@ -18,7 +18,10 @@
 // Fused mode: when the row-parallel GEMM has already summed the shared channels over
 // the ranks in its accumulators (the K-concatenated product of all ranks, §3.2's local
 // summation done in one GEMM), S [T][s_ld] holds them and only the private columns of
-// the partials are read.
+// the partials are read.  Final private rows (priv_r, single-pass kernel only): when the
+// row GEMM's epilogue has already written r = R + s_priv * Zt for the private channel
+// chunks (from n_s rounded up to 8) into out_resid, those rows are read in place of the
+// partials and the residual, and not written again.
 #include "caat_internal.h"
 #include "rowops.h"
 
