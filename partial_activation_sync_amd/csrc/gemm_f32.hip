@@ -3,29 +3,39 @@
 //
 // "Tensor-Parallelism with Partially Synchronized Activations", App. A.2, Eq. 22 / 24.
 //
-// The fp32 shapes are small (the P = 2, h = 256 sublayer: 16 to 32 output tiles of
+// The fp32 shapes are small (the P = 2, h = 256 sublayer: a few dozen output tiles of
 // 64 x 64), so a launch has few workgroups and each walks a long contraction; a
-// workgroup that steps through K alone is bound by the latency of each step's loads.
-// Here the 4 waves of a workgroup split the contraction (over every K segment in turn)
-// into 4 contiguous ranges and each computes the whole 64 x 64 tile over its range:
-//   * per step of 16, a wave copies its X [16][64] and W [16][64] slabs (and the up rows
-//     for SwiGLU) into its own LDS region and reads them back for 8 x 8 outputs per lane;
-//     the next step's global loads are issued before the current step is computed;
-//   * the four partial tiles are then summed through LDS in wave order (fixed, so the
-//     results do not depend on timing), and the epilogue runs on the sum.
+// workgroup that steps through K alone is bound by the latency of each step's loads, and
+// one lane that owns 8 x 8 outputs issues 64 FMAs per K value.  So:
+//   * the NWV waves of a workgroup split the contraction (over every K segment in turn)
+//     into NWV contiguous ranges and each computes the whole TB x TB tile over its range:
+//     per step of 16, a wave copies its X [16][TB] and W [16][TB] slabs (and the up rows
+//     for SwiGLU) into its own LDS region and reads them back for its lane's outputs; the
+//     next step's global loads are issued before the current step is computed;
+//   * the NWV partial tiles are then summed through LDS in wave order (fixed, so the
+//     results do not depend on timing), and the epilogue runs on the sum;
+//   * a launch with fewer 64 x 64 tiles than compute units takes 32 x 32 or 16 x 16 tiles
+//     with 8 waves instead (4 x 4 or 2 x 2 outputs per lane, twice the K split): the tiny
+//     sublayer's two GEMMs, 32 and 16 workgroups of 64 x 64, become 512 and 256.
 // Ragged edges read as zero and are masked on store.
 #include "caat_internal.h"
+#include "bufload.h"
 
 namespace caat {
 namespace {
 
-constexpr int TB = 64, NB = 64, BKF = 16, NWV = 4;
+constexpr int BKF = 16;
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a)
+template <int EPI, int TB, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_gemm_f32(GemmArgs a)
 {
+    constexpr int NB = TB;                               // square tiles
     constexpr bool GLU = EPI == EPI_SWIGLU;
     constexpr int NS = GLU ? 3 : 2;                      // slabs per step: X, W (, U)
+    constexpr int LPS = TB / 16;                         // 16-byte loads per lane and slab
+    constexpr int OI = TB / 8, OJ = NB / 8;              // outputs per lane: OI tokens x OJ columns
+    constexpr int OQ = (TB * NB + 64 * NWV - 1) / (64 * NWV);   // summed outputs per thread
+    static_assert(TB == 16 || TB == 32 || TB == 64, "tile");
     __shared__ float slab[NWV][NS][BKF][TB + 1];
     __shared__ float red[NWV][TB * NB];
 
@@ -42,81 +52,102 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a)
     const int S = (G + NWV - 1) / NWV;
     const int g0 = wave * S;
 
-    // Loads of one step: 64 rows x 16 k per slab, lane l reads row l (16 consecutive k as
-    // four 16-byte loads: K, the segment strides and up_off K are multiples of 8).
-    float4 ld[NS][BKF / 4];
-    auto issue = [&](int g) {
+    // Loads of one step: TB rows x 16 k per slab; lane l reads row l % TB, LPS consecutive
+    // 4-k groups from group (l / TB) LPS on (16-byte loads: K, the segment strides and
+    // up_off K are multiples of 8).  The loads of step s go to register set s % D, and
+    // those of step s + D are issued as soon as step s has been copied to LDS, so D steps
+    // are in flight while one is computed (D = 4 for the small tiles, whose short steps
+    // and few steps per wave cannot cover a load's latency one step ahead).
+    constexpr int D = TB <= 32 ? 4 : 1;
+    const int lrow = lane % TB, lkq = (lane / TB) * LPS;
+    float4 ld[D][NS][LPS];
+    // Buffer loads: a row past the matrix or a k past K gets an offset beyond the
+    // descriptor's range and reads as zero, with no branch around the load.
+    const int wrows = GLU ? a.up_off + N : N;
+    const __amdgpu_buffer_rsrc_t rX =
+        make_rsrc(Xm, (uint32_t)(((size_t)(a.kseg - 1) * a.x_kseg + (size_t)T * K) * 4u));
+    const __amdgpu_buffer_rsrc_t rW =
+        make_rsrc(Wm, (uint32_t)(((size_t)(a.kseg - 1) * a.w_kseg + (size_t)wrows * K) * 4u));
+    const int t_l = t0 + lrow, n_l = n0 + lrow;
+    auto ld4 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    };
+    auto issue = [&](int g, float4 (&dst)[NS][LPS]) {
         const bool ok = g < G && g - g0 < S;
         const int seg = ok ? g / nk : 0;
         const int k0 = ok ? (g - seg * nk) * BKF : 0;
-        const float *Xg = Xm + (size_t)seg * a.x_kseg;
-        const float *Wg = Wm + (size_t)seg * a.w_kseg;
-        const int t = t0 + lane, n = n0 + lane;
-        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        const size_t xs0 = (size_t)seg * a.x_kseg, ws0 = (size_t)seg * a.w_kseg;
 #pragma unroll
-        for (int v = 0; v < BKF / 4; ++v) {
-            const int k = k0 + 4 * v;
+        for (int v = 0; v < LPS; ++v) {
+            const int k = k0 + 4 * (lkq + v);
             const bool kin = ok && k < K;
-            ld[0][v] = (kin && t < T) ? *reinterpret_cast<const float4 *>(Xg + (size_t)t * K + k) : z;
-            ld[1][v] = (kin && n < N) ? *reinterpret_cast<const float4 *>(Wg + (size_t)n * K + k) : z;
+            dst[0][v] = ld4(rX, (kin && t_l < T) ? (uint32_t)((xs0 + (size_t)t_l * K + k) * 4u) : OOB);
+            dst[1][v] = ld4(rW, (kin && n_l < N) ? (uint32_t)((ws0 + (size_t)n_l * K + k) * 4u) : OOB);
             if (GLU)
-                ld[NS - 1][v] = (kin && n < N)
-                    ? *reinterpret_cast<const float4 *>(Wg + (size_t)(a.up_off + n) * K + k) : z;
+                dst[NS - 1][v] =
+                    ld4(rW, (kin && n_l < N) ? (uint32_t)((ws0 + (size_t)(a.up_off + n_l) * K + k) * 4u) : OOB);
         }
     };
 
-    const int ty = lane >> 3, tx = lane & 7;          // tokens ty*8 + i, columns tx + 8 j
-    float acc[8][8] = {}, accu[8][8] = {};   // accu: SwiGLU up rows only
-    issue(g0);
-    for (int s = 0; s < S; ++s) {
+    const int ty = lane >> 3, tx = lane & 7;          // tokens ty OI + i, columns tx + 8 j
+    float acc[OI][OJ] = {}, accu[OI][OJ] = {};   // accu: SwiGLU up rows only
 #pragma unroll
-        for (int q = 0; q < NS; ++q)
+    for (int u = 0; u < D; ++u) issue(g0 + u, ld[u]);
+    for (int sb = 0; sb < S; sb += D) {
 #pragma unroll
-            for (int v = 0; v < BKF / 4; ++v) {
-                slab[wave][q][4 * v + 0][lane] = ld[q][v].x;
-                slab[wave][q][4 * v + 1][lane] = ld[q][v].y;
-                slab[wave][q][4 * v + 2][lane] = ld[q][v].z;
-                slab[wave][q][4 * v + 3][lane] = ld[q][v].w;
-            }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        issue(g0 + s + 1);                            // the next step flies while this one runs
+        for (int u = 0; u < D; ++u) {
+            if (sb + u >= S) break;
 #pragma unroll
-        for (int kk = 0; kk < BKF; ++kk) {
-            float xv[8], wv[8], uv[8];
+            for (int q = 0; q < NS; ++q)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = slab[wave][0][kk][ty * 8 + i];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                wv[j] = slab[wave][1][kk][tx + 8 * j];
-                if (GLU) uv[j] = slab[wave][NS - 1][kk][tx + 8 * j];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
-                    if (GLU) accu[i][j] = fmaf(xv[i], uv[j], accu[i][j]);
+                for (int v = 0; v < LPS; ++v) {
+                    const int kb = 4 * (lkq + v);
+                    slab[wave][q][kb + 0][lrow] = ld[u][q][v].x;
+                    slab[wave][q][kb + 1][lrow] = ld[u][q][v].y;
+                    slab[wave][q][kb + 2][lrow] = ld[u][q][v].z;
+                    slab[wave][q][kb + 3][lrow] = ld[u][q][v].w;
                 }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            issue(g0 + sb + u + D, ld[u]);                // flies while D steps are computed
+#pragma unroll
+            for (int kk = 0; kk < BKF; ++kk) {
+                float xv[OI], wv[OJ], uv[OJ];
+#pragma unroll
+                for (int i = 0; i < OI; ++i) xv[i] = slab[wave][0][kk][ty * OI + i];
+#pragma unroll
+                for (int j = 0; j < OJ; ++j) {
+                    wv[j] = slab[wave][1][kk][tx + 8 * j];
+                    if (GLU) uv[j] = slab[wave][NS - 1][kk][tx + 8 * j];
+                }
+#pragma unroll
+                for (int i = 0; i < OI; ++i)
+#pragma unroll
+                    for (int j = 0; j < OJ; ++j) {
+                        acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+                        if (GLU) accu[i][j] = fmaf(xv[i], uv[j], accu[i][j]);
+                    }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // Sum of the four partial tiles in wave order; thread t then owns outputs
-    // t + 256 q (row (t + 256 q) / 64, column (t + 256 q) % 64).
-    float sum[16], sumu[16];
-    auto reduce = [&](float (&part)[8][8], float *out) {
+    // Sum of the NWV partial tiles in wave order; thread t then owns outputs
+    // t + 64 NWV q (row (t + 64 NWV q) / NB, column (t + 64 NWV q) % NB).
+    float sum[OQ], sumu[OQ];
+    auto reduce = [&](float (&part)[OI][OJ], float *out) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < OI; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) red[wave][(ty * 8 + i) * NB + tx + 8 * j] = part[i][j];
+            for (int j = 0; j < OJ; ++j) red[wave][(ty * OI + i) * NB + tx + 8 * j] = part[i][j];
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int o = threadIdx.x + 256 * q;
+        for (int q = 0; q < OQ; ++q) {
+            const int o = threadIdx.x + 64 * NWV * q;
+            if (o >= TB * NB) break;
             float v = red[0][o];
 #pragma unroll
             for (int w = 1; w < NWV; ++w) v += red[w][o];
@@ -129,8 +160,9 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a)
 
     float *O = reinterpret_cast<float *>(a.out) + (size_t)m * a.o_stride;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int o = threadIdx.x + 256 * q;
+    for (int q = 0; q < OQ; ++q) {
+        const int o = threadIdx.x + 64 * NWV * q;
+        if (o >= TB * NB) break;
         const int t = t0 + o / NB, n = n0 + o % NB;
         if (t >= T || n >= N) continue;
         float v = sum[q];
@@ -142,17 +174,31 @@ __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs a)
     }
 }
 
-}  // namespace
-
-hipError_t gemm_f32(const GemmArgs &a, hipStream_t s) {
-    const dim3 grid((a.N + NB - 1) / NB, (a.T + TB - 1) / TB, a.P), block(256);
+template <int TB, int NWV>
+hipError_t launch_f32(const GemmArgs &a, hipStream_t s) {
+    const dim3 grid((a.N + TB - 1) / TB, (a.T + TB - 1) / TB, a.P), block(64 * NWV);
     switch (a.epi) {
-    case EPI_GELU: hipLaunchKernelGGL(k_gemm_f32<EPI_GELU>, grid, block, 0, s, a); break;
-    case EPI_GELU_TANH: hipLaunchKernelGGL(k_gemm_f32<EPI_GELU_TANH>, grid, block, 0, s, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(k_gemm_f32<EPI_SWIGLU>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(k_gemm_f32<EPI_STORE>, grid, block, 0, s, a); break;
+    case EPI_GELU: hipLaunchKernelGGL((k_gemm_f32<EPI_GELU, TB, NWV>), grid, block, 0, s, a); break;
+    case EPI_GELU_TANH:
+        hipLaunchKernelGGL((k_gemm_f32<EPI_GELU_TANH, TB, NWV>), grid, block, 0, s, a);
+        break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((k_gemm_f32<EPI_SWIGLU, TB, NWV>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_f32<EPI_STORE, TB, NWV>), grid, block, 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+// The largest tile that still gives every compute unit a workgroup (the smallest when
+// none does): a lane's FMAs per K value fall with the tile (64, 16, 4), and the chip's
+// FMA rate needs all CUs.
+hipError_t gemm_f32(const GemmArgs &a, hipStream_t s) {
+    auto tiles = [&](int tb) { return (long)a.P * ((a.N + tb - 1) / tb) * ((a.T + tb - 1) / tb); };
+    const long cus = 256;   // compute units of an MI355X
+    if (tiles(64) >= cus) return launch_f32<64, 4>(a, s);
+    if (tiles(32) >= cus) return launch_f32<32, 8>(a, s);
+    return launch_f32<16, 8>(a, s);
 }
 
 }  // namespace caat
