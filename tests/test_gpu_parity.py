@@ -164,6 +164,23 @@ def test_out_projection_edge_shapes(dtype):
     _run_and_compare(w, norm_params="random")
 
 
+@pytest.mark.parametrize("P,h,ffn,T,act", [(2, 200, 2 * 136, 45, "gelu"),
+                                            (4, 264, 4 * 264, 300, "swiglu"),
+                                            (8, 520, 8 * 520, 300, "gelu_tanh")])
+def test_f32_gemm_tile_sizes(P, h, ffn, T, act):
+    """The fp32 GEMM's three tile shapes through the whole sublayer: 16 x 16 (fewer than 256
+    tiles of 32 x 32), 32 x 32 and 64 x 64 (at least 256 tiles of that size), each with a
+    ragged token tile and a contraction that is not a multiple of the 16-wide K step."""
+    f_s = ffn // P
+    tiles = lambda tb, n: P * -(-n // tb) * -(-T // tb)
+    want = {0: 16, 1: 32, 2: 64}[[(2, 200), (4, 264), (8, 520)].index((P, h))]
+    got = [64 if tiles(64, n) >= 256 else 32 if tiles(32, n) >= 256 else 16 for n in (f_s, h)]
+    assert got == [want, want], got
+    w = W.with_(W.TINY_MLP_F32, P=P, h=h, ffn=ffn, T=T, p=0.41, act=act, norm="rmsnorm",
+                replicated_x=False)
+    _run_and_compare(w, norm_params="random", s_priv=math.sqrt(P))
+
+
 def _random_cases(n=32, seed=20251203):
     """Seeded random sublayer configurations (drawn once, so the test ids are stable): MLP
     or out-projection + MLP pair, fp32 or bf16, every activation and norm, P 1..8, widths
