@@ -17,9 +17,9 @@
 //   * a launch with fewer 64 x 64 tiles than compute units takes 32 x 32 or 16 x 16 tiles
 //     with 8 waves instead (4 x 4 or 2 x 2 outputs per lane, twice the K split): the tiny
 //     sublayer's two GEMMs, 32 and 16 workgroups of 64 x 64, become 512 and 256.
-// Ragged edges read as zero and are masked on store.
+// Ragged edges read as zero (loads of past-the-edge elements are redirected and their
+// values zeroed) and are masked on store.
 #include "caat_internal.h"
-#include "bufload.h"
 
 namespace caat {
 namespace {
@@ -61,31 +61,29 @@ __global__ __launch_bounds__(64 * NWV) void k_gemm_f32(GemmArgs a)
     constexpr int D = TB <= 32 ? 4 : 1;
     const int lrow = lane % TB, lkq = (lane / TB) * LPS;
     float4 ld[D][NS][LPS];
-    // Buffer loads: a row past the matrix or a k past K gets an offset beyond the
-    // descriptor's range and reads as zero, with no branch around the load.
-    const int wrows = GLU ? a.up_off + N : N;
-    const __amdgpu_buffer_rsrc_t rX =
-        make_rsrc(Xm, (uint32_t)(((size_t)(a.kseg - 1) * a.x_kseg + (size_t)T * K) * 4u));
-    const __amdgpu_buffer_rsrc_t rW =
-        make_rsrc(Wm, (uint32_t)(((size_t)(a.kseg - 1) * a.w_kseg + (size_t)wrows * K) * 4u));
+    // A row past the matrix or a k past K loads from the operand's first element instead
+    // and the value is replaced by zero, so every load is issued unconditionally (no branch
+    // around it: the waits can then count the loads in flight) on 64-bit addresses.
     const int t_l = t0 + lrow, n_l = n0 + lrow;
-    auto ld4 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    auto ld4 = [](const float *base, size_t idx, bool ok) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(base + (ok ? idx : 0));
+        const uint32_t keep = ok ? 0xffffffffu : 0u;
+        return make_float4(__uint_as_float(u.x & keep), __uint_as_float(u.y & keep),
+                           __uint_as_float(u.z & keep), __uint_as_float(u.w & keep));
     };
     auto issue = [&](int g, float4 (&dst)[NS][LPS]) {
         const bool ok = g < G && g - g0 < S;
         const int seg = ok ? g / nk : 0;
         const int k0 = ok ? (g - seg * nk) * BKF : 0;
-        const size_t xs0 = (size_t)seg * a.x_kseg, ws0 = (size_t)seg * a.w_kseg;
+        const float *Xg = Xm + (size_t)seg * a.x_kseg;
+        const float *Wg = Wm + (size_t)seg * a.w_kseg;
 #pragma unroll
         for (int v = 0; v < LPS; ++v) {
             const int k = k0 + 4 * (lkq + v);
             const bool kin = ok && k < K;
-            dst[0][v] = ld4(rX, (kin && t_l < T) ? (uint32_t)((xs0 + (size_t)t_l * K + k) * 4u) : OOB);
-            dst[1][v] = ld4(rW, (kin && n_l < N) ? (uint32_t)((ws0 + (size_t)n_l * K + k) * 4u) : OOB);
-            if (GLU)
-                dst[NS - 1][v] =
-                    ld4(rW, (kin && n_l < N) ? (uint32_t)((ws0 + (size_t)(a.up_off + n_l) * K + k) * 4u) : OOB);
+            dst[0][v] = ld4(Xg, (size_t)t_l * K + k, kin && t_l < T);
+            dst[1][v] = ld4(Wg, (size_t)n_l * K + k, kin && n_l < N);
+            if (GLU) dst[NS - 1][v] = ld4(Wg, (size_t)(a.up_off + n_l) * K + k, kin && n_l < N);
         }
     };
 
