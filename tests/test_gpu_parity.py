@@ -149,7 +149,8 @@ def test_activation_and_norm_variants(act, norm):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("P,h,ffn,T", [(1, 8, 8, 1), (16, 128, 16 * 8, 5), (3, 264, 3 * 40, 67),
+@pytest.mark.parametrize("P,h,ffn,T", [(1, 8, 8, 1), (16, 128, 16 * 8, 5), (16, 256, 16 * 16, 100),
+                                       (3, 264, 3 * 40, 67),
                                        (5, 200, 5 * 48, 129)])
 def test_edge_shapes(dtype, P, h, ffn, T):
     for act in ("gelu", "swiglu"):
@@ -285,6 +286,9 @@ MASK_KERNEL_CASES = [(dt, P, h, T) for dt in ("bf16", "f32") for P in (1, 2, 4, 
 # P = 16 at h = 8192, at T > 64 (and the per-rank kernel at T <= 64).
 MASK_KERNEL_CASES += [("f32", 16, 4096, 100), ("bf16", 16, 8192, 100), ("bf16", 16, 8192, 3),
                       ("f32", 16, 4096, 3)]
+# bf16 with 9-16 ranks and rows that fit one register pass: the single-pass K3 with its
+# 16-rank register layout (cached and nontemporal forms).
+MASK_KERNEL_CASES += [("bf16", 16, 4096, 100), ("bf16", 12, 2048, 100), ("bf16", 16, 4096, 1100)]
 
 
 @pytest.mark.parametrize("dtype,P,h,T", MASK_KERNEL_CASES)
@@ -397,6 +401,9 @@ def _forward_mask_cases():
     # fp32 with 16 ranks (the multi-pass K3; codes up to 2^15).
     for n_s in (0, 8, 2048, 2047, 4095, 4096):
         cases.append(("f32", 16, h, 100, n_s))
+    # bf16 with 16 ranks (the single-pass K3 for up to 16 ranks; codes m + 1).
+    for n_s in (0, 8, 2048, 2047, 4095, 4096):
+        cases.append(("bf16", 16, h, 100, n_s))
     return cases
 
 
