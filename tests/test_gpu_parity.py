@@ -289,6 +289,12 @@ MASK_KERNEL_CASES += [("f32", 16, 4096, 100), ("bf16", 16, 8192, 100), ("bf16", 
 # bf16 with 9-16 ranks and rows that fit one register pass: the single-pass K3 with its
 # 16-rank register layout (cached and nontemporal forms).
 MASK_KERNEL_CASES += [("bf16", 16, 4096, 100), ("bf16", 12, 2048, 100), ("bf16", 16, 4096, 1100)]
+# Rows wider than 4096 in one register pass: two or four chunks per thread in the
+# single-pass K3 (bf16 P = 8 / 2 / 1, fp32 P = 4 / 2 / 1); the multi-pass K3 with one chunk
+# per thread (fp32 rows of 1024 or fewer with more than 8 ranks).
+MASK_KERNEL_CASES += [("bf16", 8, 8192, 100), ("bf16", 2, 16384, 100), ("bf16", 1, 16384, 100),
+                      ("f32", 4, 8192, 100), ("f32", 2, 16384, 100), ("f32", 1, 16384, 100),
+                      ("f32", 16, 1024, 100), ("f32", 9, 256, 100)]
 
 
 @pytest.mark.parametrize("dtype,P,h,T", MASK_KERNEL_CASES)
@@ -616,6 +622,17 @@ def test_partial_sync_norm_streaming(dtype):
     """K3 for T > 64 (one workgroup per token) on partials of every rank, at a size whose
     launch moves more than 256 MB (nontemporal row loads and stores), ragged T."""
     _partial_sync_norm_case(dtype, 8, 4096, 1100)
+
+
+@pytest.mark.parametrize("dtype,P,h,T", [("bf16", 8, 8192, 100), ("bf16", 2, 16384, 70),
+                                         ("bf16", 16, 4096, 100), ("bf16", 16, 8192, 66),
+                                         ("f32", 4, 8192, 100), ("f32", 1, 16384, 65),
+                                         ("f32", 16, 1024, 100), ("f32", 9, 4096, 65)])
+def test_partial_sync_norm_wide_rows_and_many_ranks(dtype, P, h, T):
+    """K3 for T > 64 on the register layouts the 7B shapes do not reach: the single-pass
+    kernel with two or four chunks per thread and with 16 ranks, and the multi-pass kernel
+    (with one, four and two chunks per thread)."""
+    _partial_sync_norm_case(dtype, P, h, T)
 
 
 def _partial_sync_norm_case(dtype, P, h, T):
