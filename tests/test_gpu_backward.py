@@ -120,6 +120,21 @@ def test_backward_single_rank_and_small_batch():
     _run(8, 3, 256, 8 * 64, "swiglu", "layernorm", 0.25, "bf16")
 
 
+@pytest.mark.parametrize("h,norm,dtype", [(8192, "layernorm", "bf16"), (8192, "rmsnorm", "f32"),
+                                          (16384, "rmsnorm", "bf16"), (16384, "layernorm", "f32")])
+def test_backward_wide_rows(h, norm, dtype):
+    """Rows of 8192 and 16384 channels: the norm derivative with two and four chunks per
+    thread (fewer ranks per register group)."""
+    _run(2, 20, h, 2 * 64, "gelu", norm, 0.5, dtype)
+
+
+def test_backward_fp32_swiglu_residual_is_input():
+    """fp32 SwiGLU backward (its activation derivative) with resid = x, so the residual
+    gradient is added into din."""
+    _run(2, 40, 256, 2 * 96, "swiglu", "rmsnorm", 0.4, "f32", resid_given=False,
+         dres_given=False)
+
+
 def test_backward_7b_dims():
     """The 7B shapes (h = 4096, SwiGLU ffn = 11008, P = 8) at a short batch."""
     _run(8, 72, 4096, 11008, "swiglu", "rmsnorm", 0.5, "bf16")

@@ -182,6 +182,29 @@ def test_f32_gemm_tile_sizes(P, h, ffn, T, act):
     _run_and_compare(w, norm_params="random", s_priv=math.sqrt(P))
 
 
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+def test_gelu_mlp_large_tiles(act):
+    """A GeLU MLP large enough for the 256 x 256 tiles (K1 with the erf or tanh GeLU
+    epilogue; 512 tiles of 256 x 256 over K = 1024), against the oracle on sampled rows."""
+    T = 4096
+    w = W.with_(W.PAIR_130M_BF16, sublayers=("mlp",), P=8, h=1024, ffn=8 * 1024, T=T, p=0.45,
+                act=act, norm="layernorm", replicated_x=False)
+    _run_and_compare(w, norm_params="random", rows=synth.sample_rows(T, 48))
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+@pytest.mark.parametrize("P,ffn,T", [(4, 4 * 512, 1), (4, 4 * 512, 8), (4, 4 * 512, 12),
+                                     (4, 4 * 512, 40), (4, 4 * 512, 64), (8, 8 * 4224, 33)])
+def test_gelu_decode_batches(act, P, ffn, T):
+    """GeLU MLPs at decode batch sizes with h >= 1024: the weight-streaming kernel with the
+    contraction split over four waves (T <= 8) and the 64-token MFMA tiles with the GeLU
+    epilogue past that, in their four-stage (few tiles) and two-stage (more tiles than CUs)
+    forms."""
+    w = W.with_(W.PAIR_130M_BF16, sublayers=("mlp",), P=P, h=1024, ffn=ffn, T=T, p=0.5,
+                act=act, norm="rmsnorm", replicated_x=False)
+    _run_and_compare(w, norm_params="random")
+
+
 def _random_cases(n=32, seed=20251203):
     """Seeded random sublayer configurations (drawn once, so the test ids are stable): MLP
     or out-projection + MLP pair, fp32 or bf16, every activation and norm, P 1..8, widths
@@ -624,6 +647,29 @@ def test_partial_sync_norm_streaming(dtype):
     _partial_sync_norm_case(dtype, 8, 4096, 1100)
 
 
+def _k3_layout_cases():
+    """One (dtype, P, h, T) per register layout the K3 dispatch can reach, for each norm:
+    the single-pass kernel (ranks rounded up to a power of two, times chunks per thread,
+    within 16 for bf16 and 8 for fp32; cached, and nontemporal past 256 MB per launch), the
+    per-rank kernel for T <= 64, and the multi-pass kernel (one to eight chunks per thread)."""
+    one_pass = {"bf16": [(1, 256), (1, 8192), (1, 16384), (2, 4096), (2, 8192), (2, 16384),
+                         (3, 4096), (4, 8192), (4, 16384), (8, 4096), (8, 8192), (16, 4096)],
+                "f32": [(1, 256), (1, 8192), (1, 16384), (2, 4096), (2, 8192), (2, 16384),
+                        (4, 4096), (4, 8192), (8, 4096)]}
+    cases = [(dt, P, h, 65) for dt, l in one_pass.items() for P, h in l]
+    cases += [("bf16", 16, 4096, 600), ("f32", 4, 8192, 600), ("bf16", 1, 16384, 2100)]
+    cases += [(dt, P, h, 5) for dt in ("bf16", "f32")
+              for P, h in ((8, 4096), (8, 8192), (16, 4096), (16, 8192), (4, 16384))]
+    cases += [("bf16", 16, 8192, 66), ("bf16", 8, 16384, 66), ("f32", 16, 1024, 66),
+              ("f32", 16, 4096, 66), ("f32", 16, 8192, 66), ("f32", 8, 16384, 66)]
+    return [(dt, P, h, T, nm) for dt, P, h, T in cases for nm in ("layernorm", "rmsnorm")]
+
+
+@pytest.mark.parametrize("dtype,P,h,T,norm", _k3_layout_cases())
+def test_partial_sync_norm_every_layout(dtype, P, h, T, norm):
+    _partial_sync_norm_case(dtype, P, h, T, norm)
+
+
 @pytest.mark.parametrize("dtype,P,h,T", [("bf16", 8, 8192, 100), ("bf16", 2, 16384, 70),
                                          ("bf16", 16, 4096, 100), ("bf16", 16, 8192, 66),
                                          ("f32", 4, 8192, 100), ("f32", 1, 16384, 65),
@@ -635,23 +681,24 @@ def test_partial_sync_norm_wide_rows_and_many_ranks(dtype, P, h, T):
     _partial_sync_norm_case(dtype, P, h, T)
 
 
-def _partial_sync_norm_case(dtype, P, h, T):
-    """caat_partial_sync_norm with LayerNorm, beta and a private scale, against the
-    oracle's reduce + norm."""
-    _say(f"[case] partial_sync_norm {dtype} P={P} h={h} T={T}")
+def _partial_sync_norm_case(dtype, P, h, T, norm="layernorm"):
+    """caat_partial_sync_norm with the given norm (LayerNorm with beta), a private scale and
+    p = 0.37, against the oracle's reduce + norm."""
+    _say(f"[case] partial_sync_norm {dtype} P={P} h={h} T={T} {norm}")
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    s = caat.Sublayer(h, 8 * P, P, 0.37, norm="layernorm", act="gelu", dtype=dtype, s_priv=1.5)
+    s = caat.Sublayer(h, 8 * P, P, 0.37, norm=norm, act="gelu", dtype=dtype, s_priv=1.5)
     Z = synth.normal((P, T, h), synth.PARTIALS, dtype=dt)
     R = synth.normal((P, T, h), synth.RESID, dtype=dt)
     gamma = synth.normal((h,), synth.GAMMA, std=0.1, mean=1.0, dtype=dt)
-    beta = synth.normal((h,), synth.BETA, std=0.1, dtype=dt)
+    beta = synth.normal((h,), synth.BETA, std=0.1, dtype=dt) if norm == "layernorm" else None
     out = torch.empty((P, T, h), dtype=dt, device="cuda")
     out_resid = torch.empty_like(out)
-    caat.caat_partial_sync_norm(s.handle, T, Z.cuda(), R.cuda(), gamma.cuda(), beta.cuda(),
-                                out, out_resid)
+    caat.caat_partial_sync_norm(s.handle, T, Z.cuda(), R.cuda(), gamma.cuda(),
+                                None if beta is None else beta.cuda(), out, out_resid)
     torch.cuda.synchronize()
-    ref_out, ref_res = oracle.partial_sync_norm(Z, R, gamma, beta=beta, norm=oracle.LAYERNORM,
-                                                n_s=s.n_s, s_priv=1.5)
+    ref_out, ref_res = oracle.partial_sync_norm(
+        Z, R, gamma, beta=beta, norm=oracle.LAYERNORM if norm == "layernorm" else oracle.RMSNORM,
+        n_s=s.n_s, s_priv=1.5)
     from tests.oracle_ref import rel_err
     e1, e2 = rel_err(out, ref_out), rel_err(out_resid, ref_res)
     _say(f"   errors out {e1:.2e} out_resid {e2:.2e}")
