@@ -120,8 +120,9 @@ def test_backward_single_rank_and_small_batch():
     _run(8, 3, 256, 8 * 64, "swiglu", "layernorm", 0.25, "bf16")
 
 
-@pytest.mark.parametrize("h,norm,dtype", [(8192, "layernorm", "bf16"), (8192, "rmsnorm", "f32"),
-                                          (16384, "rmsnorm", "bf16"), (16384, "layernorm", "f32")])
+@pytest.mark.parametrize("h", [8192, 16384])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_backward_wide_rows(h, norm, dtype):
     """Rows of 8192 and 16384 channels: the norm derivative with two and four chunks per
     thread (fewer ranks per register group)."""

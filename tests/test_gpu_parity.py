@@ -193,6 +193,15 @@ def test_gelu_mlp_large_tiles(act):
 
 
 @pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
+@pytest.mark.parametrize("T", [5, 12, 24, 40])
+def test_gelu_decode_short_contraction(act, T):
+    """GeLU MLPs at decode batch sizes with a contraction under 1024 (the 130M widths): the
+    weight-streaming kernel up to 48 tokens, with one, two and three 16-token blocks."""
+    _run_and_compare(W.with_(W.PAIR_130M_BF16, sublayers=("mlp",), T=T, act=act),
+                     norm_params="random")
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
 @pytest.mark.parametrize("P,ffn,T", [(4, 4 * 512, 1), (4, 4 * 512, 8), (4, 4 * 512, 12),
                                      (4, 4 * 512, 40), (4, 4 * 512, 64), (8, 8 * 4224, 33)])
 def test_gelu_decode_batches(act, P, ffn, T):
@@ -652,12 +661,16 @@ def _k3_layout_cases():
     the single-pass kernel (ranks rounded up to a power of two, times chunks per thread,
     within 16 for bf16 and 8 for fp32; cached, and nontemporal past 256 MB per launch), the
     per-rank kernel for T <= 64, and the multi-pass kernel (one to eight chunks per thread)."""
-    one_pass = {"bf16": [(1, 256), (1, 8192), (1, 16384), (2, 4096), (2, 8192), (2, 16384),
-                         (3, 4096), (4, 8192), (4, 16384), (8, 4096), (8, 8192), (16, 4096)],
-                "f32": [(1, 256), (1, 8192), (1, 16384), (2, 4096), (2, 8192), (2, 16384),
-                        (4, 4096), (4, 8192), (8, 4096)]}
+    one_pass = {"bf16": [(1, 256), (1, 4096), (1, 8192), (1, 16384), (2, 4096), (2, 8192),
+                         (2, 16384), (3, 4096), (4, 8192), (4, 16384), (8, 4096), (8, 8192),
+                         (16, 4096)],
+                "f32": [(1, 256), (1, 4096), (1, 8192), (1, 16384), (2, 4096), (2, 8192),
+                        (2, 16384), (4, 4096), (4, 8192), (8, 4096)]}
     cases = [(dt, P, h, 65) for dt, l in one_pass.items() for P, h in l]
-    cases += [("bf16", 16, 4096, 600), ("f32", 4, 8192, 600), ("bf16", 1, 16384, 2100)]
+    # The same layouts with more than 256 MB moved per launch (nontemporal rows).
+    esize = {"bf16": 2, "f32": 4}
+    cases += [(dt, P, h, 2 ** 26 // (P * h * esize[dt]) + 3) for dt, l in one_pass.items()
+              for P, h in l if h >= 4096]
     cases += [(dt, P, h, 5) for dt in ("bf16", "f32")
               for P, h in ((8, 4096), (8, 8192), (16, 4096), (16, 8192), (4, 16384))]
     cases += [("bf16", 16, 8192, 66), ("bf16", 8, 16384, 66), ("f32", 16, 1024, 66),
