@@ -597,9 +597,15 @@ hipError_t launch(const GemmArgs &a, hipStream_t s) {
     case EPI_GELU: return launch_epi<BN, BT, WGN, WGT, EPI_GELU, NST>(a, tilesN, tilesT, s);
     case EPI_GELU_TANH: return launch_epi<BN, BT, WGN, WGT, EPI_GELU_TANH, NST>(a, tilesN, tilesT, s);
     case EPI_SWIGLU: return launch_epi<BN, BT, WGN, WGT, EPI_SWIGLU, NST>(a, tilesN, tilesT, s);
-    case EPI_RESID: return launch_epi<BN, BT, WGN, WGT, EPI_RESID, NST>(a, tilesN, tilesT, s);
+    // The residual epilogues serve prefill batches (T > 64) only, so the 64-token tiles
+    // do not carry them; the per-rank one (EPI_RESID_SPLIT) runs only for P T h >= 2^25,
+    // i.e. on thousands of 128 x 128 tiles, never on the four-stage form (<= 256 tiles).
+    case EPI_RESID:
+        if constexpr (BT == 64) return hipErrorInvalidValue;
+        else return launch_epi<BN, BT, WGN, WGT, EPI_RESID, NST>(a, tilesN, tilesT, s);
     case EPI_RESID_SPLIT:
-        return launch_epi<BN, BT, WGN, WGT, EPI_RESID_SPLIT, NST>(a, tilesN, tilesT, s);
+        if constexpr (BT == 64 || NST == 4) return hipErrorInvalidValue;
+        else return launch_epi<BN, BT, WGN, WGT, EPI_RESID_SPLIT, NST>(a, tilesN, tilesT, s);
     default: return launch_epi<BN, BT, WGN, WGT, EPI_STORE, NST>(a, tilesN, tilesT, s);
     }
 }

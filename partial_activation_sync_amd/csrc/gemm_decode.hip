@@ -201,25 +201,22 @@ __global__ __launch_bounds__(64 * KS) void k_gemm_decode_lds(GemmArgs a, int blo
     }
 }
 
-template <int RB, int JB, int KS>
+template <int EPI, int RB, int JB, int KS>
 hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
     const int blocksN = (a.N + 16 * RB - 1) / (16 * RB);
     const dim3 grid(a.P * blocksN), block(64 * KS);
-    switch (a.epi) {
-    case EPI_GELU:
-        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_GELU, RB, JB, KS>), grid, block, 0, s, a, blocksN);
-        break;
-    case EPI_GELU_TANH:
-        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_GELU_TANH, RB, JB, KS>), grid, block, 0, s, a, blocksN);
-        break;
-    case EPI_SWIGLU:
-        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_SWIGLU, RB, JB, KS>), grid, block, 0, s, a, blocksN);
-        break;
-    default:
-        hipLaunchKernelGGL((k_gemm_decode_lds<EPI_STORE, RB, JB, KS>), grid, block, 0, s, a, blocksN);
-        break;
-    }
+    hipLaunchKernelGGL((k_gemm_decode_lds<EPI, RB, JB, KS>), grid, block, 0, s, a, blocksN);
     return hipGetLastError();
+}
+
+// The epilogues other than SwiGLU share their launch shapes.
+template <int RB, int JB, int KS>
+hipError_t launch_plain(const GemmArgs &a, hipStream_t s) {
+    switch (a.epi) {
+    case EPI_GELU: return launch_lds<EPI_GELU, RB, JB, KS>(a, s);
+    case EPI_GELU_TANH: return launch_lds<EPI_GELU_TANH, RB, JB, KS>(a, s);
+    default: return launch_lds<EPI_STORE, RB, JB, KS>(a, s);
+    }
 }
 
 }  // namespace
@@ -251,26 +248,27 @@ bool gemm_decode_applies(const GemmArgs &a) {
 //   * otherwise each token fragment read from L2 should feed more weight rows: for the
 //     SwiGLU epilogue two blocks per wave (64 weight rows), for the plain and GeLU ones
 //     four (64 rows) once T > 8 (K2 at T = 16 / 32 / 64: 21.7 / 25.8 / 34.8 -> 19.5 /
-//     22.0 / 25.7 us; the out-projection at T = 64: 13.5 -> 10.3 us), two (with K split
-//     over 4 waves when K >= 1024) at T 9 .. 16.
+//     22.0 / 25.7 us; the out-projection at T = 64: 13.5 -> 10.3 us).
 hipError_t gemm_decode_bf16(const GemmArgs &a, hipStream_t s) {
+    // Only batches gemm_decode_applies admits come here (at most 48 tokens, at most 8 for
+    // a plain or GeLU contraction of 1024 or more, 16 for SwiGLU), so at most three token
+    // blocks, and a single one with K split over the waves.
+    if (!gemm_decode_applies(a)) return hipErrorInvalidValue;
     const int jb = (a.T + 15) / 16;
-    const bool glu = a.epi == EPI_SWIGLU;
-    if (glu) {
-        if (a.K >= 1024 && a.T <= 16) return launch_lds<1, 1, 4>(a, s);
+    if (a.epi == EPI_SWIGLU) {
+        if (a.K >= 1024) return launch_lds<EPI_SWIGLU, 1, 1, 4>(a, s);
         switch (jb) {
-        case 1: return launch_lds<2, 1, 1>(a, s);
-        case 2: return launch_lds<2, 2, 1>(a, s);
-        case 3: return launch_lds<2, 3, 1>(a, s);
-        default: return launch_lds<2, 4, 1>(a, s);
+        case 1: return launch_lds<EPI_SWIGLU, 2, 1, 1>(a, s);
+        case 2: return launch_lds<EPI_SWIGLU, 2, 2, 1>(a, s);
+        default: return launch_lds<EPI_SWIGLU, 2, 3, 1>(a, s);
         }
     }
-    if (a.T <= 8) return a.K >= 1024 ? launch_lds<1, 1, 4>(a, s) : launch_lds<2, 1, 1>(a, s);
+    if (a.K >= 1024) return launch_plain<1, 1, 4>(a, s);
+    if (a.T <= 8) return launch_plain<2, 1, 1>(a, s);
     switch (jb) {
-    case 1: return a.K >= 1024 ? launch_lds<2, 1, 4>(a, s) : launch_lds<4, 1, 1>(a, s);
-    case 2: return launch_lds<4, 2, 1>(a, s);
-    case 3: return launch_lds<4, 3, 1>(a, s);
-    default: return launch_lds<4, 4, 1>(a, s);
+    case 1: return launch_plain<4, 1, 1>(a, s);
+    case 2: return launch_plain<4, 2, 1>(a, s);
+    default: return launch_plain<4, 3, 1>(a, s);
     }
 }
 

@@ -501,10 +501,11 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
                        a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
             // All partial loads up front while they fit in registers: P <= 8 with up to two
             // chunks per thread, P <= 16 with one.
+            // (At most 16 ranks reach here: caat_create rejects more.)
             if (a.P <= 8 && nchr == 1) CAAT_K3R(8, 1);
             else if (a.P <= 8 && nchr == 2) CAAT_K3R(8, 2);
             else if (a.P <= 16 && nchr == 1) CAAT_K3R(16, 1);
-            else if (nchr == 1) CAAT_K3R(0, 1);
+            else if (nchr == 1) return hipErrorInvalidValue;
             else if (nchr == 2) CAAT_K3R(0, 2);
             else CAAT_K3R(0, 4);
 #undef CAAT_K3R
@@ -520,23 +521,29 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
         // Bytes the launch reads and writes (partials, residual, two outputs), against the
         // 256 MB Infinity Cache.
         const bool nt = 4.0 * (double)a.P * a.T * a.h * sizeof(TIO) > 256.0 * 1024 * 1024;
+        // Only the shapes one_pass_shape admits are instantiated: ranks x chunks within the
+        // dtype's register budget, and at most four chunks (rows of at most 16384).
+        constexpr int budget = sizeof(TIO) == 2 ? 16 : 8;
 #define CAAT_K3S(PM, N)                                                                        \
-    if (nt)                                                                                    \
-        hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, true>), grid, block, 0, s, a.P, \
-                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld, \
-                           PR);                                                                \
-    else                                                                                       \
-        hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, false>), grid, block, 0, s, a.P, \
-                           a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld, PR)
+    if constexpr ((PM) * (N) <= budget) {                                                      \
+        if (nt)                                                                                \
+            hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, true>), grid, block, 0, s,   \
+                               a.P, a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp,  \
+                               a.s_ld, PR);                                                    \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_psync_norm_1p<PM, N, NORM, TIO, false>), grid, block, 0, s,  \
+                               a.P, a.T, a.h, a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp,  \
+                               a.s_ld, PR);                                                    \
+    } else {                                                                                   \
+        return hipErrorInvalidValue;                                                           \
+    }
         switch (pmax * 16 + nch) {
         case 1 * 16 + 1: CAAT_K3S(1, 1); break;
         case 1 * 16 + 2: CAAT_K3S(1, 2); break;
         case 1 * 16 + 4: CAAT_K3S(1, 4); break;
-        case 1 * 16 + 8: CAAT_K3S(1, 8); break;
         case 2 * 16 + 1: CAAT_K3S(2, 1); break;
         case 2 * 16 + 2: CAAT_K3S(2, 2); break;
         case 2 * 16 + 4: CAAT_K3S(2, 4); break;
-        case 2 * 16 + 8: CAAT_K3S(2, 8); break;
         case 4 * 16 + 1: CAAT_K3S(4, 1); break;
         case 4 * 16 + 2: CAAT_K3S(4, 2); break;
         case 4 * 16 + 4: CAAT_K3S(4, 4); break;
@@ -550,9 +557,15 @@ hipError_t launch_t(const PsyncArgs &a, hipStream_t s) {
     }
 multipass:
     if (PR != nullptr) return hipErrorInvalidValue;   // only the single-pass kernel reads them
-#define CAAT_K3(N)                                                                     \
-    hipLaunchKernelGGL((k_psync_norm<N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
-                       a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld)
+    // bf16 rows come here only past 4096 channels (shorter ones fit one pass for any P),
+    // so with at least four chunks per thread.
+#define CAAT_K3(N)                                                                         \
+    if constexpr (sizeof(TIO) == 4 || (N) >= 4) {                                          \
+        hipLaunchKernelGGL((k_psync_norm<N, NORM, TIO>), grid, block, 0, s, a.P, a.T, a.h, \
+                           a.n_s, a.s_priv, a.eps, P, R, Gm, B, O, OR, Sp, a.s_ld);        \
+    } else {                                                                               \
+        return hipErrorInvalidValue;                                                       \
+    }
     switch (nch) {
     case 1: CAAT_K3(1); break;
     case 2: CAAT_K3(2); break;

@@ -21,6 +21,12 @@ position in the step.
 median and minimum duration of each launch position of the repeating step (the library's
 kernels only; the labels name the positions in order), and the mean gap between launches.
 
+    python -m partial_activation_sync_amd.rocprof_summary coverage <dir> <library>
+
+``coverage`` compares the kernels a shared library holds (the ``*.kd`` kernel-descriptor
+symbols of its code object) with those a ``--kernel-trace --stats`` run launched (its
+``*_kernel_stats.csv``), and lists the ones never launched.
+
 ``stats`` prints a markdown table of per-kernel call counts and durations from the
 ``*_kernel_stats.csv`` of a ``--kernel-trace --stats`` run.  ``traffic`` reads the
 ``*_counter_collection.csv`` of four ``--pmc`` runs (FETCH_SIZE and WRITE_SIZE, in KiB
@@ -233,6 +239,27 @@ def mfma(d, title, command, labels=(), simds=1024, xcds=8):
     return "\n".join(out) + "\n"
 
 
+def _demangle(names):
+    import subprocess
+    r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+    out = r.stdout.split("\n") if r.returncode == 0 else list(names)
+    return [o.split("(")[0].replace("(anonymous namespace)::", "").strip() for o in out[:len(names)]]
+
+
+def coverage(trace_dir, library):
+    """Markdown summary: kernels held by ``library`` against kernels launched in the trace."""
+    data = open(library, "rb").read()
+    held = sorted({m.decode()[:-3] for m in re.findall(rb"_Z[0-9A-Za-z_]+\.kd(?=\x00)", data)})
+    path = glob.glob(os.path.join(trace_dir, "**", "*_kernel_stats.csv"), recursive=True)[0]
+    launched = set(_demangle([r["Name"] for r in csv.DictReader(open(path))]))
+    held_names = _demangle(held)
+    never = sorted(n for n in held_names if n not in launched)
+    out = [f"Kernels in `{os.path.basename(library)}`: {len(held_names)}; launched by the traced "
+           f"run: {len(held_names) - len(never)}; never launched: {len(never)}."]
+    out += [f"- `{n}`" for n in never]
+    return "\n".join(out) + "\n"
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2], sys.argv[3], sys.argv[4]), end="")
@@ -241,6 +268,8 @@ if __name__ == "__main__":
     elif sys.argv[1] == "mfma":
         print(mfma(sys.argv[2], sys.argv[3], sys.argv[4],
                    [tuple(a.split("=", 1)) for a in sys.argv[5:]]), end="")
+    elif sys.argv[1] == "coverage":
+        print(coverage(sys.argv[2], sys.argv[3]), end="")
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(*sys.argv[2:10]), indent=1))
     else:

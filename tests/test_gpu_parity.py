@@ -167,11 +167,15 @@ def test_out_projection_edge_shapes(dtype):
 
 @pytest.mark.parametrize("P,h,ffn,T,act", [(2, 200, 2 * 136, 45, "gelu"),
                                             (4, 264, 4 * 264, 300, "swiglu"),
-                                            (8, 520, 8 * 520, 300, "gelu_tanh")])
+                                            (4, 264, 4 * 264, 300, "gelu"),
+                                            (8, 520, 8 * 520, 300, "gelu_tanh"),
+                                            (8, 520, 8 * 520, 300, "gelu"),
+                                            (8, 520, 8 * 520, 300, "swiglu")])
 def test_f32_gemm_tile_sizes(P, h, ffn, T, act):
     """The fp32 GEMM's three tile shapes through the whole sublayer: 16 x 16 (fewer than 256
-    tiles of 32 x 32), 32 x 32 and 64 x 64 (at least 256 tiles of that size), each with a
-    ragged token tile and a contraction that is not a multiple of the 16-wide K step."""
+    tiles of 32 x 32), 32 x 32 and 64 x 64 (at least 256 tiles of that size), with the
+    activation epilogues, each with a ragged token tile and a contraction that is not a
+    multiple of the 16-wide K step."""
     f_s = ffn // P
     tiles = lambda tb, n: P * -(-n // tb) * -(-T // tb)
     want = {0: 16, 1: 32, 2: 64}[[(2, 200), (4, 264), (8, 520)].index((P, h))]
@@ -180,6 +184,20 @@ def test_f32_gemm_tile_sizes(P, h, ffn, T, act):
     w = W.with_(W.TINY_MLP_F32, P=P, h=h, ffn=ffn, T=T, p=0.41, act=act, norm="rmsnorm",
                 replicated_x=False)
     _run_and_compare(w, norm_params="random", s_priv=math.sqrt(P))
+
+
+def test_per_rank_private_rows_on_small_tiles():
+    """The per-rank row GEMM writing the private chunks into out_resid (P T h >= 2^25, n_s
+    not a multiple of 8) on a shape where the 128 x 128 tiles finish first: 784 tiles of
+    256 x 256 take 4 rounds, 2716 of 128 x 128 six half-efficiency ones (P = 4, h = 12320,
+    T = 769, a 64-wide FFN shard), against the oracle on sampled rows."""
+    T, h, p = 769, 12320, 0.301
+    w = W.with_(W.PAIR_130M_BF16, sublayers=("mlp",), P=4, h=h, ffn=4 * 64, T=T, p=p,
+                act="gelu", norm="rmsnorm", replicated_x=False)
+    hd = caat.Sublayer(h, 4 * 64, 4, p, act="gelu", dtype="bf16")
+    assert hd.n_s % 8 != 0 and not caat.caat_forward_fused(hd.handle, T)
+    assert caat.caat_forward_private_in_epilogue(hd.handle, T)
+    _run_and_compare(w, norm_params="random", rows=synth.sample_rows(T, 48))
 
 
 @pytest.mark.parametrize("act", ["gelu", "gelu_tanh"])
