@@ -49,6 +49,9 @@
  *     makes it return CAAT_EUNSUPPORTED, as on another architecture.
  *   Concurrency: calls on one handle that overlap on different streams must use
  *     different workspaces (one handle per stream).
+ *   Aliasing: in the forward calls, out_resid or out may be the resid buffer itself
+ *     (the residual stream updated in place; each element is read before it is written,
+ *     by the same thread); no other output may overlap an input or another output.
  */
 #ifndef CAAT_H
 #define CAAT_H

@@ -232,6 +232,41 @@ def test_gelu_decode_batches(act, P, ffn, T):
     _run_and_compare(w, norm_params="random")
 
 
+@pytest.mark.parametrize("act,dtype,P,h,fs,T,p", [
+    ("swiglu", "bf16", 4, 1024, 256, 8192, 0.5),     # fused, private rows from the GEMM epilogue
+    ("swiglu", "bf16", 4, 1024, 256, 8192, 0.501),   # per-rank, private chunks from the epilogue
+    ("gelu", "bf16", 4, 1024, 256, 300, 0.37),       # per-rank, stored partials
+    ("none", "bf16", 8, 4096, 0, 5, 0.5),            # decode: per-rank K3 (one token, one rank)
+    ("gelu", "f32", 16, 1024, 64, 100, 0.3),         # fp32, multi-pass K3
+])
+def test_residual_updated_in_place(act, dtype, P, h, fs, T, p):
+    """out_resid may be the resid buffer itself (the residual stream updated in place): each
+    element of r is read and then written by the same thread, in K3 and in the row GEMM's
+    residual epilogue alike, so the outputs are bitwise those of separate buffers."""
+    _say(f"[case] in-place residual {act} {dtype} P={P} h={h} T={T} p={p}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kin = h // P if act == "none" else h
+    F1 = 2 * fs if act == "swiglu" else fs
+    x = synth.normal((P, T, kin), synth.X, dtype=dt).cuda()
+    W1 = None if act == "none" else (synth.normal((P, F1, h), synth.W1, std=0.02, dtype=dt).cuda())
+    W2 = synth.normal((P, h, fs if act != "none" else kin), synth.W2, std=0.02, dtype=dt).cuda()
+    R = synth.normal((P, T, h), synth.X0, dtype=dt).cuda()
+    gamma = synth.normal((h,), synth.GAMMA, std=0.1, mean=1.0, dtype=dt).cuda()
+    s = caat.Sublayer(h, P * fs, P, p, norm="rmsnorm", act=act, dtype=dtype, s_priv=1.5)
+    out1 = torch.empty_like(R)
+    res1 = torch.empty_like(R)
+    s.forward(x, W1, W2, gamma, out1, resid=R, out_resid=res1)
+    R2 = R.clone()
+    out2 = torch.empty_like(R)
+    s.forward(x, W1, W2, gamma, out2, resid=R2, out_resid=R2)
+    R3 = R.clone()
+    res3 = torch.empty_like(R)
+    s.forward(x, W1, W2, gamma, R3, resid=R3, out_resid=res3)
+    torch.cuda.synchronize()
+    assert torch.equal(R2, res1) and torch.equal(out2, out1)
+    assert torch.equal(R3, out1) and torch.equal(res3, res1)
+
+
 def _random_cases(n=32, seed=20251203):
     """Seeded random sublayer configurations (drawn once, so the test ids are stable): MLP
     or out-projection + MLP pair, fp32 or bf16, every activation and norm, P 1..8, widths
